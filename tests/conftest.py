@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def O():
+    """The CPU oracle (built on first use if this checkout has no build yet)."""
+    from oracle import oracle as orc
+
+    if not os.path.exists(orc.LIB):
+        orc.build()
+    return orc

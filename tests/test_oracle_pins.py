@@ -1,0 +1,409 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-worked examples, library routines (torch's bf16 cast, numpy sort /
+quantile / argsort, torch matmul), brute force on tiny inputs, exhaustive
+checks over the bf16 patterns, closed forms and invariants.
+
+Definitions pinned: "[Dev] Add global-batch quantile balancing" (Megatron-LM
+PR #6637, section "Quantile estimator"); "Exact Quantile Balancing and
+Load-Error Injection for Mixture-of-Experts" (summary page, EQB and LEI
+paragraphs).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from exact_quantile_selection_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+# Independent of the oracle: torch's CPU cast is the bf16 reference, numpy
+# float32 arithmetic is IEEE single precision with round-to-nearest-even.
+
+def torch_bf16_bits(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_values(u):
+    return (np.asarray(u, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def not_nan_f32(bits):
+    return ~((((bits >> 23) & 0xFF) == 0xFF) & ((bits & 0x7FFFFF) != 0))
+
+
+def numpy_margins(s, b, K):
+    """alpha by numpy sort, fp32 margins, their bf16 patterns."""
+    v = (s + b[None, :]).astype(np.float32)
+    alpha = -np.sort(-v, axis=1)[:, K]
+    r = (alpha[:, None] - s).astype(np.float32)
+    return alpha, r, torch_bf16_bits(r).reshape(r.shape)
+
+
+def rank_m(N, E, K):
+    return -(-K * N // E)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_bf16_rne_hand_values(O):
+    cases = {
+        0x3F800000: 0x3F80,  # 1.0 exact
+        0x3F808000: 0x3F80,  # 1 + 2^-8: halfway, even neighbour is 0x3F80
+        0x3F818000: 0x3F82,  # 1 + 3*2^-8: halfway, even neighbour is 0x3F82
+        0x3F808001: 0x3F81,  # just above halfway
+        0xBF808000: 0xBF80,  # negative halfway
+        0x7F7F7FFF: 0x7F7F,  # below halfway to 2^128: largest finite bf16
+        0x7F7F8000: 0x7F80,  # halfway to 2^128 with odd lower neighbour -> inf
+        0x7F7FFFFF: 0x7F80,  # largest finite float -> inf
+        0x00000001: 0x0000,  # smallest subnormal float -> +0 (no flush needed)
+        0x00008000: 0x0000,  # halfway between 0 and the smallest bf16 subnormal
+        0x00018000: 0x0002,  # halfway between 1 and 2 subnormal steps -> even
+        0x80018000: 0x8002,
+        0x00010000: 0x0001,  # smallest bf16 subnormal is exact
+        0x80000000: 0x8000,  # -0 stays -0
+        0x7F800000: 0x7F80,  # inf
+    }
+    for bits, want in cases.items():
+        x = np.array([bits], np.uint32).view(np.float32)[0]
+        assert O.lib().oq_bf16_rne(float(x)) == want, hex(bits)
+
+
+def test_bf16_rne_vs_torch_structured(O):
+    hi = np.arange(65536, dtype=np.uint32) << 16
+    lows = np.array([0, 1, 0x3FFF, 0x4000, 0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xC000, 0xFFFF], np.uint32)
+    bits = (hi[:, None] | lows[None, :]).ravel()
+    bits = bits[not_nan_f32(bits)]
+    x = bits.view(np.float32)
+    np.testing.assert_array_equal(O.bf16_rne(x), torch_bf16_bits(x))
+
+
+def test_bf16_rne_vs_torch_random(O):
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2**32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    bits = bits[not_nan_f32(bits)]
+    x = bits.view(np.float32)
+    np.testing.assert_array_equal(O.bf16_rne(x), torch_bf16_bits(x))
+
+
+def test_bf16_rne_vs_torch_exhaustive_sampled_exponents(O):
+    """Every float pattern in 8 full exponent bands (2^23 patterns each, both
+    signs): subnormals, the score range [0.25, 1), large and overflow bands."""
+    for exp in (0x00, 0x01, 0x7C, 0x7D, 0x7E, 0x7F, 0xFD, 0xFE):
+        for sign in (0, 1):
+            bits = (np.uint32(sign << 31) | np.uint32(exp << 23)
+                    | np.arange(1 << 23, dtype=np.uint32))
+            x = bits.view(np.float32)
+            np.testing.assert_array_equal(O.bf16_rne(x), torch_bf16_bits(x), err_msg=f"{sign} {exp:#x}")
+
+
+# ---------------------------------------------------------------- key map
+
+def test_key_order_exhaustive(O):
+    u = np.arange(65536, dtype=np.uint32)
+    nan = ((u & 0x7F80) == 0x7F80) & ((u & 0x7F) != 0)
+    u = u[~nan]
+    keys = np.array([O.key(int(x)) for x in u], np.int64)
+    assert len(set(keys.tolist())) == u.size  # injective
+    assert all(O.unkey(int(k)) == int(x) for k, x in zip(keys, u))
+    order = np.argsort(keys)
+    vals = bf16_values(u[order])
+    d = np.diff(vals)
+    assert (d >= 0).all()  # key order is value order
+    zero_steps = np.nonzero(d == 0)[0]
+    assert zero_steps.size == 1  # only -0 -> +0 compare equal
+    i = zero_steps[0]
+    assert u[order][i] == 0x8000 and u[order][i + 1] == 0x0000
+    assert O.key(0x8000) == 0x7FFF and O.key(0x0000) == 0x8000
+
+
+# ---------------------------------------------------------------- alpha + loads
+
+ALPHA_CASES = [
+    (257, 16, 2, None), (300, 32, 3, 8.0), (129, 256, 6, 64.0), (64, 7, 6, None),
+    (500, 64, 8, 4.0), (33, 8, 1, None), (200, 128, 6, 2.0),
+]
+
+
+@pytest.mark.parametrize("N,E,K,quant", ALPHA_CASES)
+def test_alpha_and_loads_vs_numpy(O, N, E, K, quant):
+    s, b, _ = synth.random_case(1, N, E, K, quant=quant)
+    v = (s + b[None, :]).astype(np.float32)
+    a, load = O.alpha(s, b, K)
+    np.testing.assert_array_equal(a, -np.sort(-v, axis=1)[:, K])
+    top = np.argsort(-v, axis=1, kind="stable")[:, :K]  # ties -> lower index
+    np.testing.assert_array_equal(load, np.bincount(top.ravel(), minlength=E))
+    assert load.sum() == N * K
+
+
+def test_alpha_when_E_is_K_plus_1(O):
+    s, b, _ = synth.random_case(2, 100, 7, 6, quant=16.0)
+    a = O.alpha(s, b, 6, with_load=False)
+    np.testing.assert_array_equal(a, (s + b[None, :]).astype(np.float32).min(axis=1))
+
+
+# ---------------------------------------------------------------- quantile
+
+QUANT_CASES = [
+    (1024, 16, 2, None), (999, 32, 3, None), (4096, 64, 6, 64.0), (2048, 256, 6, 64.0),
+    (777, 8, 1, 8.0), (3000, 128, 8, None),
+]
+
+
+@pytest.mark.parametrize("N,E,K,quant", QUANT_CASES)
+def test_quantile_vs_numpy_inverted_cdf(O, N, E, K, quant):
+    s, b, _ = synth.random_case(3, N, E, K, quant=quant)
+    _, _, u = numpy_margins(s, b, K)
+    vals = bf16_values(u)
+    ref = np.array([np.quantile(vals[:, j], K / E, method="inverted_cdf") for j in range(E)])
+    out = O.eqb_layer(s, b, K)
+    np.testing.assert_array_equal(out["q"].astype(np.float64), ref)
+    if (K * N) % E == 0:  # equals torch's 'lower' interpolation there
+        t = torch.quantile(torch.from_numpy(vals), K / E, dim=0, interpolation="lower").numpy()
+        np.testing.assert_array_equal(out["q"].astype(np.float64), t)
+
+
+def brute_force_q(s, b, K):
+    """Definition, pure Python loops: alpha is the value x of the row with
+    #(v > x) <= K < #(v >= x); q_j is the smallest margin x of column j with
+    #(margins <= x) >= m."""
+    N, E = s.shape
+    v = (s + b[None, :]).astype(np.float32)
+    alpha = np.empty(N, np.float32)
+    for i in range(N):
+        row = [float(x) for x in v[i]]
+        for x in row:
+            if sum(y > x for y in row) <= K < sum(y >= x for y in row):
+                alpha[i] = x
+                break
+    r = (alpha[:, None] - s).astype(np.float32)
+    vals = bf16_values(torch_bf16_bits(r)).reshape(N, E)
+    m = rank_m(N, E, K)
+    q = []
+    for j in range(E):
+        col = [float(x) for x in vals[:, j]]
+        q.append(min(x for x in col if sum(y <= x for y in col) >= m))
+    return alpha, np.array(q)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 17, 64])
+@pytest.mark.parametrize("E", [2, 3, 5, 8])
+def test_brute_force_tiny(O, seed, N, E):
+    for K in range(1, E):
+        s, b, _ = synth.random_case(seed, N, E, K, quant=4.0 if seed == 1 else None)
+        alpha_bf, q_bf = brute_force_q(s, b, K)
+        out = O.eqb_layer(s, b, K)
+        np.testing.assert_array_equal(out["alpha"], alpha_bf)
+        np.testing.assert_array_equal(out["q"].astype(np.float64), q_bf)
+
+
+# ---------------------------------------------------------------- histograms
+
+@pytest.mark.parametrize("N,E,K,quant", [(1000, 16, 2, None), (3000, 32, 6, 64.0), (2048, 256, 6, 64.0)])
+def test_radix_histograms_consistent(O, N, E, K, quant):
+    s, b, _ = synth.random_case(4, N, E, K, quant=quant)
+    _, _, u = numpy_margins(s, b, K)
+    keys = np.where(u & 0x8000, ~u, u | 0x8000).astype(np.uint16)  # independent key map
+    out = O.eqb_layer(s, b, K)
+    m = rank_m(N, E, K)
+    assert out["hist_hi"].shape == (E, 256) and out["hist_lo"].shape == (E, 256)
+    for j in range(E):
+        kj = keys[:, j]
+        np.testing.assert_array_equal(out["hist_hi"][j], np.bincount(kj >> 8, minlength=256))
+        assert out["hist_hi"][j].sum() == N  # every row sums to the token count
+        sel = int(out["sel_hi"][j])
+        C = np.cumsum(out["hist_hi"][j])
+        assert (C[sel - 1] if sel else 0) < m <= C[sel]
+        np.testing.assert_array_equal(
+            out["hist_lo"][j], np.bincount(kj[(kj >> 8) == sel] & 0xFF, minlength=256))
+        assert out["hist_lo"][j].sum() == out["hist_hi"][j][sel]
+        lstar = int(out["key"][j]) & 0xFF
+        assert int(out["key"][j]) >> 8 == sel
+        Cl = np.cumsum(out["hist_lo"][j])
+        assert (Cl[lstar - 1] if lstar else 0) < out["rank_lo"][j] <= Cl[lstar]
+        assert out["rank_lo"][j] == m - (C[sel - 1] if sel else 0)
+        assert np.sort(kj)[m - 1] == out["key"][j]
+
+
+def test_buffer_sizes_closed_form():
+    """EQB paragraph: 2 * E * 256 int32 counts per layer = 0.5 MiB at E=256,
+    24 MiB over 48 layers; K3 (PR 6637): E * 1000 int32 per router."""
+    E = 256
+    per_layer = 2 * E * 256 * np.dtype(np.int32).itemsize
+    assert per_layer == 512 * 1024
+    assert 48 * per_layer == 24 * 1024 * 1024
+    assert E * 1000 * 4 == 1_024_000
+    assert (65536 * E * 4) // per_layer == 128  # one int32 per bf16 pattern per expert
+
+
+# ---------------------------------------------------------------- b_next
+
+@pytest.mark.parametrize("N,E,K,quant", [(2048, 256, 6, 64.0), (1000, 16, 2, None), (5000, 64, 4, None)])
+def test_bnext_sums_to_zero(O, N, E, K, quant):
+    s, b, _ = synth.random_case(5, N, E, K, quant=quant)
+    out = O.eqb_layer(s, b, K)
+    bn = out["b_next"].astype(np.float64)
+    half_ulp = 0.5 * np.spacing(np.abs(out["b_next"]).max())
+    assert abs(bn.sum()) <= E * half_ulp
+    assert out["bounds"][0] == np.float32(out["b_next"].min() - np.float32(1))
+    assert out["bounds"][1] == np.float32(out["b_next"].max() + np.float32(1))
+
+
+def test_constant_scores_give_zero_bias(O):
+    s = np.full((300, 32), 0.375, np.float32)
+    out = O.eqb_layer(s, np.zeros(32, np.float32), 3)
+    assert (out["q"] == 0).all() and (out["b_next"] == 0).all()
+    np.testing.assert_array_equal(out["bounds"], [-1.0, 1.0])
+
+
+def test_per_expert_constant_scores_closed_form(O):
+    E, K, N = 64, 6, 257
+    rng = np.random.default_rng(11)
+    c = rng.uniform(0, 1, E).astype(np.float32)
+    b = rng.uniform(-0.2, 0.2, E).astype(np.float32)
+    s = np.repeat(c[None, :], N, axis=0)
+    alpha = np.sort((c + b).astype(np.float32))[::-1][K]
+    want = bf16_values(torch_bf16_bits((alpha - c).astype(np.float32)))
+    out = O.eqb_layer(s, b, K)
+    np.testing.assert_array_equal(out["q"].astype(np.float64), want)
+
+
+def test_single_token(O):
+    s, b, _ = synth.random_case(6, 1, 32, 4)
+    _, r, u = numpy_margins(s, b, 4)
+    out = O.eqb_layer(s, b, 4)
+    np.testing.assert_array_equal(out["q"].astype(np.float64), bf16_values(u[0]))
+
+
+def test_permutation_and_partition_invariance(O):
+    s, b, K = synth.random_case(8, 3000, 32, 6, quant=64.0)
+    full = O.eqb_layer(s, b, K)
+    perm = np.random.default_rng(0).permutation(3000)
+    p = O.eqb_layer(s[perm], b, K)
+    for k in ("hist_hi", "hist_lo", "key", "q", "b_next", "bounds"):
+        np.testing.assert_array_equal(full[k], p[k])
+    # histograms of row chunks add up to the histogram of the whole batch
+    parts = [O.eqb_layer(s[a:a + 700], b, K)["hist_hi"] for a in range(0, 3000, 700)]
+    np.testing.assert_array_equal(sum(parts), full["hist_hi"])
+
+
+# ---------------------------------------------------------------- hand examples
+
+def test_hand_examples(O):
+    g = json.load(open(os.path.join(GOLDEN, "hand_examples.json")))
+    s = np.array(g["s"], np.float32)
+    b = np.array(g["b"], np.float32)
+    for case in g["cases"]:
+        K = case["K"]
+        out = O.eqb_layer(s, b, K)
+        np.testing.assert_array_equal(out["alpha"], case["alpha"])
+        np.testing.assert_array_equal(out["load"], case["load"])
+        np.testing.assert_array_equal(out["q"], case["q"])
+        np.testing.assert_array_equal(out["key"], case["key"])
+        np.testing.assert_array_equal(out["b_next"], case["b_next"])
+        np.testing.assert_array_equal(out["bounds"], case["bounds"])
+        if "sel_hi" in case:
+            np.testing.assert_array_equal(out["sel_hi"], case["sel_hi"])
+            np.testing.assert_array_equal(out["rank_lo"], case["rank_lo"])
+            nz = {str(h): int(c) for h, c in enumerate(out["hist_hi"][0]) if c}
+            assert nz == case["hist_hi_nonzero_expert0"]
+
+
+# ---------------------------------------------------------------- K3 mode
+
+@pytest.mark.parametrize("N,E,K,n_bins,quant", [(4000, 16, 2, 1000, None), (2048, 256, 6, 1000, None),
+                                                (3000, 64, 6, 50, 64.0), (500, 8, 1, 7, None)])
+def test_k3_histogram_and_containment(O, N, E, K, n_bins, quant):
+    s, b, _ = synth.random_case(9, N, E, K, quant=quant)
+    bounds = O.bounds_of(b)
+    assert bounds[0] == np.float32(b.min() - np.float32(1)) and bounds[1] == np.float32(b.max() + np.float32(1))
+    out = O.k3_layer(s, b, K, bounds, n_bins)
+    _, r, _ = numpy_margins(s, b, K)
+    lo, hi = float(bounds[0]), float(bounds[1])
+    # closed form: with scores in [0, 1] every margin lies inside the range
+    assert (r >= bounds[0]).all() and (r <= bounds[1]).all()
+    assert (out["hist_u"].sum(axis=1) == N).all()
+    # bins agree with the real-number bin floor((r - lo) / w) away from edges
+    w = (hi - lo) / n_bins
+    t = (r.astype(np.float64) - lo) / w
+    exact = np.clip(np.floor(t), 0, n_bins - 1).astype(np.int64)
+    far = np.abs(t - np.round(t)) > 1e-3
+    m = rank_m(N, E, K)
+    for j in range(E):
+        mine = np.array([O.k3_bin(x, lo, hi, n_bins) for x in r[far[:, j], j]])
+        np.testing.assert_array_equal(mine, exact[far[:, j], j])
+        C = np.cumsum(out["hist_u"][j])
+        c = int(np.searchsorted(C, m))  # first bin with C >= m
+        true_q = np.sort(r[:, j].astype(np.float64))[m - 1]
+        tol = 1e-4 * w
+        assert lo + c * w - tol <= true_q <= lo + (c + 1) * w + tol
+        assert lo + c * w - tol <= out["q"][j] <= lo + (c + 1) * w + tol
+    bn = out["b_next"].astype(np.float64)
+    assert abs(bn.sum()) <= E * 0.5 * np.spacing(np.abs(out["b_next"]).max())
+
+
+def test_k3_hand_bins(O):
+    # range [-1, 1] in 4 bins of width 0.5: edges -1, -0.5, 0, 0.5, 1
+    assert O.k3_bin(-1.0, -1.0, 1.0, 4) == 0
+    assert O.k3_bin(-0.75, -1.0, 1.0, 4) == 0
+    assert O.k3_bin(-0.5, -1.0, 1.0, 4) == 1
+    assert O.k3_bin(0.0, -1.0, 1.0, 4) == 2
+    assert O.k3_bin(0.999, -1.0, 1.0, 4) == 3
+    assert O.k3_bin(1.0, -1.0, 1.0, 4) == 3   # last bin closed
+    assert O.k3_bin(-7.0, -1.0, 1.0, 4) == 0  # clamped
+    assert O.k3_bin(9.0, -1.0, 1.0, 4) == 3
+
+
+def test_k3_interpolation_hand_example(O):
+    # one expert column (E=2, K=1 -> level 1/2), N=4 tokens; bounds [-1, 1],
+    # 2 bins of width 1.  Scores chosen so the margins are known exactly.
+    s = np.array([[0.5, 0.25], [0.5, 0.75], [0.5, 0.125], [0.5, 0.625]], np.float32)
+    b = np.zeros(2, np.float32)
+    out = O.k3_layer(s, b, 1, np.array([-1.0, 1.0], np.float32), 2)
+    # alpha = min of each row (2nd largest of 2): .25,.5,.125,.5
+    # margins col0: -.25, 0, -.375, 0 -> bins [2 in bin0, 2 in bin1]; m=2
+    # -> bin0 holds rank 2: q0 = -1 + 1*(0 + 2/2) = 0
+    # col1: 0, -.25, 0, -.125 -> bins: -.25,-.125 in bin0, 0,0 in bin1;
+    # -> q1 = -1 + (0 + 2/2) = 0
+    np.testing.assert_array_equal(out["hist_u"], [[2, 2], [2, 2]])
+    np.testing.assert_array_equal(out["q"], [0.0, 0.0])
+
+
+# ---------------------------------------------------------------- LEI
+
+def test_lei_hand_example(O):
+    eta = np.float32(1e-5)
+    g = np.zeros((4, 4), np.float32)
+    out = O.lei(g, np.array([4, 0, 0, 0], np.int32), 1, eta)  # M = 1, rho = [3,-1,-1,-1]
+    want = np.array([eta * np.float32(3), -eta, -eta, -eta], np.float32)
+    np.testing.assert_array_equal(out, np.repeat(want[None, :], 4, axis=0))
+
+
+def test_lei_relative_error(O):
+    s, b, K = synth.random_case(10, 2000, 64, 6)
+    _, load = O.alpha(s, b, K)
+    M = 2000 * K / 64
+    assert (load - M).sum() == 0
+    out = O.lei(np.zeros((2000, 64), np.float32), load, K, 1e-5)
+    np.testing.assert_allclose(out[0] / np.float32(1e-5), (load - M) / M, rtol=1e-6, atol=1e-7)
+    assert (out == out[0][None, :]).all()
+
+
+# ---------------------------------------------------------------- router logits
+
+def test_router_logits_vs_torch(O):
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal((50, 96), dtype=np.float32)
+    w = rng.normal(0, 0.02, (96, 24)).astype(np.float32)
+    hb, wb = torch_bf16_bits(h).reshape(h.shape), torch_bf16_bits(w).reshape(w.shape)
+    rows = np.array([0, 7, 49, 3])
+    out = O.router_logits(hb, wb, rows)
+    ref = (torch.from_numpy(bf16_values(hb)[rows]) @ torch.from_numpy(bf16_values(wb))).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
