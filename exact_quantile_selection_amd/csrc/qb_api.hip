@@ -1,0 +1,257 @@
+// qb_api.hip -- the extern "C" boundary of libqb: argument checks, shape
+// dispatch and status reporting.  Every entry point validates its arguments
+// on the host, launches asynchronously on the caller's stream and never
+// synchronises or allocates.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/qb.h"
+#include "qb_internal.hpp"
+
+namespace qbk {
+
+int launch_margins_topk_e16(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e32(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e64(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e128(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e256(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+
+int launch_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
+                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st) {
+  switch (E) {
+    case 16: return launch_margins_topk_e16(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 32: return launch_margins_topk_e32(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 64: return launch_margins_topk_e64(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 128: return launch_margins_topk_e128(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 256: return launch_margins_topk_e256(s, b, L, N, K, alpha, load, hist_hi, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+bool supported_E(int E) { return E == 16 || E == 32 || E == 64 || E == 128 || E == 256; }
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+RowSplit split_rows(int L, int64_t N, int step, int cap) {
+  const int64_t per_layer = std::max<int64_t>(1, (device_cu_count() + L - 1) / L);
+  int64_t rows = round_up((N + per_layer - 1) / per_layer, step);
+  const int64_t cap_r = std::max<int64_t>(step, int64_t(cap) / step * step);
+  const int64_t cap16 = std::max<int64_t>(step, 65535 / step * step);  // 16-bit LDS counters
+  rows = std::min(rows, std::min(cap_r, cap16));
+  RowSplit r;
+  r.rows_per_wg = int(rows);
+  r.wg_per_layer = int((N + rows - 1) / rows);
+  r.blocks = int64_t(L) * r.wg_per_layer;
+  return r;
+}
+
+RowSplit split_rows_chunks(int64_t N, int64_t chunks, int step) {
+  const int64_t rows = std::max<int64_t>(step, round_up((N + chunks - 1) / chunks, step));
+  RowSplit r;
+  r.rows_per_wg = int(std::min<int64_t>(rows, int64_t(1) << 30));
+  r.wg_per_layer = int((N + r.rows_per_wg - 1) / r.rows_per_wg);
+  r.blocks = r.wg_per_layer;
+  return r;
+}
+
+}  // namespace qbk
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return QB_OK;
+}
+
+int hip_status(int rc, const char* what) {
+  if (rc != int(hipSuccess))
+    return fail(QB_EHIP, "%s: HIP launch failed: %s", what, hipGetErrorString(hipError_t(rc)));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Common shape checks of the passes over s [L][N][E].
+int check_pass(const char* fn, const float* s, int L, int64_t N, int E) {
+  if (!s) return fail(QB_EINVAL, "%s: s is NULL (expected float [L][N][E] device pointer)", fn);
+  if (!aligned16(s)) return fail(QB_EINVAL, "%s: s must be 16-byte aligned", fn);
+  if (L < 1) return fail(QB_EINVAL, "%s: L=%d, expected L >= 1", fn, L);
+  if (N < 1 || N > INT32_MAX)
+    return fail(QB_EINVAL, "%s: N=%lld, expected 1 <= N < 2^31", fn, (long long)N);
+  if (!qbk::supported_E(E))
+    return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {16, 32, 64, 128, 256}", fn, E);
+  return QB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+QB_API int qb_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
+                           float* alpha, int32_t* load, int32_t* hist_hi, qb_stream_t stream) {
+  const char* fn = "qb_margins_topk";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!b) return fail(QB_EINVAL, "%s: b is NULL (expected float [L=%d][E=%d])", fn, L, E);
+  if (!alpha) return fail(QB_EINVAL, "%s: alpha is NULL (expected float [L=%d][N=%lld])", fn, L, (long long)N);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (!aligned4(b) || !aligned4(alpha) || (load && !aligned4(load)) || (hist_hi && !aligned4(hist_hi)))
+    return fail(QB_EINVAL, "%s: b, alpha, load and hist_hi must be 4-byte aligned", fn);
+  return hip_status(qbk::launch_margins_topk(s, b, L, N, E, K, alpha, load, hist_hi, stream), fn);
+}
+
+QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N, int E,
+                            int32_t* hist_hi, qb_stream_t stream) {
+  const char* fn = "qb_radix_hist_hi";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!alpha || !hist_hi)
+    return fail(QB_EINVAL, "%s: alpha (float [L][N]) and hist_hi (int32 [L=%d][E=%d][256]) are required",
+                fn, L, E);
+  return hip_status(qbk::launch_radix_hist(false, s, alpha, L, N, E, nullptr, hist_hi, stream), fn);
+}
+
+QB_API int qb_radix_hist_lo(const float* s, const float* alpha, int L, int64_t N, int E,
+                            const int32_t* sel_hi, int32_t* hist_lo, qb_stream_t stream) {
+  const char* fn = "qb_radix_hist_lo";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!alpha || !sel_hi || !hist_lo)
+    return fail(QB_EINVAL,
+                "%s: alpha (float [L][N]), sel_hi (int32 [L=%d][E=%d]) and hist_lo (int32 [L][E][256]) are required",
+                fn, L, E);
+  return hip_status(qbk::launch_radix_hist(true, s, alpha, L, N, E, sel_hi, hist_lo, stream), fn);
+}
+
+QB_API int qb_margin_keys(const float* s, const float* alpha, int L, int64_t N, int E,
+                          uint16_t* keys, qb_stream_t stream) {
+  const char* fn = "qb_margin_keys";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!alpha || !keys)
+    return fail(QB_EINVAL, "%s: alpha (float [L][N]) and keys (uint16 [L=%d][N][E=%d]) are required", fn,
+                L, E);
+  if ((reinterpret_cast<uintptr_t>(keys) & 7u) != 0)
+    return fail(QB_EINVAL, "%s: keys must be 8-byte aligned", fn);
+  return hip_status(qbk::launch_margin_keys(s, alpha, L, N, E, keys, stream), fn);
+}
+
+QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist, int n_bins,
+                            int32_t* sel_hi, int32_t* rank_lo, uint16_t* key_out, float* q_out,
+                            float* b, float* bounds, int32_t* err, qb_stream_t stream) {
+  const char* fn = "qb_select_update";
+  if (L < 1) return fail(QB_EINVAL, "%s: L=%d, expected L >= 1", fn, L);
+  if (!qbk::supported_E(E))
+    return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {16, 32, 64, 128, 256}", fn, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (!hist) return fail(QB_EINVAL, "%s: hist is NULL", fn);
+  switch (phase) {
+    case QB_SELECT_HI:
+      if (!sel_hi || !rank_lo)
+        return fail(QB_EINVAL, "%s(HI): sel_hi and rank_lo (int32 [L=%d][E=%d]) are required", fn, L, E);
+      n_bins = 256;
+      break;
+    case QB_SELECT_LO:
+      if (!sel_hi || !rank_lo || !b || !bounds)
+        return fail(QB_EINVAL,
+                    "%s(LO): sel_hi, rank_lo (int32 [L=%d][E=%d]), b (float [L][E]) and bounds (float [L][2]) are required",
+                    fn, L, E);
+      n_bins = 256;
+      break;
+    case QB_SELECT_UNIFORM:
+      if (!b || !bounds)
+        return fail(QB_EINVAL, "%s(UNIFORM): b (float [L=%d][E=%d]) and bounds (float [L][2]) are required",
+                    fn, L, E);
+      if (n_bins < 1 || n_bins > 2048)
+        return fail(QB_EINVAL, "%s(UNIFORM): n_bins=%d, expected 1 <= n_bins <= 2048", fn, n_bins);
+      break;
+    default:
+      return fail(QB_EINVAL, "%s: phase=%d, expected QB_SELECT_HI, QB_SELECT_LO or QB_SELECT_UNIFORM", fn,
+                  phase);
+  }
+  return hip_status(qbk::launch_select(phase, L, E, K, hist, n_bins, sel_hi, rank_lo, key_out, q_out, b,
+                                       bounds, err, stream),
+                    fn);
+}
+
+QB_API int qb_uniform_hist(const float* s, const float* alpha, int L, int64_t N, int E,
+                           const float* bounds, int n_bins, int32_t* hist_u, qb_stream_t stream) {
+  const char* fn = "qb_uniform_hist";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!alpha || !bounds || !hist_u)
+    return fail(QB_EINVAL,
+                "%s: alpha (float [L][N]), bounds (float [L=%d][2]) and hist_u (int32 [L][E=%d][n_bins]) are required",
+                fn, L, E);
+  if (n_bins < 1 || n_bins > 2048)
+    return fail(QB_EINVAL, "%s: n_bins=%d, expected 1 <= n_bins <= 2048", fn, n_bins);
+  return hip_status(qbk::launch_uniform_hist(s, alpha, L, N, E, bounds, n_bins, hist_u, stream), fn);
+}
+
+QB_API int qb_bias_bounds(const float* b, int L, int E, float* bounds, qb_stream_t stream) {
+  const char* fn = "qb_bias_bounds";
+  if (!b || !bounds) return fail(QB_EINVAL, "%s: b (float [L][E]) and bounds (float [L][2]) are required", fn);
+  if (L < 1 || E < 1) return fail(QB_EINVAL, "%s: L=%d E=%d, expected >= 1", fn, L, E);
+  return hip_status(qbk::launch_bias_bounds(b, L, E, bounds, stream), fn);
+}
+
+QB_API int qb_fill_i32(int32_t* dst, int64_t count, int32_t value, qb_stream_t stream) {
+  const char* fn = "qb_fill_i32";
+  if (count < 0) return fail(QB_EINVAL, "%s: count=%lld < 0", fn, (long long)count);
+  if (count == 0) return ok();
+  if (!dst || !aligned4(dst)) return fail(QB_EINVAL, "%s: dst is NULL or not 4-byte aligned", fn);
+  return hip_status(qbk::launch_fill_i32(dst, count, value, stream), fn);
+}
+
+QB_API int qb_lei_grad(float* g, const int32_t* load, int64_t N, int E, int K, float eta,
+                       qb_stream_t stream) {
+  const char* fn = "qb_lei_grad";
+  if (!g || !load) return fail(QB_EINVAL, "%s: g (float [N][E]) and load (int32 [E]) are required", fn);
+  if (!aligned16(g)) return fail(QB_EINVAL, "%s: g must be 16-byte aligned", fn);
+  if (N < 1 || N > INT32_MAX)
+    return fail(QB_EINVAL, "%s: N=%lld, expected 1 <= N < 2^31", fn, (long long)N);
+  if (!qbk::supported_E(E))
+    return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {16, 32, 64, 128, 256}", fn, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  return hip_status(qbk::launch_lei(g, load, N, E, K, eta, stream), fn);
+}
+
+QB_API const char* qb_status_string(int status) {
+  switch (status) {
+    case QB_OK: return "QB_OK";
+    case QB_EINVAL: return "QB_EINVAL: invalid argument";
+    case QB_EUNSUPPORTED: return "QB_EUNSUPPORTED: shape outside the compiled instantiations";
+    case QB_EHIP: return "QB_EHIP: HIP runtime error";
+  }
+  return "unknown status";
+}
+
+QB_API const char* qb_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// qb_device.hpp -- device building blocks shared by the libqb kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qbk {
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+typedef short s2v __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Two fp32 -> two bf16 patterns (round to nearest even, subnormals kept) in
+// one v_cvt_pk_bf16_f32: low half = a, high half = b.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  f2v x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, b2v));
+}
+
+// Order-preserving 16-bit key of each bf16 half: negative -> ~u,
+// non-negative -> u | 0x8000 (so unsigned key order is value order).
+__device__ __forceinline__ uint32_t key2(uint32_t p) {
+  s2v x = __builtin_bit_cast(s2v, p);
+  s2v sm = x >> (s2v){15, 15};  // 0xFFFF where the half is negative
+  uint32_t m = (__builtin_bit_cast(uint32_t, sm) & 0x7FFF7FFFu) | 0x80008000u;
+  return p ^ m;
+}
+
+// Inverse of the key map for one 16-bit key.
+__device__ __forceinline__ uint32_t unkey16(uint32_t k) {
+  return (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+}
+
+// Cross-lane move inside a row of 4 lanes (DPP quad_perm).
+template <int CTRL>
+__device__ __forceinline__ float quad_mov(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int quad_mov_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+
+// Insert v into a descending list t[0..P-1] keeping the P largest values:
+// t'_0 = max(t_0, v), t'_k = med3(t_{k-1}, t_k, v).  One VALU op per slot.
+template <int P>
+__device__ __forceinline__ void top_insert(float (&t)[P], float v) {
+#pragma unroll
+  for (int k = P - 1; k >= 1; --k) t[k] = __builtin_amdgcn_fmed3f(t[k - 1], t[k], v);
+  t[0] = fmaxf(t[0], v);
+}
+
+// Compare-exchange for a descending network; positions below PAD hold +inf
+// and never move, so exchanges that touch them are skipped at compile time.
+template <int PAD, int A, int B>
+__device__ __forceinline__ void ce_desc(float (&c)[8]) {
+  if constexpr (A >= PAD) {
+    const float hi = fmaxf(c[A], c[B]);
+    const float lo = fminf(c[A], c[B]);
+    c[A] = hi;
+    c[B] = lo;
+  }
+}
+
+// Merge this lane's descending list with the partner lane's (DPP control
+// CTRL) into the descending list of the P largest of their union.
+// max(A_k, B_{P-1-k}) is the top-P multiset in bitonic order; a bitonic
+// sorting network of width 8 (front-padded with +inf) restores the order.
+template <int P, int CTRL>
+__device__ __forceinline__ void top_merge(float (&t)[P]) {
+  static_assert(P >= 1 && P <= 8, "list length");
+  constexpr int PAD = 8 - P;
+  float pt[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) pt[k] = quad_mov<CTRL>(t[k]);
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < PAD; ++k) c[k] = __builtin_inff();
+#pragma unroll
+  for (int k = 0; k < P; ++k) c[PAD + k] = fmaxf(t[k], pt[P - 1 - k]);
+  ce_desc<PAD, 0, 4>(c); ce_desc<PAD, 1, 5>(c); ce_desc<PAD, 2, 6>(c); ce_desc<PAD, 3, 7>(c);
+  ce_desc<PAD, 0, 2>(c); ce_desc<PAD, 1, 3>(c); ce_desc<PAD, 4, 6>(c); ce_desc<PAD, 5, 7>(c);
+  ce_desc<PAD, 0, 1>(c); ce_desc<PAD, 2, 3>(c); ce_desc<PAD, 4, 5>(c); ce_desc<PAD, 6, 7>(c);
+#pragma unroll
+  for (int k = 0; k < P; ++k) t[k] = c[PAD + k];
+}
+
+// P-th largest of the union of this lane's and the partner's lists: the
+// minimum of the top-P multiset max(A_k, B_{P-1-k}).
+template <int P, int CTRL>
+__device__ __forceinline__ float top_merge_last(const float (&t)[P]) {
+  float a = __builtin_inff();
+#pragma unroll
+  for (int k = 0; k < P; ++k) a = fminf(a, fmaxf(t[k], quad_mov<CTRL>(t[P - 1 - k])));
+  return a;
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+__device__ __forceinline__ float comp(const float4& v, int c) {
+  return c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w));
+}
+
+}  // namespace qbk
+
+namespace qbk {
+
+// Packed per-workgroup histogram of E experts x 256 bins in LDS: two 16-bit
+// counters per dword.  Expert j = 4*quad + c lives in dword row
+// (j >> 1) = 2*quad + (c >> 1), half (j & 1) = (c & 1); the bin is XOR-ed
+// with (quad & 63) so the 64 lanes of one instruction, which hold distinct
+// quads, land in distinct banks even when their bins coincide.
+__device__ __forceinline__ uint32_t hist16_swizzle2(int quad) {
+  return uint32_t(quad & 63) * 0x01000100u;  // swizzle for both halves of a key pair
+}
+
+// Adds one (key pair) of experts 4*quad + {c0, c0+1} (c0 = 0 or 2) into the
+// packed LDS histogram by the high byte of each key.  `kp` is the key pair
+// already XOR-ed with hist16_swizzle2(quad).
+__device__ __forceinline__ void hist16_add_hi(uint32_t* lds, int quad, int c0, uint32_t kp) {
+  uint32_t* rowp = lds + quad * 512 + (c0 >> 1) * 256;
+  atomicAdd(rowp + ((kp >> 8) & 0xFFu), 1u);
+  atomicAdd(rowp + (kp >> 24), 0x10000u);
+}
+
+// Adds the packed LDS histogram into the global int32 histogram
+// out[E][256] (non-zero counters only, agent-scope atomics).
+template <int E>
+__device__ __forceinline__ void hist16_flush(const uint32_t* lds, int32_t* out, int tid, int nthreads) {
+  constexpr int HDW = (E / 2) * 256;
+  for (int d = tid; d < HDW; d += nthreads) {
+    const uint32_t v = lds[d];
+    if (v) {
+      const int pair = d >> 8;
+      const int quad = pair >> 1;
+      const int h = (d & 255) ^ (quad & 63);
+      const int j0 = 2 * pair;
+      if (v & 0xFFFFu) atomicAdd(out + j0 * 256 + h, int(v & 0xFFFFu));
+      if (v >> 16) atomicAdd(out + (j0 + 1) * 256 + h, int(v >> 16));
+    }
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void hist16_zero(uint32_t* lds, int tid, int nthreads) {
+  constexpr int HDW = (E / 2) * 256;
+  uint4* h4 = reinterpret_cast<uint4*>(lds);
+  for (int d = tid; d < HDW / 4; d += nthreads) h4[d] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+}  // namespace qbk

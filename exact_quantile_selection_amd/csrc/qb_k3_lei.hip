@@ -1,0 +1,148 @@
+// qb_k3_lei.hip -- the K3 uniform-bin histogram pass and the LEI gradient
+// offset.
+//
+// K3: "[Dev] Add global-batch quantile balancing" (Megatron-LM PR #6637),
+// sections "Quantile estimator" and "Implementation": 1000 uniform bins per
+// expert over [min(b) - 1, max(b) + 1], accumulated into an int32 [E, bins]
+// histogram.  The fp32 margin is binned directly (no bf16 rounding).
+// LEI: "Exact Quantile Balancing and Load-Error Injection for
+// Mixture-of-Experts" (summary page), LEI paragraph: add eta * rho_e to the
+// score gradient of expert e for every token of the batch.
+//
+// Layout of the K3 pass: E x 1000 int32 counters do not fit in LDS, so each
+// workgroup owns a slice of 16 experts (16 * n_bins int32 in LDS, 64 KB at
+// 1000 bins, two workgroups per CU) and a chunk of rows; 4 lanes read the
+// slice's 64 contiguous bytes of a row, 16 rows per load instruction.
+#include <algorithm>
+
+#include "qb_device.hpp"
+#include "qb_internal.hpp"
+
+namespace qbk {
+
+constexpr int kUHThreads = 512;
+constexpr int kUHWaves = kUHThreads / kWave;
+constexpr int kUHSlice = 16;                 // experts per workgroup
+constexpr int kUHRPI = kWave / (kUHSlice / 4);  // rows per load instruction
+constexpr int kUHUnroll = 4;
+constexpr int kUHStep = kUHWaves * kUHRPI * kUHUnroll;
+
+__global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
+    const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int E,
+    const float* __restrict__ bounds, int n_bins, int rows_per_wg, int wg_per_layer,
+    int32_t* __restrict__ hist_u) {
+  extern __shared__ int32_t lds_u[];  // [kUHSlice][n_bins]
+  const int n_slices = E / kUHSlice;
+  const int per_layer = n_slices * wg_per_layer;
+  const int layer = blockIdx.x / per_layer;
+  const int rem = blockIdx.x - layer * per_layer;
+  const int slice = rem % n_slices;
+  const int g = rem / n_slices;
+  const int64_t row0 = int64_t(g) * rows_per_wg;
+  const int64_t row_end = min(N, row0 + int64_t(rows_per_wg));
+  s += int64_t(layer) * N * E + slice * kUHSlice;
+  alpha += int64_t(layer) * N;
+  const int tid = threadIdx.x;
+  for (int d = tid; d < kUHSlice * n_bins; d += kUHThreads) lds_u[d] = 0;
+  const float lo = bounds[2 * layer];
+  const float hi = bounds[2 * layer + 1];
+  const float width = hi - lo;
+  const float inv_w = float(n_bins) / width;
+  const float fbins = float(n_bins);
+  __syncthreads();
+
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int q4 = lane & 3;
+  const int rsub = lane >> 2;
+  int32_t* cnt = lds_u + 4 * q4 * n_bins;
+  for (int64_t base = row0 + int64_t(wave) * kUHRPI * kUHUnroll; base < row_end;
+       base += int64_t(kUHStep)) {
+    float4 x[kUHUnroll];
+    float a[kUHUnroll];
+#pragma unroll
+    for (int u = 0; u < kUHUnroll; ++u) {
+      int64_t row = base + u * kUHRPI + rsub;
+      row = row < row_end ? row : row_end - 1;
+      x[u] = ld4(s + row * E + 4 * q4);
+      a[u] = alpha[row];
+    }
+#pragma unroll
+    for (int u = 0; u < kUHUnroll; ++u) {
+      if (base + u * kUHRPI + rsub < row_end) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float r = a[u] - comp(x[u], c);
+          const float t = (r - lo) * inv_w;
+          const int idx = !(t >= 0.0f) ? 0 : (t >= fbins ? n_bins - 1 : int(t));
+          atomicAdd(cnt + c * n_bins + idx, 1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  int32_t* out = hist_u + (int64_t(layer) * E + slice * kUHSlice) * n_bins;
+  for (int d = tid; d < kUHSlice * n_bins; d += kUHThreads)
+    if (lds_u[d]) atomicAdd(out + d, lds_u[d]);
+}
+
+int launch_uniform_hist(const float* s, const float* alpha, int L, int64_t N, int E,
+                        const float* bounds, int n_bins, int32_t* hist_u, hipStream_t st) {
+  // Row chunks per layer so that all layers' slices make about two
+  // workgroups per CU.
+  const int n_slices = E / kUHSlice;
+  const int64_t chunks = std::max<int64_t>(
+      1, (2 * int64_t(device_cu_count()) + int64_t(L) * n_slices - 1) / (int64_t(L) * n_slices));
+  const RowSplit sp = split_rows_chunks(N, chunks, kUHStep);
+  const int64_t blocks = int64_t(L) * n_slices * sp.wg_per_layer;
+  const size_t lds = size_t(kUHSlice) * size_t(n_bins) * sizeof(int32_t);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uniform_hist),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return int(e);
+  }
+  hipLaunchKernelGGL(k_uniform_hist, dim3(unsigned(blocks)), dim3(kUHThreads), lds, st, s, alpha, N,
+                     E, bounds, n_bins, sp.rows_per_wg, sp.wg_per_layer, hist_u);
+  return int(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
+constexpr int kLeiThreads = 256;
+
+__global__ __launch_bounds__(kLeiThreads) void k_lei(float* __restrict__ g,
+                                                     const int32_t* __restrict__ load, int64_t N,
+                                                     int E, int K, float eta) {
+  __shared__ float add[256];
+  const double M = double(N) * double(K) / double(E);
+  for (int e = threadIdx.x; e < E; e += kLeiThreads) {
+    const float rho = float((double(load[e]) - M) / M);
+    add[e] = eta * rho;
+  }
+  __syncthreads();
+  // The float4 stride of the grid is a multiple of E/4, so every thread
+  // keeps the same four experts.
+  const int64_t n4 = N * E / 4;
+  const int64_t stride = int64_t(gridDim.x) * kLeiThreads;
+  const int64_t i0 = int64_t(blockIdx.x) * kLeiThreads + threadIdx.x;
+  const int e0 = int((i0 * 4) % E);
+  const float a0 = add[e0], a1 = add[e0 + 1], a2 = add[e0 + 2], a3 = add[e0 + 3];
+  float4* g4 = reinterpret_cast<float4*>(g);
+  for (int64_t i = i0; i < n4; i += stride) {
+    float4 v = g4[i];
+    v.x = v.x + a0;
+    v.y = v.y + a1;
+    v.z = v.z + a2;
+    v.w = v.w + a3;
+    g4[i] = v;
+  }
+}
+
+int launch_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta, hipStream_t st) {
+  const int64_t n4 = N * E / 4;
+  const int64_t blocks = std::min<int64_t>(int64_t(device_cu_count()) * 8,
+                                           std::max<int64_t>(1, (n4 + kLeiThreads - 1) / kLeiThreads));
+  hipLaunchKernelGGL(k_lei, dim3(unsigned(blocks)), dim3(kLeiThreads), 0, st, g, load, N, E, K, eta);
+  return int(hipGetLastError());
+}
+
+}  // namespace qbk

@@ -1,0 +1,248 @@
+// qb_pass1.hip -- first pass over the score matrix: per-token top-(K+1) of
+// s + b (alpha), optional top-K load counts, and the fused high-byte
+// histogram of the bf16 margin keys.
+//
+// Method: "[Dev] Add global-batch quantile balancing" (Megatron-LM PR #6637),
+// section "Quantile estimator" (alpha = (k+1)-th largest of s + b, margin
+// r = alpha - s); "Exact Quantile Balancing and Load-Error Injection for
+// Mixture-of-Experts" (summary page), EQB paragraph (first radix pass: 256-bin
+// histogram of the high byte of the bf16 margins).
+//
+// Layout on gfx950: a row of E fp32 scores is split over LPR = E/64 lanes
+// (E <= 64: one lane per row), each lane holding V = min(E, 64) scores in
+// registers (V/4 float4 loads).  A wave therefore takes 64/LPR rows per trip.
+// The lanes of one row read 64 contiguous bytes per load; the starting
+// column block is rotated by the row index so that, in every later
+// instruction, the 64 lanes of the wave touch 64 distinct experts (distinct
+// LDS banks for the histogram atomics, distinct bias entries).
+//   * top-(K+1): per-lane insertion with v_med3_f32 (one op per list slot),
+//     then DPP merges across the row's lanes (bitonic), the last merge only
+//     producing the minimum of the merged top list, which is alpha.
+//   * histogram: keys of both halves of a packed bf16 pair are made in three
+//     integer ops; counters are 16-bit pairs in LDS (E*512 bytes), flushed to
+//     the global int32 histogram once per workgroup (<= 65535 rows each).
+#include "qb_device.hpp"
+#include "qb_internal.hpp"
+
+namespace qbk {
+
+// 16 waves per workgroup (<= 128 VGPRs each); the load-counting variant
+// keeps more state per lane and runs 8 waves (<= 256 VGPRs each).
+template <bool LOAD>
+constexpr int p1_waves() { return LOAD ? 8 : 16; }
+
+template <int E>
+struct P1Shape {
+  static constexpr int V = E < 64 ? E : 64;  // scores per lane
+  static constexpr int LPR = E / V;          // lanes per row
+  static constexpr int F4 = V / 4;           // float4 loads per lane
+  static constexpr int RPW = kWave / LPR;    // rows per wave trip
+  static constexpr int HDW = (E / 2) * 256;
+  static_assert(LPR == 1 || LPR == 2 || LPR == 4, "lanes per row");
+  static_assert((F4 & (F4 - 1)) == 0, "power-of-two loads per lane");
+};
+
+__device__ __forceinline__ uint64_t low_bits(int n) {
+  return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+}
+
+// Top-K membership of this lane's scores for one row, added to the LDS load
+// counters.  Members are v > alpha plus, when alpha's value occurs more than
+// once, the lowest-index elements equal to alpha up to K in total.  A lane's
+// element (u, c) has expert j = 4*(LPR*u + ql) + c; `eq` holds bit 4u+c for
+// elements equal to alpha, so bit order is j order within a lane.
+template <int E, int P>
+__device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], const float* lds_b,
+                                            int rho, int ql, int lane, float a, int K, bool valid,
+                                            int32_t* lds_load) {
+  using S = P1Shape<E>;
+  int gt = 0;
+  uint64_t eq = 0;
+#pragma unroll
+  for (int t = 0; t < S::F4; ++t) {
+    const int u = (t + rho) & (S::F4 - 1);
+    const int quad = S::LPR * u + ql;
+    const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float v = comp(x[t], c) + comp(bb, c);
+      gt += v > a;
+      if (v == a) eq |= 1ull << (4 * u + c);
+    }
+  }
+  int G = gt;
+  if constexpr (S::LPR >= 2) G += quad_mov_i<kQuadXor1>(G);
+  if constexpr (S::LPR == 4) G += quad_mov_i<kQuadXor2>(G);
+  const int need = K - G;  // equal-to-alpha elements that still belong to the top K
+  uint64_t M[S::LPR];
+#pragma unroll
+  for (int q2 = 0; q2 < S::LPR; ++q2) {
+    const int src = rho * S::LPR + q2;
+    const uint32_t lo = __shfl(uint32_t(eq), src);
+    const uint32_t hi = __shfl(uint32_t(eq >> 32), src);
+    M[q2] = (uint64_t(hi) << 32) | lo;
+  }
+  (void)lane;
+  if (!valid) return;
+#pragma unroll
+  for (int t = 0; t < S::F4; ++t) {
+    const int u = (t + rho) & (S::F4 - 1);
+    const int quad = S::LPR * u + ql;
+    const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float v = comp(x[t], c) + comp(bb, c);
+      bool member = v > a;
+      if (!member && need > 0 && v == a) {
+        int r = 0;
+#pragma unroll
+        for (int q2 = 0; q2 < S::LPR; ++q2) {
+          const int nb = q2 < ql ? 4 * (u + 1) : (q2 > ql ? 4 * u : 4 * u + c);
+          r += __popcll(M[q2] & low_bits(nb));
+        }
+        member = r < need;
+      }
+      if (member) atomicAdd(&lds_load[4 * quad + c], 1);
+    }
+  }
+}
+
+template <int E, int P, bool HIST, bool LOAD>
+__global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
+    const float* __restrict__ s, const float* __restrict__ b, int64_t N, int rows_per_wg,
+    int wg_per_layer, int K, float* __restrict__ alpha, int32_t* __restrict__ load,
+    int32_t* __restrict__ hist_hi) {
+  using S = P1Shape<E>;
+  constexpr int kWaves = p1_waves<LOAD>();
+  constexpr int kThreads = kWaves * kWave;
+  __shared__ uint32_t lds_hist[HIST ? S::HDW : 4];
+  __shared__ float lds_b[E];
+  __shared__ int32_t lds_load[E];
+
+  const int tid = threadIdx.x;
+  const int layer = blockIdx.x / wg_per_layer;
+  const int g = blockIdx.x - layer * wg_per_layer;
+  const int64_t row0 = int64_t(g) * rows_per_wg;
+  const int64_t row_end = min(N, row0 + int64_t(rows_per_wg));
+  s += int64_t(layer) * N * E;
+  b += int64_t(layer) * E;
+  alpha += int64_t(layer) * N;
+
+  if constexpr (HIST) hist16_zero<E>(lds_hist, tid, kThreads);
+  for (int j = tid; j < E; j += kThreads) {
+    lds_b[j] = b[j];
+    lds_load[j] = 0;
+  }
+  __syncthreads();
+
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int rho = lane / S::LPR;
+  const int ql = lane % S::LPR;
+
+  for (int64_t base = row0 + int64_t(wave) * S::RPW; base < row_end;
+       base += int64_t(kWaves) * S::RPW) {
+    const int64_t row = base + rho;
+    const bool valid = row < row_end;
+    const float* src = s + (valid ? row : row_end - 1) * E;
+    // The per-slot bias values, addresses and swizzles are loop-invariant;
+    // kept invariant they would be hoisted out of this loop and occupy ~100
+    // VGPRs.  An opaque copy of the rotation makes them cheap per-trip work.
+    int rot = rho;
+    asm volatile("" : "+v"(rot));
+    float4 x[S::F4];
+#pragma unroll
+    for (int t = 0; t < S::F4; ++t) {
+      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+      x[t] = ld4(src + 4 * quad);
+    }
+    float top[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) top[k] = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < S::F4; ++t) {
+      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+      const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
+      top_insert<P>(top, x[t].x + bb.x);
+      top_insert<P>(top, x[t].y + bb.y);
+      top_insert<P>(top, x[t].z + bb.z);
+      top_insert<P>(top, x[t].w + bb.w);
+    }
+    float a;
+    if constexpr (S::LPR == 1) {
+      a = top[P - 1];
+    } else if constexpr (S::LPR == 2) {
+      a = top_merge_last<P, kQuadXor1>(top);
+    } else {
+      top_merge<P, kQuadXor1>(top);
+      a = top_merge_last<P, kQuadXor2>(top);
+    }
+    if (valid && ql == 0) alpha[row] = a;
+    if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, lane, a, K, valid, lds_load);
+    if constexpr (HIST) {
+      if (valid) {
+#pragma unroll
+        for (int t = 0; t < S::F4; ++t) {
+          const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+          const uint32_t swz = hist16_swizzle2(quad);
+          hist16_add_hi(lds_hist, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
+          hist16_add_hi(lds_hist, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (HIST) hist16_flush<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads);
+  if constexpr (LOAD) {
+    for (int j = tid; j < E; j += kThreads)
+      if (lds_load[j]) atomicAdd(load + int64_t(layer) * E + j, lds_load[j]);
+  }
+}
+
+template <int E, int P, bool HIST, bool LOAD>
+static int launch_p1_v(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
+                       int32_t* load, int32_t* hist_hi, hipStream_t st) {
+  constexpr int kThreads = p1_waves<LOAD>() * kWave;
+  const RowSplit sp = split_rows(L, N, p1_waves<LOAD>() * P1Shape<E>::RPW, 4096);
+  hipLaunchKernelGGL((k_margins_topk<E, P, HIST, LOAD>), dim3(unsigned(sp.blocks)), dim3(kThreads),
+                     0, st, s, b, N, sp.rows_per_wg, sp.wg_per_layer, K, alpha, load, hist_hi);
+  return int(hipGetLastError());
+}
+
+template <int E, int P>
+static int launch_p1(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
+                     int32_t* load, int32_t* hist_hi, hipStream_t st) {
+  if (hist_hi && load) return launch_p1_v<E, P, true, true>(s, b, L, N, K, alpha, load, hist_hi, st);
+  if (hist_hi) return launch_p1_v<E, P, true, false>(s, b, L, N, K, alpha, load, hist_hi, st);
+  if (load) return launch_p1_v<E, P, false, true>(s, b, L, N, K, alpha, load, hist_hi, st);
+  return launch_p1_v<E, P, false, false>(s, b, L, N, K, alpha, load, hist_hi, st);
+}
+
+template <int E>
+static int launch_p1_k(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
+                       int32_t* load, int32_t* hist_hi, hipStream_t st) {
+  switch (K + 1) {
+    case 2: return launch_p1<E, 2>(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 3: return launch_p1<E, 3>(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 4: return launch_p1<E, 4>(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 5: return launch_p1<E, 5>(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 6: return launch_p1<E, 6>(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 7: return launch_p1<E, 7>(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 8: return launch_p1<E, 8>(s, b, L, N, K, alpha, load, hist_hi, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+#ifndef QB_P1_E
+#error "compile with -DQB_P1_E=<experts>: one translation unit per expert count"
+#endif
+
+#define QB_P1_CAT2(a, b) a##b
+#define QB_P1_CAT(a, b) QB_P1_CAT2(a, b)
+int QB_P1_CAT(launch_margins_topk_e, QB_P1_E)(const float* s, const float* b, int L, int64_t N,
+                                               int K, float* alpha, int32_t* load,
+                                               int32_t* hist_hi, hipStream_t st) {
+  return launch_p1_k<QB_P1_E>(s, b, L, N, K, alpha, load, hist_hi, st);
+}
+
+}  // namespace qbk

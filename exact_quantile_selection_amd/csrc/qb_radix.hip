@@ -1,0 +1,164 @@
+// qb_radix.hip -- streaming byte histograms of the bf16 margin keys from a
+// precomputed alpha: the high-byte pass, and the low-byte pass restricted to
+// each expert's selected high byte.
+//
+// Method: "Exact Quantile Balancing and Load-Error Injection for
+// Mixture-of-Experts" (summary page), EQB paragraph: histogram the high byte
+// into 256 bins, locate the bin holding the rank, then histogram the low byte
+// within that bin; concatenating the bytes gives the exact quantile.
+//
+// Layout on gfx950: lane l of a wave owns float4 column block (quad)
+// l % (E/4) of its row, so one load instruction covers 64*16 contiguous bytes
+// (one row at E=256).  Each lane keeps kUnroll rows of loads in flight.
+// Counters are the packed 16-bit LDS histogram of qb_device.hpp (bank
+// swizzle by quad), flushed once per workgroup.  A lane's experts are fixed
+// for the whole kernel, so the low-byte pass keeps their selected high bytes
+// in registers and filters with one compare per element.
+#include <algorithm>
+
+#include "qb_device.hpp"
+#include "qb_internal.hpp"
+
+namespace qbk {
+
+constexpr int kRHWaves = 16;
+constexpr int kRHThreads = kRHWaves * kWave;
+constexpr int kRHUnroll = 8;
+
+template <int E>
+struct RHShape {
+  static constexpr int QPR = E / 4;            // lanes per row
+  static constexpr int RPI = kWave / QPR;      // rows per load instruction
+  static constexpr int RPW = RPI * kRHUnroll;  // rows per wave trip
+  static constexpr int STEP = kRHWaves * RPW;  // rows per workgroup trip
+  static_assert(QPR <= kWave && (kWave % QPR) == 0, "row split");
+};
+
+template <int E, bool LO>
+__global__ __launch_bounds__(kRHThreads) void k_radix_hist(
+    const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int rows_per_wg,
+    int wg_per_layer, const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist) {
+  using S = RHShape<E>;
+  __shared__ uint32_t lds_hist[(E / 2) * 256];
+  const int tid = threadIdx.x;
+  const int layer = blockIdx.x / wg_per_layer;
+  const int g = blockIdx.x - layer * wg_per_layer;
+  const int64_t row0 = int64_t(g) * rows_per_wg;
+  const int64_t row_end = min(N, row0 + int64_t(rows_per_wg));
+  s += int64_t(layer) * N * E;
+  alpha += int64_t(layer) * N;
+
+  hist16_zero<E>(lds_hist, tid, kRHThreads);
+
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int quad = lane % S::QPR;
+  const int rsub = lane / S::QPR;
+  const uint32_t swz = hist16_swizzle2(quad);               // high bytes of a key pair
+  const uint32_t swzl = uint32_t(quad & 63) * 0x00010001u;  // low bytes of a key pair
+  uint32_t* rowp = lds_hist + quad * 512;
+  // Selected high byte of each of the lane's four experts; an invalid
+  // selection (< 0) becomes 0x100, which no byte equals.
+  uint32_t sel[4] = {0x100u, 0x100u, 0x100u, 0x100u};
+  if constexpr (LO) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int v = sel_hi[int64_t(layer) * E + 4 * quad + c];
+      sel[c] = (v >= 0 && v < 256) ? uint32_t(v) : 0x100u;
+    }
+  }
+  __syncthreads();
+
+  for (int64_t base = row0 + int64_t(wave) * S::RPW; base < row_end;
+       base += int64_t(kRHWaves) * S::RPW) {
+    float4 x[kRHUnroll];
+    float a[kRHUnroll];
+#pragma unroll
+    for (int u = 0; u < kRHUnroll; ++u) {
+      int64_t row = base + u * S::RPI + rsub;
+      row = row < row_end ? row : row_end - 1;
+      x[u] = ld4(s + row * E + 4 * quad);
+      a[u] = alpha[row];
+    }
+#pragma unroll
+    for (int u = 0; u < kRHUnroll; ++u) {
+      if (base + u * S::RPI + rsub < row_end) {
+        const uint32_t k01 = key2(bf16x2_rne(a[u] - x[u].x, a[u] - x[u].y));
+        const uint32_t k23 = key2(bf16x2_rne(a[u] - x[u].z, a[u] - x[u].w));
+        if constexpr (!LO) {
+          hist16_add_hi(lds_hist, quad, 0, k01 ^ swz);
+          hist16_add_hi(lds_hist, quad, 2, k23 ^ swz);
+        } else {
+          // low byte of the key, swizzled like the high-byte histogram
+          const uint32_t l01 = k01 ^ swzl, l23 = k23 ^ swzl;
+          if (((k01 >> 8) & 0xFFu) == sel[0]) atomicAdd(rowp + (l01 & 0xFFu), 1u);
+          if ((k01 >> 24) == sel[1]) atomicAdd(rowp + ((l01 >> 16) & 0xFFu), 0x10000u);
+          if (((k23 >> 8) & 0xFFu) == sel[2]) atomicAdd(rowp + 256 + (l23 & 0xFFu), 1u);
+          if ((k23 >> 24) == sel[3]) atomicAdd(rowp + 256 + ((l23 >> 16) & 0xFFu), 0x10000u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  hist16_flush<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads);
+}
+
+template <int E>
+static int launch_rh(bool lo, const float* s, const float* alpha, int L, int64_t N,
+                     const int32_t* sel_hi, int32_t* hist, hipStream_t st) {
+  const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, 4096);
+  if (lo)
+    hipLaunchKernelGGL((k_radix_hist<E, true>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
+                       s, alpha, N, sp.rows_per_wg, sp.wg_per_layer, sel_hi, hist);
+  else
+    hipLaunchKernelGGL((k_radix_hist<E, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
+                       s, alpha, N, sp.rows_per_wg, sp.wg_per_layer, sel_hi, hist);
+  return int(hipGetLastError());
+}
+
+int launch_radix_hist(bool lo, const float* s, const float* alpha, int L, int64_t N, int E,
+                      const int32_t* sel_hi, int32_t* hist, hipStream_t st) {
+  switch (E) {
+    case 16: return launch_rh<16>(lo, s, alpha, L, N, sel_hi, hist, st);
+    case 32: return launch_rh<32>(lo, s, alpha, L, N, sel_hi, hist, st);
+    case 64: return launch_rh<64>(lo, s, alpha, L, N, sel_hi, hist, st);
+    case 128: return launch_rh<128>(lo, s, alpha, L, N, sel_hi, hist, st);
+    case 256: return launch_rh<256>(lo, s, alpha, L, N, sel_hi, hist, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+// ---------------------------------------------------------------------------
+// Keys of every margin, token-major u16 [L][N][E] (same layout as s).
+constexpr int kMKThreads = 256;
+
+__global__ __launch_bounds__(kMKThreads) void k_margin_keys(const float* __restrict__ s,
+                                                            const float* __restrict__ alpha,
+                                                            int64_t N, int E,
+                                                            uint16_t* __restrict__ keys) {
+  const int64_t total4 = N * E / 4;  // float4 groups of one layer
+  const int layer = blockIdx.y;
+  s += int64_t(layer) * N * E;
+  alpha += int64_t(layer) * N;
+  keys += int64_t(layer) * N * E;
+  const int64_t stride = int64_t(gridDim.x) * kMKThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kMKThreads + threadIdx.x; i < total4; i += stride) {
+    const float4 x = ld4(s + 4 * i);
+    const float a = alpha[(4 * i) / E];
+    const uint32_t k01 = key2(bf16x2_rne(a - x.x, a - x.y));
+    const uint32_t k23 = key2(bf16x2_rne(a - x.z, a - x.w));
+    *reinterpret_cast<uint2*>(keys + 4 * i) = make_uint2(k01, k23);
+  }
+}
+
+int launch_margin_keys(const float* s, const float* alpha, int L, int64_t N, int E, uint16_t* keys,
+                       hipStream_t st) {
+  const int64_t total4 = N * E / 4;
+  const int64_t bx = std::min<int64_t>(int64_t(device_cu_count()) * 8,
+                                       std::max<int64_t>(1, (total4 + kMKThreads - 1) / kMKThreads));
+  hipLaunchKernelGGL(k_margin_keys, dim3(unsigned(bx), unsigned(L)), dim3(kMKThreads), 0, st, s, alpha,
+                     N, E, keys);
+  return int(hipGetLastError());
+}
+
+}  // namespace qbk

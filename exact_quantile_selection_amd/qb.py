@@ -1,0 +1,239 @@
+"""Thin Python binding of libqb's C ABI (include/qb.h), same names.
+
+Argument marshalling only: every function checks dtype / device / layout /
+shape of torch tensors, passes raw device pointers and the current HIP
+stream, and raises ``QBError`` on a non-zero status.  All arithmetic runs in
+the HIP kernels of libqb.so; there is no CPU fallback -- a missing library
+is an error.
+
+Tensors may carry a leading layer dimension (s [L, N, E], b [L, E],
+alpha [L, N], ...) or omit it for one layer.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqb.so")
+
+QB_OK, QB_EINVAL, QB_EUNSUPPORTED, QB_EHIP = 0, -1, -2, -3
+QB_SELECT_HI, QB_SELECT_LO, QB_SELECT_UNIFORM = 0, 1, 2
+QB_ERR_ROW_TOTALS, QB_ERR_EMPTY, QB_ERR_RANK = 1, 2, 4
+
+SUPPORTED_E = (16, 32, 64, 128, 256)
+MAX_K = 7
+
+_lib = None
+
+
+class QBError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> C.CDLL:
+    """Load libqb.so once.  torch is imported first so that libqb binds to
+    the HIP runtime torch already mapped (one runtime per process)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(or python exact_quantile_selection_amd/build.py)")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = C.c_void_p, C.c_int, C.c_int64, C.c_float
+        sig = {
+            "qb_margins_topk": [vp, vp, i32, i64, i32, i32, vp, vp, vp, vp],
+            "qb_radix_hist_hi": [vp, vp, i32, i64, i32, vp, vp],
+            "qb_radix_hist_lo": [vp, vp, i32, i64, i32, vp, vp, vp],
+            "qb_margin_keys": [vp, vp, i32, i64, i32, vp, vp],
+            "qb_select_update": [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp],
+            "qb_uniform_hist": [vp, vp, i32, i64, i32, vp, i32, vp, vp],
+            "qb_bias_bounds": [vp, i32, i32, vp, vp],
+            "qb_fill_i32": [vp, i64, C.c_int32, vp],
+            "qb_lei_grad": [vp, vp, i64, i32, i32, f32, vp],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = C.c_int
+        L.qb_status_string.argtypes = [C.c_int]
+        L.qb_status_string.restype = C.c_char_p
+        L.qb_last_error.argtypes = []
+        L.qb_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != QB_OK:
+        L = lib()
+        raise QBError(rc, f"{L.qb_status_string(rc).decode()}: {L.qb_last_error().decode()}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t, dtype, name, shape=None, opt=False):
+    if t is None:
+        if opt:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _lne(s):
+    if s.dim() == 2:
+        return 1, s.shape[0], s.shape[1], ()
+    if s.dim() == 3:
+        return s.shape[0], s.shape[1], s.shape[2], (s.shape[0],)
+    raise ValueError(f"s must be [N, E] or [L, N, E], got {tuple(s.shape)}")
+
+
+def qb_margins_topk(s, b, K, alpha, load=None, hist_hi=None, stream=None):
+    L, N, E, lead = _lne(s)
+    rc = lib().qb_margins_topk(
+        _ptr(s, torch.float32, "s"), _ptr(b, torch.float32, "b", lead + (E,)), L, N, E, K,
+        _ptr(alpha, torch.float32, "alpha", lead + (N,)),
+        _ptr(load, torch.int32, "load", lead + (E,), opt=True),
+        _ptr(hist_hi, torch.int32, "hist_hi", lead + (E, 256), opt=True), _stream(stream))
+    _check(rc)
+
+
+def qb_radix_hist_hi(s, alpha, hist_hi, stream=None):
+    L, N, E, lead = _lne(s)
+    _check(lib().qb_radix_hist_hi(
+        _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
+        _ptr(hist_hi, torch.int32, "hist_hi", lead + (E, 256)), _stream(stream)))
+
+
+def qb_radix_hist_lo(s, alpha, sel_hi, hist_lo, stream=None):
+    L, N, E, lead = _lne(s)
+    _check(lib().qb_radix_hist_lo(
+        _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
+        _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)),
+        _ptr(hist_lo, torch.int32, "hist_lo", lead + (E, 256)), _stream(stream)))
+
+
+def qb_margin_keys(s, alpha, keys, stream=None):
+    L, N, E, lead = _lne(s)
+    _check(lib().qb_margin_keys(
+        _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
+        _ptr(keys, torch.uint16, "keys", lead + (N, E)), _stream(stream)))
+
+
+def qb_select_update(phase, K, hist, sel_hi=None, rank_lo=None, key_out=None, q_out=None, b=None,
+                     bounds=None, err=None, stream=None):
+    if hist.dim() == 2:
+        L, lead = 1, ()
+    elif hist.dim() == 3:
+        L, lead = hist.shape[0], (hist.shape[0],)
+    else:
+        raise ValueError("hist must be [E, bins] or [L, E, bins]")
+    E, n_bins = hist.shape[-2], hist.shape[-1]
+    _check(lib().qb_select_update(
+        phase, L, E, K, _ptr(hist, torch.int32, "hist"), n_bins,
+        _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,), opt=True),
+        _ptr(rank_lo, torch.int32, "rank_lo", lead + (E,), opt=True),
+        _ptr(key_out, torch.uint16, "key_out", lead + (E,), opt=True),
+        _ptr(q_out, torch.float32, "q_out", lead + (E,), opt=True),
+        _ptr(b, torch.float32, "b", lead + (E,), opt=True),
+        _ptr(bounds, torch.float32, "bounds", lead + (2,), opt=True),
+        _ptr(err, torch.int32, "err", (1,), opt=True), _stream(stream)))
+
+
+def qb_uniform_hist(s, alpha, bounds, hist_u, stream=None):
+    L, N, E, lead = _lne(s)
+    n_bins = hist_u.shape[-1]
+    _check(lib().qb_uniform_hist(
+        _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
+        _ptr(bounds, torch.float32, "bounds", lead + (2,)), n_bins,
+        _ptr(hist_u, torch.int32, "hist_u", lead + (E, n_bins)), _stream(stream)))
+
+
+def qb_bias_bounds(b, bounds, stream=None):
+    L, E = (1, b.shape[0]) if b.dim() == 1 else (b.shape[0], b.shape[1])
+    lead = () if b.dim() == 1 else (L,)
+    _check(lib().qb_bias_bounds(_ptr(b, torch.float32, "b"), L, E,
+                                _ptr(bounds, torch.float32, "bounds", lead + (2,)), _stream(stream)))
+
+
+def qb_fill_i32(t, value=0, stream=None):
+    _check(lib().qb_fill_i32(_ptr(t, torch.int32, "t"), t.numel(), int(value), _stream(stream)))
+
+
+def qb_lei_grad(g, load, K, eta, stream=None):
+    N, E = g.shape
+    _check(lib().qb_lei_grad(_ptr(g, torch.float32, "g"), _ptr(load, torch.int32, "load", (E,)),
+                             N, E, K, float(eta), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Composition of the calls above for one global batch (no arithmetic here).
+
+class EqbBuffers:
+    """Device buffers of one EQB update over L layers of E experts."""
+
+    def __init__(self, L: int, E: int, device="cuda", lead: bool = True):
+        shp = (L,) if lead else ()
+        kw = dict(device=device)
+        self.hist_hi = torch.zeros(shp + (E, 256), dtype=torch.int32, **kw)
+        self.hist_lo = torch.zeros(shp + (E, 256), dtype=torch.int32, **kw)
+        self.sel_hi = torch.zeros(shp + (E,), dtype=torch.int32, **kw)
+        self.rank_lo = torch.zeros(shp + (E,), dtype=torch.int32, **kw)
+        self.key = torch.zeros(shp + (E,), dtype=torch.uint16, **kw)
+        self.q = torch.zeros(shp + (E,), dtype=torch.float32, **kw)
+        self.bounds = torch.zeros(shp + (2,), dtype=torch.float32, **kw)
+        self.err = torch.zeros((1,), dtype=torch.int32, **kw)
+
+    def reset(self, stream=None):
+        """In-place reset of the accumulated histograms (addresses unchanged)."""
+        qb_fill_i32(self.hist_hi, 0, stream)
+        qb_fill_i32(self.hist_lo, 0, stream)
+        qb_fill_i32(self.err, 0, stream)
+
+
+def eqb_update(s, b, K, alpha, buf: EqbBuffers, load=None, stream=None):
+    """One exact quantile-balancing update: pass 1 (alpha + high-byte
+    histogram), high-byte select, pass 2 (low-byte histogram), low-byte select
+    and the in-place bias update.  Histograms must be zero on entry."""
+    qb_margins_topk(s, b, K, alpha, load=load, hist_hi=buf.hist_hi, stream=stream)
+    qb_select_update(QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                     err=buf.err, stream=stream)
+    qb_radix_hist_lo(s, alpha, buf.sel_hi, buf.hist_lo, stream=stream)
+    qb_select_update(QB_SELECT_LO, K, buf.hist_lo, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                     key_out=buf.key, q_out=buf.q, b=b, bounds=buf.bounds, err=buf.err,
+                     stream=stream)
+
+
+def k3_update(s, b, K, alpha, bounds, hist_u, q_out=None, err=None, stream=None):
+    """One K3 update: alpha pass, uniform-bin pass over the current bounds,
+    select + in-place bias/bounds update.  hist_u must be zero on entry."""
+    qb_margins_topk(s, b, K, alpha, stream=stream)
+    qb_uniform_hist(s, alpha, bounds, hist_u, stream=stream)
+    qb_select_update(QB_SELECT_UNIFORM, K, hist_u, q_out=q_out, b=b, bounds=bounds, err=err,
+                     stream=stream)
+
+
+def runtime_libraries():
+    """Paths of HIP runtime libraries mapped into this process."""
+    out = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                out.add(line.split()[-1])
+    return sorted(out)

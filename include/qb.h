@@ -1,0 +1,190 @@
+/*
+ * qb.h -- C ABI of libqb, the MI355X (gfx950) quantile-balancing bias update
+ * for an auxiliary-loss-free MoE router.
+ *
+ * What is computed (per layer, N tokens, E experts, top-K routing):
+ *   alpha[i]   = (K+1)-th largest of s[i,:] + b[:] (duplicates counted)
+ *   r[i,j]     = fl32(alpha[i] - s[i,j])
+ *   key[i,j]   = order-preserving 16-bit key of bf16_rne(r[i,j])
+ *   q[j]       = value of the key of rank m = ceil(K*N/E) in expert j's column
+ *   b_next[j]  = fl32((double)q[j] - mean_j (double)q[j]); written over b
+ *   bounds     = [fl32(min b_next - 1), fl32(max b_next + 1)]
+ * Sources: "[Dev] Add global-batch quantile balancing" (Megatron-LM pull
+ * request #6637), sections "Quantile estimator" and "Implementation"; "Exact
+ * Quantile Balancing and Load-Error Injection for Mixture-of-Experts" (paper
+ * summary page), EQB paragraph (two-pass byte radix select over the bf16
+ * margins) and LEI paragraph.
+ *
+ * The exact quantile is reached in two passes over the score matrix:
+ *   1. qb_margins_topk (alpha + high-byte histogram of the keys)
+ *   2. qb_select_update(QB_SELECT_HI)   -> high byte + residual rank per expert
+ *   3. qb_radix_hist_lo                 (low-byte histogram inside that bin)
+ *   4. qb_select_update(QB_SELECT_LO)   -> key, q, b_next in place, bounds
+ * The K3 mode (1000 uniform bins over the current bounds) is
+ *   qb_margins_topk (alpha only) -> qb_uniform_hist -> qb_select_update(UNIFORM).
+ *
+ * Conventions shared by every call:
+ *   - Pointers are DEVICE pointers owned by the caller; the library keeps no
+ *     reference after the call returns and allocates no memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronises the host, so a sequence of calls can be
+ *     captured in a HIP graph.
+ *   - Arrays are dense row-major with layers outermost:
+ *       s       float  [L][N][E]   (16-byte aligned; one token's scores contiguous)
+ *       b       float  [L][E]
+ *       alpha   float  [L][N]
+ *       load    int32  [L][E]
+ *       hist_hi int32  [L][E][256], hist_lo int32 [L][E][256]
+ *       hist_u  int32  [L][E][n_bins]
+ *       sel_hi, rank_lo int32 [L][E];  key_out uint16 [L][E]; q_out float [L][E]
+ *       bounds  float  [L][2]  ({lo, hi})
+ *   - Histograms and loads are ACCUMULATED (+=) so that several token chunks
+ *     (microbatches) of one global batch can be added into one buffer.  The
+ *     caller clears them in place (qb_fill_i32) after the update; buffer
+ *     addresses never change.
+ *   - Scores are sigmoid outputs: finite, >= +0.  Bias values are finite.
+ *     NaN/Inf inputs give unspecified (but memory-safe) results.
+ *   - Supported shapes: E in {16, 32, 64, 128, 256}; 1 <= K <= 7 and K < E;
+ *     1 <= N < 2^31; L >= 1; n_bins in [1, 2048].
+ *   - Return value: QB_OK, or a negative status; on error nothing is launched.
+ *     qb_status_string() names a status; qb_last_error() gives the detailed
+ *     message of the calling thread's last failed call (expected shapes
+ *     included).
+ */
+#ifndef QB_H
+#define QB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QB_API __attribute__((visibility("default")))
+
+typedef struct ihipStream_t* qb_stream_t; /* same type as hipStream_t */
+
+enum {
+  QB_OK = 0,
+  QB_EINVAL = -1,       /* null required pointer, bad size, bad alignment */
+  QB_EUNSUPPORTED = -2, /* E or K outside the compiled instantiations */
+  QB_EHIP = -3          /* the HIP runtime refused the launch */
+};
+
+enum { QB_SELECT_HI = 0, QB_SELECT_LO = 1, QB_SELECT_UNIFORM = 2 };
+
+/* Device-side error bits OR-ed into qb_select_update's optional err word. */
+enum {
+  QB_ERR_ROW_TOTALS = 1, /* expert rows of the histogram do not share one total */
+  QB_ERR_EMPTY = 2,      /* the histogram holds no token */
+  QB_ERR_RANK = 4        /* no bin reaches the rank (histogram inconsistent) */
+};
+
+/*
+ * Pass 1.  For every token: v_j = fl32(s_ij + b_j); alpha_i = (K+1)-th
+ * largest v (IEEE totalOrder, duplicates counted).  "[Dev] Add global-batch
+ * quantile balancing", section "Quantile estimator".
+ *   alpha   out [L][N], overwritten.
+ *   load    nullable; += 1 for each expert among the first K of the order
+ *           (larger v first, equal v by lower expert index).  These are the
+ *           per-expert top-K counts the LEI paragraph of the EQB summary page
+ *           turns into relative load errors.
+ *   hist_hi nullable; if given, hist_hi[l][j][key_ij >> 8] += 1 for every
+ *           (i, j) -- the first radix pass of the EQB paragraph, fused so the
+ *           scores are read once here.
+ */
+QB_API int qb_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
+                           float* alpha, int32_t* load, int32_t* hist_hi, qb_stream_t stream);
+
+/*
+ * First radix pass from a precomputed alpha (EQB paragraph):
+ * hist_hi[l][j][key_ij >> 8] += 1 with key from r = fl32(alpha_i - s_ij).
+ */
+QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N, int E,
+                            int32_t* hist_hi, qb_stream_t stream);
+
+/*
+ * Second radix pass (EQB paragraph): for keys whose high byte equals
+ * sel_hi[l][j] (from QB_SELECT_HI), hist_lo[l][j][key & 0xFF] += 1.
+ * sel_hi entries < 0 (invalid selection) match nothing.
+ */
+QB_API int qb_radix_hist_lo(const float* s, const float* alpha, int L, int64_t N, int E,
+                            const int32_t* sel_hi, int32_t* hist_lo, qb_stream_t stream);
+
+/*
+ * The 16-bit keys themselves, keys[l][i][j] = key of bf16_rne(fl32(alpha_i -
+ * s_ij)) (EQB paragraph: bf16 bit patterns, order-preserving), uint16
+ * [L][N][E], 8-byte aligned.  For inspection and for callers that keep the
+ * keys instead of re-reading the scores.
+ */
+QB_API int qb_margin_keys(const float* s, const float* alpha, int L, int64_t N, int E,
+                          uint16_t* keys, qb_stream_t stream);
+
+/*
+ * Rank scans and the bias update, one workgroup per layer.  The token count
+ * is read from expert 0's histogram row (every token adds exactly one margin
+ * per expert: review thread of Megatron-LM PR #6637); m = ceil(K * total / E).
+ *   QB_SELECT_HI:  hist = hist_hi.  sel_hi[l][j] = first bin h whose running
+ *                  count reaches m; rank_lo[l][j] = m - count below h.
+ *   QB_SELECT_LO:  hist = hist_lo; reads sel_hi, rank_lo.  key = sel_hi << 8 |
+ *                  first low byte whose running count reaches rank_lo; q =
+ *                  bf16 value of the key; b <- q - mean(q) (float64 mean in
+ *                  expert order, rounded once); bounds <- [min - 1, max + 1].
+ *                  ("Quantile estimator": b_next and its mean-centring; the
+ *                  in-place update of "Implementation".)
+ *   QB_SELECT_UNIFORM: hist = hist_u with n_bins bins over the CURRENT bounds
+ *                  (read, then overwritten with the next range); q = lo + w *
+ *                  (c + (m - below) / count[c]) in float64 (w = (hi-lo)/n_bins,
+ *                  c = first bin reaching m), then centring as above.
+ *   key_out, q_out, err: nullable.  err receives QB_ERR_* bits (atomic OR);
+ *   a layer with an error keeps its b and bounds unchanged.
+ */
+QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist, int n_bins,
+                            int32_t* sel_hi, int32_t* rank_lo, uint16_t* key_out,
+                            float* q_out, float* b, float* bounds, int32_t* err,
+                            qb_stream_t stream);
+
+/*
+ * K3 mode binning ("[Dev] Add global-batch quantile balancing", sections
+ * "Quantile estimator" and "Implementation"): for the fp32 margin r,
+ * bin = clamp(floor(fl32(fl32(r - lo) * fl32(n_bins / fl32(hi - lo)))), 0,
+ * n_bins - 1) with {lo, hi} = bounds[l]; hist_u[l][j][bin] += 1.
+ */
+QB_API int qb_uniform_hist(const float* s, const float* alpha, int L, int64_t N, int E,
+                           const float* bounds, int n_bins, int32_t* hist_u, qb_stream_t stream);
+
+/*
+ * Histogram range from a bias vector: bounds[l] = {fl32(min b - 1),
+ * fl32(max b + 1)} (section "Quantile estimator").  Seeds the K3 mode.
+ */
+QB_API int qb_bias_bounds(const float* b, int L, int E, float* bounds, qb_stream_t stream);
+
+/*
+ * In-place reset of int32 buffers (histograms, loads) by a fill kernel, so a
+ * captured graph holds no memset node.  "Implementation": reset the
+ * histogram without changing buffer addresses.
+ */
+QB_API int qb_fill_i32(int32_t* dst, int64_t count, int32_t value, qb_stream_t stream);
+
+/*
+ * LEI ("Exact Quantile Balancing and Load-Error Injection for
+ * Mixture-of-Experts", summary page, LEI paragraph): with M = N*K/E,
+ * rho_e = fl32((load_e - M) / M) in float64, add_e = fl32(eta * rho_e),
+ * g[i][e] = fl32(g[i][e] + add_e) for every token i.  g: float [N][E] in/out
+ * (16-byte aligned); load: int32 [E].
+ */
+QB_API int qb_lei_grad(float* g, const int32_t* load, int64_t N, int E, int K, float eta,
+                       qb_stream_t stream);
+
+/* Short name of a status code (static storage). */
+QB_API const char* qb_status_string(int status);
+
+/* Detailed message of this thread's last failed call ("" if none). */
+QB_API const char* qb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QB_H */

@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+exactly what include/qb.h declares, and rejects bad arguments with the
+documented status codes before touching the device."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qb.h")
+LIB = os.path.join(ROOT, "exact_quantile_selection_amd", "libqb.so")
+
+
+@pytest.fixture(scope="module")
+def libqb():
+    if not os.path.exists(LIB):
+        from exact_quantile_selection_amd import build
+
+        build.build()
+    import torch  # noqa: F401  (the binding always loads torch's HIP runtime first)
+
+    from exact_quantile_selection_amd import qb
+
+    return qb.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"QB_API\s+[\w\s\*]+?\b(qb_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("qb_margins_topk", "qb_radix_hist_hi", "qb_radix_hist_lo", "qb_select_update",
+              "qb_uniform_hist", "qb_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(libqb):
+    for n in declared_functions():
+        assert hasattr(libqb, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r" T (qb_\w+)", out)))
+    assert exported == declared_functions()
+
+
+def _last(libqb):
+    return libqb.qb_last_error().decode()
+
+
+def test_invalid_arguments_are_rejected_without_launch(libqb):
+    from exact_quantile_selection_amd import qb
+
+    fake = 0x1000  # never dereferenced: validation fails first
+    rc = libqb.qb_margins_topk(None, fake, 1, 1024, 256, 6, fake, None, None, None)
+    assert rc == qb.QB_EINVAL and "s is NULL" in _last(libqb)
+    rc = libqb.qb_margins_topk(fake, fake, 1, 1024, 48, 6, fake, None, None, None)
+    assert rc == qb.QB_EUNSUPPORTED and "E=48" in _last(libqb)
+    rc = libqb.qb_margins_topk(fake, fake, 1, 1024, 256, 8, fake, None, None, None)
+    assert rc == qb.QB_EUNSUPPORTED and "K=8" in _last(libqb)
+    rc = libqb.qb_margins_topk(fake, fake, 1, 1024, 16, 16, fake, None, None, None)
+    assert rc == qb.QB_EINVAL and "K=16" in _last(libqb)
+    rc = libqb.qb_margins_topk(fake + 4, fake, 1, 1024, 256, 6, fake, None, None, None)
+    assert rc == qb.QB_EINVAL and "16-byte aligned" in _last(libqb)
+    rc = libqb.qb_margins_topk(fake, fake, 1, 0, 256, 6, fake, None, None, None)
+    assert rc == qb.QB_EINVAL and "N=0" in _last(libqb)
+    rc = libqb.qb_margins_topk(fake, fake, 0, 10, 256, 6, fake, None, None, None)
+    assert rc == qb.QB_EINVAL and "L=0" in _last(libqb)
+    rc = libqb.qb_radix_hist_lo(fake, fake, 1, 10, 256, None, fake, None)
+    assert rc == qb.QB_EINVAL and "sel_hi" in _last(libqb)
+    rc = libqb.qb_select_update(7, 1, 256, 6, fake, 256, fake, fake, None, None, fake, fake, None, None)
+    assert rc == qb.QB_EINVAL and "phase=7" in _last(libqb)
+    rc = libqb.qb_select_update(qb.QB_SELECT_LO, 1, 256, 6, fake, 256, fake, fake, None, None, None,
+                                fake, None, None)
+    assert rc == qb.QB_EINVAL and "[L=1][E=256]" in _last(libqb)
+    rc = libqb.qb_select_update(qb.QB_SELECT_UNIFORM, 1, 256, 6, fake, 4096, None, None, None, None,
+                                fake, fake, None, None)
+    assert rc == qb.QB_EINVAL and "n_bins=4096" in _last(libqb)
+    rc = libqb.qb_uniform_hist(fake, fake, 1, 10, 256, None, 1000, fake, None)
+    assert rc == qb.QB_EINVAL
+    rc = libqb.qb_lei_grad(fake, fake, 10, 100, 6, C.c_float(1e-5), None)
+    assert rc == qb.QB_EUNSUPPORTED
+    rc = libqb.qb_margin_keys(fake, fake, 1, 10, 256, fake + 2, None)
+    assert rc == qb.QB_EINVAL and "8-byte aligned" in _last(libqb)
+    assert libqb.qb_fill_i32(None, 0, 0, None) == qb.QB_OK  # empty fill is a no-op
+    assert libqb.qb_fill_i32(None, 5, 0, None) == qb.QB_EINVAL
+    for st in (0, -1, -2, -3):
+        assert libqb.qb_status_string(st).startswith(b"QB_")
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    from exact_quantile_selection_amd import qb
+
+    monkeypatch.setattr(qb, "_lib", None)
+    monkeypatch.setattr(qb, "LIB_PATH", "/nonexistent/libqb.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        qb.lib()
+
+
+def test_product_code_never_touches_the_oracle():
+    """The package (library sources and binding) neither imports, links nor
+    loads anything under oracle/."""
+    pkg = os.path.join(ROOT, "exact_quantile_selection_amd")
+    pat = re.compile(r"(from\s+oracle|import\s+oracle|liboracle|qb_oracle|oracle/)")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat.search(text), f

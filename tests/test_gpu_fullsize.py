@@ -1,0 +1,100 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times: the 65,536-token single layer (EQB and K3), the 1,048,576-
+token skewed layer with forced bf16 ties, and the 48-layer step (every layer
+checked against invariants, three sampled layers against the full oracle)."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+from exact_quantile_selection_amd import qb, synth
+
+import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qb.lib()
+
+
+def test_single_layer_eqb_and_k3(O):
+    s, b, K = synth.single()
+    G.say(f"single EQB N={s.shape[0]}")
+    G.compare_eqb(G.run_eqb(s, b, K), O.eqb_layer(s, b, K), tag="single ")
+    bounds = O.bounds_of(b)
+    ref = O.k3_layer(s, b, K, bounds, 1000)
+    G.say("single K3")
+    got = G.run_k3(s, b, K, bounds, 1000)
+    assert got["err"] == 0
+    for k in ("alpha", "hist_u", "q", "b_next", "bounds"):
+        G.assert_same(f"k3 {k}", got[k], ref[k])
+
+
+@pytest.mark.timeout(600)
+def test_skew_full_size(O):
+    s, b, K = synth.skew()
+    G.say(f"skew N={s.shape[0]} E={s.shape[1]}")
+    got = G.run_eqb(s, b, K)
+    ref = O.eqb_layer(s, b, K)
+    G.compare_eqb(got, ref, tag="skew ")
+
+
+def _invariants(l, N, E, K, hist_hi, sel_hi, rank_lo, hist_lo, key, b_next):
+    m = -(-K * N // E)
+    assert (hist_hi.sum(axis=1) == N).all(), f"layer {l}: hist_hi row totals"
+    C = np.cumsum(hist_hi, axis=1)
+    for j in range(E):
+        sel = sel_hi[j]
+        below = C[j, sel - 1] if sel else 0
+        assert below < m <= C[j, sel], f"layer {l} expert {j}: high-byte bin"
+        assert rank_lo[j] == m - below
+        assert hist_lo[j].sum() == hist_hi[j, sel]
+        Cl = np.cumsum(hist_lo[j])
+        lo = int(key[j]) & 0xFF
+        assert int(key[j]) >> 8 == sel
+        assert (Cl[lo - 1] if lo else 0) < rank_lo[j] <= Cl[lo], f"layer {l} expert {j}: low byte"
+    half_ulp = 0.5 * np.spacing(np.abs(b_next).max())
+    assert abs(b_next.astype(np.float64).sum()) <= E * half_ulp
+
+
+@pytest.mark.timeout(900)
+def test_step_48_layers(O):
+    p = synth.WORKLOADS["step"]
+    L, N, E, K = p["L"], p["N"], p["E"], p["K"]
+    s = torch.empty((L, N, E), dtype=torch.float32, device=G.DEV)
+    b = torch.empty((L, E), dtype=torch.float32, device=G.DEV)
+    G.say(f"step: generating {L} layers")
+    sampled = {0: None, 23: None, 47: None}
+
+    def gen(l):
+        sl, bl, _ = synth.step_layer(l)
+        return l, sl, bl
+
+    with ThreadPoolExecutor(8) as ex:
+        for l, sl, bl in ex.map(gen, range(L)):
+            s[l].copy_(torch.from_numpy(sl))
+            b[l].copy_(torch.from_numpy(bl))
+            if l in sampled:
+                sampled[l] = (sl, bl)
+    alpha = torch.empty((L, N), dtype=torch.float32, device=G.DEV)
+    buf = qb.EqbBuffers(L, E, device=G.DEV)
+    G.say("step: EQB over 48 layers")
+    qb.eqb_update(s, b, K, alpha, buf)
+    torch.cuda.synchronize()
+    assert int(buf.err.item()) == 0
+    hh, hl = G.host(buf.hist_hi), G.host(buf.hist_lo)
+    sel, rk, key, bn = G.host(buf.sel_hi), G.host(buf.rank_lo), G.host(buf.key), G.host(b)
+    for l in range(L):
+        _invariants(l, N, E, K, hh[l], sel[l], rk[l], hl[l], key[l], bn[l])
+    for l, (sl, bl) in sampled.items():
+        G.say(f"step: oracle layer {l}")
+        ref = O.eqb_layer(sl, bl, K)
+        got = dict(alpha=G.host(alpha[l]), hist_hi=hh[l], sel_hi=sel[l], rank_lo=rk[l],
+                   hist_lo=hl[l], key=key[l], q=G.host(buf.q[l]), b_next=bn[l],
+                   bounds=G.host(buf.bounds[l]), err=0)
+        G.compare_eqb(got, ref, with_load=False, tag=f"step layer {l} ")

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, bit
+for bit, on seeded inputs that span several workgroup tiles and a ragged
+tail, plus accumulation, reset, error and graph-capture behaviour."""
+import numpy as np
+import pytest
+import torch
+
+from exact_quantile_selection_amd import qb, synth
+
+pytestmark = pytest.mark.gpu
+
+import gpu_util as G
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qb.lib()
+
+
+def test_single_hip_runtime():
+    torch.zeros(1, device="cuda")
+    libs = qb.runtime_libraries()
+    assert len(libs) == 1, libs
+
+
+def test_tiny_workload(O):
+    s, b, K = synth.tiny()
+    G.say(f"tiny N={s.shape[0]} E={s.shape[1]} K={K}")
+    G.compare_eqb(G.run_eqb(s, b, K), O.eqb_layer(s, b, K), tag="tiny ")
+
+
+SWEEP = [
+    # (N, E, K, quant)
+    (1, 16, 2, None), (5, 16, 7, None), (1000, 16, 2, 8.0), (4097, 16, 3, None),
+    (1, 32, 1, None), (777, 32, 4, 16.0), (3000, 32, 7, None),
+    (2, 64, 6, None), (1025, 64, 5, 64.0), (5000, 64, 1, None),
+    (3, 128, 2, None), (999, 128, 6, 32.0), (4100, 128, 7, None),
+    (1, 256, 6, None), (17, 256, 6, 64.0), (4097, 256, 6, None), (6000, 256, 1, 4.0),
+    (2500, 256, 7, 64.0), (1500, 256, 3, None),
+]
+
+
+@pytest.mark.parametrize("N,E,K,quant", SWEEP)
+def test_eqb_sweep(O, N, E, K, quant):
+    s, b, _ = synth.random_case(21, N, E, K, quant=quant)
+    G.say(f"sweep N={N} E={E} K={K} quant={quant}")
+    G.compare_eqb(G.run_eqb(s, b, K), O.eqb_layer(s, b, K), tag=f"N={N} E={E} K={K} ")
+
+
+def test_ties_at_alpha_and_constant_rows(O):
+    """Heavy duplicates: many tokens with identical scores (alpha tied across
+    experts, loads decided by the lower index), constant columns."""
+    N, E, K = 3000, 64, 6
+    rng = np.random.default_rng(5)
+    s = (rng.integers(0, 4, (N, E)) / 4.0).astype(np.float32)
+    s[::7] = 0.5
+    s[:, 3] = 0.25
+    b = np.zeros(E, np.float32)
+    b[10:20] = 0.25
+    G.say("ties")
+    G.compare_eqb(G.run_eqb(s, b, K), O.eqb_layer(s, b, K), tag="ties ")
+
+
+def test_multi_layer_batch(O):
+    L, N, E, K = 3, 2049, 256, 6
+    cases = [synth.random_case(30 + l, N, E, K, quant=64.0 if l == 1 else None) for l in range(L)]
+    s = G.dev(np.stack([c[0] for c in cases]))
+    b = G.dev(np.stack([c[1] for c in cases]))
+    alpha = torch.empty((L, N), dtype=torch.float32, device=G.DEV)
+    load = torch.zeros((L, E), dtype=torch.int32, device=G.DEV)
+    buf = qb.EqbBuffers(L, E, device=G.DEV)
+    G.say("multi-layer L=3")
+    qb.eqb_update(s, b, K, alpha, buf, load=load)
+    torch.cuda.synchronize()
+    assert int(buf.err.item()) == 0
+    for l in range(L):
+        ref = O.eqb_layer(cases[l][0], cases[l][1], K)
+        got = dict(alpha=G.host(alpha[l]), load=G.host(load[l]), hist_hi=G.host(buf.hist_hi[l]),
+                   sel_hi=G.host(buf.sel_hi[l]), rank_lo=G.host(buf.rank_lo[l]),
+                   hist_lo=G.host(buf.hist_lo[l]), key=G.host(buf.key[l]), q=G.host(buf.q[l]),
+                   b_next=G.host(b[l]), bounds=G.host(buf.bounds[l]), err=0)
+        G.compare_eqb(got, ref, tag=f"layer {l} ")
+
+
+def test_standalone_hist_hi_and_keys(O):
+    N, E, K = 3001, 128, 6
+    s_np, b_np, _ = synth.random_case(40, N, E, K, quant=16.0)
+    ref = O.eqb_layer(s_np, b_np, K)
+    s, alpha = G.dev(s_np), G.dev(ref["alpha"])
+    hh = torch.zeros((E, 256), dtype=torch.int32, device=G.DEV)
+    keys = torch.empty((N, E), dtype=torch.uint16, device=G.DEV)
+    G.say("standalone hist_hi + keys")
+    qb.qb_radix_hist_hi(s, alpha, hh)
+    qb.qb_margin_keys(s, alpha, keys)
+    torch.cuda.synchronize()
+    G.assert_same("hist_hi", G.host(hh), ref["hist_hi"])
+    G.assert_same("keys", G.host(keys), O.margin_keys(s_np, ref["alpha"]).T)
+
+
+@pytest.mark.parametrize("N,E,K,n_bins,quant", [
+    (4000, 16, 2, 1000, None), (3000, 64, 6, 50, 64.0), (5000, 256, 6, 1000, None),
+    (1, 32, 3, 1000, None), (2049, 128, 7, 2048, None), (777, 256, 1, 7, 8.0)])
+def test_k3_sweep(O, N, E, K, n_bins, quant):
+    s, b, _ = synth.random_case(50, N, E, K, quant=quant)
+    bounds = O.bounds_of(b)
+    ref = O.k3_layer(s, b, K, bounds, n_bins)
+    G.say(f"k3 N={N} E={E} K={K} bins={n_bins}")
+    got = G.run_k3(s, b, K, bounds, n_bins)
+    assert got["err"] == 0
+    for k in ("alpha", "hist_u", "q", "b_next", "bounds"):
+        G.assert_same(k, got[k], ref[k])
+
+
+def test_bias_bounds(O):
+    b_np = np.random.default_rng(3).uniform(-0.3, 0.3, (5, 64)).astype(np.float32)
+    bounds = torch.zeros((5, 2), dtype=torch.float32, device=G.DEV)
+    G.say("bias bounds")
+    qb.qb_bias_bounds(G.dev(b_np), bounds)
+    torch.cuda.synchronize()
+    G.assert_same("bounds", G.host(bounds), np.stack([O.bounds_of(r) for r in b_np]))
+
+
+def test_lei_gradient(O):
+    N, E, K = 4096, 256, 6
+    s_np, b_np, _ = synth.random_case(60, N, E, K)
+    a_ref, load_ref = O.alpha(s_np, b_np, K)
+    s, b = G.dev(s_np), G.dev(b_np)
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    load = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+    g_np = np.random.default_rng(61).standard_normal((N, E), dtype=np.float32)
+    g = G.dev(g_np)
+    G.say("lei")
+    qb.qb_margins_topk(s, b, K, alpha, load=load)
+    qb.qb_lei_grad(g, load, K, 1e-5)
+    torch.cuda.synchronize()
+    G.assert_same("alpha", G.host(alpha), a_ref)
+    G.assert_same("load", G.host(load), load_ref)
+    G.assert_same("g", G.host(g), O.lei(g_np, load_ref, K, np.float32(1e-5)))
+
+
+def test_partition_invariance_chunked_accumulation(O):
+    """Microbatches accumulated into one histogram give the one-shot result
+    bit for bit (integer sums; the EQB paragraph's partition invariance)."""
+    N, E, K = 5000, 256, 6
+    s_np, b_np, _ = synth.random_case(70, N, E, K, quant=64.0)
+    ref = O.eqb_layer(s_np, b_np, K)
+    s, b = G.dev(s_np), G.dev(b_np)
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    buf = qb.EqbBuffers(1, E, device=G.DEV, lead=False)
+    cuts = [0, 1, 1777, 1778, 4096, N]
+    G.say("partition")
+    for a, c in zip(cuts[:-1], cuts[1:]):
+        qb.qb_margins_topk(s[a:c], b, K, alpha[a:c], hist_hi=buf.hist_hi)
+    qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                        err=buf.err)
+    for a, c in zip(cuts[:-1][::-1], cuts[1:][::-1]):  # reverse order
+        qb.qb_radix_hist_lo(s[a:c], alpha[a:c], buf.sel_hi, buf.hist_lo)
+    qb.qb_select_update(qb.QB_SELECT_LO, K, buf.hist_lo, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                        key_out=buf.key, q_out=buf.q, b=b, bounds=buf.bounds, err=buf.err)
+    torch.cuda.synchronize()
+    got = dict(alpha=G.host(alpha), hist_hi=G.host(buf.hist_hi), sel_hi=G.host(buf.sel_hi),
+               rank_lo=G.host(buf.rank_lo), hist_lo=G.host(buf.hist_lo), key=G.host(buf.key),
+               q=G.host(buf.q), b_next=G.host(b), bounds=G.host(buf.bounds), err=int(buf.err.item()))
+    G.compare_eqb(got, ref, with_load=False, tag="chunked ")
+
+
+def test_reset_in_place_and_replay():
+    N, E, K = 3000, 64, 4
+    s_np, b_np, _ = synth.random_case(80, N, E, K)
+    s, b = G.dev(s_np), G.dev(b_np)
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    hh = torch.zeros((E, 256), dtype=torch.int32, device=G.DEV)
+    addr = hh.data_ptr()
+    G.say("reset/replay")
+    qb.qb_margins_topk(s, b, K, alpha, hist_hi=hh)
+    once = G.host(hh).copy()
+    qb.qb_margins_topk(s, b, K, alpha, hist_hi=hh)  # replay without reset
+    twice = G.host(hh).copy()
+    assert (twice.sum(axis=1) == 2 * N).all()  # caught by the row-total check
+    qb.qb_fill_i32(hh, 0)
+    qb.qb_margins_topk(s, b, K, alpha, hist_hi=hh)
+    torch.cuda.synchronize()
+    assert hh.data_ptr() == addr
+    np.testing.assert_array_equal(G.host(hh), once)
+    np.testing.assert_array_equal(twice, 2 * once)
+    assert (once.sum(axis=1) == N).all()
+
+
+def test_select_error_flags_keep_bias():
+    E, K = 32, 2
+    hist = np.zeros((E, 256), np.int32)
+    hist[:, 100] = 50
+    hist[5, 100] = 49  # one expert row short: totals differ
+    b0 = np.linspace(-0.1, 0.1, E).astype(np.float32)
+    h = G.dev(hist)
+    sel = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+    rank = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+    G.say("select errors")
+    qb.qb_select_update(qb.QB_SELECT_HI, K, h, sel_hi=sel, rank_lo=rank, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & qb.QB_ERR_ROW_TOTALS
+    # an empty low-byte histogram cannot reach the rank: b and bounds untouched
+    b = G.dev(b0)
+    bounds = G.dev(np.array([7.0, 8.0], np.float32))
+    err.zero_()
+    lo = torch.zeros((E, 256), dtype=torch.int32, device=G.DEV)
+    qb.qb_select_update(qb.QB_SELECT_LO, K, lo, sel_hi=sel, rank_lo=rank, b=b, bounds=bounds, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & qb.QB_ERR_RANK
+    np.testing.assert_array_equal(G.host(b), b0)
+    np.testing.assert_array_equal(G.host(bounds), [7.0, 8.0])
+    # empty high-byte histogram
+    err.zero_()
+    qb.qb_select_update(qb.QB_SELECT_HI, K, lo, sel_hi=sel, rank_lo=rank, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & qb.QB_ERR_EMPTY
+
+
+def test_run_to_run_determinism():
+    N, E, K = 65536, 256, 6
+    s_np, b_np, _ = synth.single(N=N)
+    G.say("determinism")
+    r1 = G.run_eqb(s_np, b_np, K)
+    r2 = G.run_eqb(s_np, b_np, K)
+    for k in G.EQB_KEYS + ("load",):
+        G.assert_same(k, r1[k], r2[k])
+
+
+def test_graph_capture_replays(O):
+    """The whole update (resets included, no memset nodes) captured once and
+    replayed several times with eager work in between."""
+    N, E, K = 20000, 256, 6
+    s_np, b_np, _ = synth.random_case(90, N, E, K, quant=64.0)
+    ref = O.eqb_layer(s_np, b_np, K)
+    s, b0 = G.dev(s_np), G.dev(b_np)
+    b = b0.clone()
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    buf = qb.EqbBuffers(1, E, device=G.DEV, lead=False)
+    G.say("graph capture")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        buf.reset()
+        qb.eqb_update(s, b, K, alpha, buf)  # warm-up outside capture
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        buf.reset()
+        qb.eqb_update(s, b, K, alpha, buf)
+    for rep in range(4):
+        b.copy_(b0)
+        junk = torch.randn(1 << 20, device=G.DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        got = dict(alpha=G.host(alpha), hist_hi=G.host(buf.hist_hi), sel_hi=G.host(buf.sel_hi),
+                   rank_lo=G.host(buf.rank_lo), hist_lo=G.host(buf.hist_lo), key=G.host(buf.key),
+                   q=G.host(buf.q), b_next=G.host(b), bounds=G.host(buf.bounds),
+                   err=int(buf.err.item()))
+        G.compare_eqb(got, ref, with_load=False, tag=f"replay {rep} ")
