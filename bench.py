@@ -1,0 +1,334 @@
+"""Benchmark of the exact quantile-balancing (EQB) bias update on one MI355X.
+
+A step is one full EQB layer update of the skewed 1,048,576-token workload
+(E=256, K=6): the in-place histogram reset, pass 1 (alpha + high-byte
+histogram), the high-byte select, pass 2 (low-byte histogram) and the
+low-byte select with the in-place bias update; the bias is restored first
+so every step does identical work.  Inputs are resident in HBM before timing starts.  The step
+is replayed from a HIP graph captured once.
+
+Printed: one JSON line with the metric (tokens/s per layer), the roofline
+of the dominant kernel (algorithmic bytes / average duration from HIP events
+around each launch on its stream) and the CPU oracle timed on a bounded
+sample of the same workload.  --suite adds the 65,536-token layer (EQB and
+K3) and the 48-layer step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+class EqbStep:
+    """Device state of one EQB layer update and its launch sequence."""
+
+    def __init__(self, s, b0, K, qb, torch, L=None):
+        self.qb, self.torch = qb, torch
+        self.s, self.b0, self.K = s, b0, K
+        lead = s.dim() == 3
+        N, E = s.shape[-2], s.shape[-1]
+        Lx = s.shape[0] if lead else 1
+        self.b = b0.clone()
+        self.alpha = torch.empty(((Lx,) if lead else ()) + (N,), dtype=torch.float32, device=s.device)
+        self.buf = qb.EqbBuffers(Lx, E, device=s.device, lead=lead)
+
+    def launches(self):
+        """(name, callable) of the step, in stream order."""
+        qb, buf = self.qb, self.buf
+        return [
+            ("restore_bias", lambda: self.b.copy_(self.b0)),
+            ("reset_hist", lambda: buf.reset()),
+            ("pass1_topk_hist_hi", lambda: qb.qb_margins_topk(self.s, self.b, self.K, self.alpha,
+                                                              hist_hi=buf.hist_hi)),
+            ("select_hi", lambda: qb.qb_select_update(qb.QB_SELECT_HI, self.K, buf.hist_hi,
+                                                      sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                                                      err=buf.err)),
+            ("pass2_hist_lo", lambda: qb.qb_radix_hist_lo(self.s, self.alpha, buf.sel_hi, buf.hist_lo)),
+            ("select_lo", lambda: qb.qb_select_update(qb.QB_SELECT_LO, self.K, buf.hist_lo,
+                                                      sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                                                      key_out=buf.key, q_out=buf.q, b=self.b,
+                                                      bounds=buf.bounds, err=buf.err)),
+        ]
+
+    def run(self):
+        for _, f in self.launches():
+            f()
+
+
+def time_graph(step, torch, steps, warmup):
+    """Capture the step in a HIP graph; time `steps` replays."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            step.run()
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step.run()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, g
+
+
+def time_kernels(step, torch, reps):
+    """Average duration of each launch of the step: HIP events on the stream
+    the kernels run on, around `reps` back-to-back launches of that one call
+    (so launch gaps do not count, as in a kernel trace)."""
+    stream = torch.cuda.current_stream()
+    out = {}
+    for n, f in step.launches():
+        f()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[n] = e0.elapsed_time(e1) * 1e-3 / reps
+    return out
+
+
+def ceilings(torch, s, reps=10):
+    """Plain streaming kernels over the same score tensor, for context: a
+    read-only reduction and an elementwise copy (read + write)."""
+    out = {}
+    dst = torch.empty_like(s)
+    nbytes = s.numel() * 4
+    for name, f, moved in (("read_sum", lambda: s.sum(), nbytes),
+                           ("copy_add0", lambda: torch.add(s, 0.0, out=dst), 2 * nbytes)):
+        f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        out[name] = dict(us=round(sec * 1e6, 2), GBps=round(moved / sec / 1e9, 1), bytes=moved)
+    del dst
+    return out
+
+
+def cpu_baseline(s_np, b_np, K, rows):
+    from oracle import oracle
+
+    if not os.path.exists(oracle.LIB):
+        oracle.build()
+    sample = np.ascontiguousarray(s_np[:rows])
+    t0 = time.perf_counter()
+    oracle.eqb_layer(sample, b_np, K)
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {rows} of {s_np.shape[0]} tokens of the skewed workload; full "
+                       f"oracle EQB layer update (alpha, bf16 keys, per-expert sort-and-pick, "
+                       f"histograms, b_next), single thread, {dt:.1f} s on {cpu_model()} "
+                       f"(nproc={os.cpu_count()})")
+
+
+KERNEL_SOURCES = ("qb_device.hpp", "qb_pass1.hip", "qb_radix.hip")
+
+
+def kernel_source_hash():
+    """Hash of the sources of the two streaming passes."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_quantile_selection_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a
+    plain copy of known size), or None when that summary is missing or was
+    taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_skew_N1048576_E256.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    v = kv.get(f"{kernel}.hbm_bytes")
+    return float(v) if v else None
+
+
+def bytes_per_token(E):
+    """Algorithmic HBM bytes per token of one EQB layer: two reads of the
+    E fp32 scores (one per pass), alpha written once and read once."""
+    return dict(pass1=4 * E + 4, pass2=4 * E + 4, step=8 * E + 8)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--suite", action="store_true", help="also time the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=262144)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the update shards over "
+              "tokens with one histogram all-reduce per pass, which this build does not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_quantile_selection_amd import qb, synth
+
+    qb.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    p = synth.WORKLOADS["skew"]
+    N, E, K = p["N"], p["E"], p["K"]
+    log(f"generating skew workload N={N} E={E} K={K}")
+    s_np, b_np, _ = synth.skew()
+    s = torch.from_numpy(s_np).to(dev)
+    b0 = torch.from_numpy(b_np).to(dev)
+    step = EqbStep(s, b0, K, qb, torch)
+
+    log("timing")
+    torch.cuda.synchronize()
+    sec, _graph = time_graph(step, torch, args.steps, args.warmup)
+    assert int(step.buf.err.item()) == 0
+    per_k = time_kernels(step, torch, max(5, args.steps))
+    ceil = ceilings(torch, s)
+
+    bpt = bytes_per_token(E)
+    dominant = max(("pass1_topk_hist_hi", "pass2_hist_lo"), key=lambda n: per_k[n])
+    dom_bytes = N * bpt["pass1" if dominant.startswith("pass1") else "pass2"]
+    achieved = dom_bytes / per_k[dominant] / 1e9
+    kernels = {n: dict(us=round(t * 1e6, 2)) for n, t in per_k.items()}
+    for n, key in (("pass1_topk_hist_hi", "pass1"), ("pass2_hist_lo", "pass2")):
+        kernels[n]["GBps"] = round(N * bpt[key] / per_k[n] / 1e9, 1)
+    step_gbs = N * bpt["step"] / sec / 1e9
+
+    out = {
+        "metric": "EQB tokens/s per layer at E=256,K=6; achieved HBM GB/s vs peak",
+        "value": N / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "skew: N=1048576 tokens (256 x 4096), E=256, K=6, one layer, EQB",
+                   "N": N, "E": E, "K": K, "L": 1, "launch": "hip_graph",
+                   "step_algorithmic_bytes": N * bpt["step"],
+                   "step_GBps": round(step_gbs, 1),
+                   "step_frac_of_peak": round(step_gbs / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(dominant),
+                     "algorithmic_bytes_per_launch": dom_bytes},
+        "kernels": kernels,
+        "stream_ceilings": ceil,
+    }
+
+    if args.suite:
+        out["suite"] = suite(torch, qb, synth, dev, args)
+
+    if not args.no_cpu:
+        log(f"cpu baseline on {args.cpu_rows} tokens")
+        out["cpu_baseline"] = cpu_baseline(s_np, b_np, K, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+def suite(torch, qb, synth, dev, args):
+    res = {}
+    # 65,536-token layer: EQB and K3 (scores fit in the 256 MB infinity cache)
+    s_np, b_np, K = synth.single()
+    N, E = s_np.shape
+    s = torch.from_numpy(s_np).to(dev)
+    b0 = torch.from_numpy(b_np).to(dev)
+    st = EqbStep(s, b0, K, qb, torch)
+    sec, _ = time_graph(st, torch, args.steps, args.warmup)
+    res["single_eqb"] = dict(N=N, us_per_step=round(sec * 1e6, 2), tokens_per_s=N / sec,
+                             effective_GBps=round(N * (8 * E + 8) / sec / 1e9, 1))
+    bounds0 = torch.zeros(2, dtype=torch.float32, device=dev)
+    qb.qb_bias_bounds(b0, bounds0)
+    b = b0.clone()
+    bounds = bounds0.clone()
+    alpha = torch.empty(N, dtype=torch.float32, device=dev)
+    hist_u = torch.zeros((E, 1000), dtype=torch.int32, device=dev)
+    q_u = torch.zeros(E, dtype=torch.float32, device=dev)
+
+    class K3Step:
+        def run(self_):
+            b.copy_(b0)
+            bounds.copy_(bounds0)
+            qb.qb_fill_i32(hist_u, 0)
+            qb.k3_update(s, b, K, alpha, bounds, hist_u, q_u)
+
+    sec, _ = time_graph(K3Step(), torch, args.steps, args.warmup)
+    res["single_k3"] = dict(N=N, n_bins=1000, us_per_step=round(sec * 1e6, 2), tokens_per_s=N / sec,
+                            effective_GBps=round(N * (8 * E + 8) / sec / 1e9, 1))
+    del s, st
+    # 48-layer step on device-generated scores of the same recipe
+    p = synth.WORKLOADS["step"]
+    L, N, E, K = p["L"], p["N"], p["E"], p["K"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    mu = torch.rand((L, 1, 1), generator=g, device=dev) * 2 - 1
+    s = torch.empty((L, N, E), dtype=torch.float32, device=dev)
+    for l in range(L):
+        s[l].normal_(generator=g)
+        s[l].add_(mu[l]).sigmoid_()
+    b0 = (torch.rand((L, E), generator=g, device=dev) * 0.2 - 0.1).contiguous()
+    st = EqbStep(s, b0, K, qb, torch)
+    sec, _ = time_graph(st, torch, max(3, args.steps // 4), 1)
+    res["step_48_layers"] = dict(L=L, N=N, ms_per_step=round(sec * 1e3, 3),
+                                 tokens_per_s_per_layer=L * N / sec,
+                                 GBps=round(L * N * (8 * E + 8) / sec / 1e9, 1))
+    del s, st
+    torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    main()

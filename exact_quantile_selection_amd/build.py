@@ -38,10 +38,10 @@ def _units():
     return units
 
 
-def _compile(unit, verbose):
+def _compile(unit, verbose, build_dir, defines):
     obj, src, extra = unit
-    out = os.path.join(BUILD, obj)
-    cmd = [HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", out]
+    out = os.path.join(build_dir, obj)
+    cmd = [HIPCC, *CFLAGS, *extra, *defines, "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     p = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,18 +55,23 @@ def _compile(unit, verbose):
     return out
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str | None = None) -> str:
+    """Compile and link libqb.so.  `defines` (e.g. ["-DQB_RH_UNROLL=16"])
+    override the kernels' tuning constants; `out` puts the library (and its
+    objects) elsewhere, for comparing such variants."""
+    lib = out or LIB
+    build_dir = os.path.join(os.path.dirname(lib), "_build") if out else BUILD
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda u: _compile(u, verbose), _units()))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda u: _compile(u, verbose, build_dir, list(defines)), _units()))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -47,27 +47,25 @@ int device_cu_count() {
   return n;
 }
 
-static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-RowSplit split_rows(int L, int64_t N, int step, int cap) {
-  const int64_t per_layer = std::max<int64_t>(1, (device_cu_count() + L - 1) / L);
-  int64_t rows = round_up((N + per_layer - 1) / per_layer, step);
-  const int64_t cap_r = std::max<int64_t>(step, int64_t(cap) / step * step);
-  const int64_t cap16 = std::max<int64_t>(step, 65535 / step * step);  // 16-bit LDS counters
-  rows = std::min(rows, std::min(cap_r, cap16));
-  RowSplit r;
-  r.rows_per_wg = int(rows);
-  r.wg_per_layer = int((N + rows - 1) / rows);
-  r.blocks = int64_t(L) * r.wg_per_layer;
-  return r;
+static int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    const int64_t r = a % b;
+    a = b;
+    b = r;
+  }
+  return a;
 }
 
-RowSplit split_rows_chunks(int64_t N, int64_t chunks, int step) {
-  const int64_t rows = std::max<int64_t>(step, round_up((N + chunks - 1) / chunks, step));
+RowSplit split_rows(int L, int64_t N, int step, int64_t max_rows) {
+  const int64_t cus = device_cu_count();
   RowSplit r;
-  r.rows_per_wg = int(std::min<int64_t>(rows, int64_t(1) << 30));
-  r.wg_per_layer = int((N + r.rows_per_wg - 1) / r.rows_per_wg);
-  r.blocks = r.wg_per_layer;
+  r.trips = (N + step - 1) / step;
+  int64_t G = cus / gcd64(int64_t(L), cus);  // L * G = lcm(L, CUs)
+  const int64_t max_trips = std::max<int64_t>(1, max_rows / step);
+  G = std::max(G, (r.trips + max_trips - 1) / max_trips);
+  G = std::min(G, r.trips);
+  r.wg_per_layer = int(std::max<int64_t>(1, G));
+  r.blocks = int64_t(L) * r.wg_per_layer;
   return r;
 }
 
@@ -100,6 +98,7 @@ int hip_status(int rc, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 // Common shape checks of the passes over s [L][N][E].
 int check_pass(const char* fn, const float* s, int L, int64_t N, int E) {
@@ -125,8 +124,9 @@ QB_API int qb_margins_topk(const float* s, const float* b, int L, int64_t N, int
   if (!alpha) return fail(QB_EINVAL, "%s: alpha is NULL (expected float [L=%d][N=%lld])", fn, L, (long long)N);
   if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
   if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
-  if (!aligned4(b) || !aligned4(alpha) || (load && !aligned4(load)) || (hist_hi && !aligned4(hist_hi)))
-    return fail(QB_EINVAL, "%s: b, alpha, load and hist_hi must be 4-byte aligned", fn);
+  if (!aligned4(b) || !aligned4(alpha) || (load && !aligned4(load)))
+    return fail(QB_EINVAL, "%s: b, alpha and load must be 4-byte aligned", fn);
+  if (hist_hi && !aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
   return hip_status(qbk::launch_margins_topk(s, b, L, N, E, K, alpha, load, hist_hi, stream), fn);
 }
 
@@ -137,6 +137,7 @@ QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N
   if (!alpha || !hist_hi)
     return fail(QB_EINVAL, "%s: alpha (float [L][N]) and hist_hi (int32 [L=%d][E=%d][256]) are required",
                 fn, L, E);
+  if (!aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
   return hip_status(qbk::launch_radix_hist(false, s, alpha, L, N, E, nullptr, hist_hi, stream), fn);
 }
 
@@ -148,6 +149,7 @@ QB_API int qb_radix_hist_lo(const float* s, const float* alpha, int L, int64_t N
     return fail(QB_EINVAL,
                 "%s: alpha (float [L][N]), sel_hi (int32 [L=%d][E=%d]) and hist_lo (int32 [L][E][256]) are required",
                 fn, L, E);
+  if (!aligned8(hist_lo)) return fail(QB_EINVAL, "%s: hist_lo must be 8-byte aligned", fn);
   return hip_status(qbk::launch_radix_hist(true, s, alpha, L, N, E, sel_hi, hist_lo, stream), fn);
 }
 
@@ -179,16 +181,17 @@ QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist,
       n_bins = 256;
       break;
     case QB_SELECT_LO:
-      if (!sel_hi || !rank_lo || !b || !bounds)
+      if (!sel_hi || !rank_lo || !q_out || !b || !bounds)
         return fail(QB_EINVAL,
-                    "%s(LO): sel_hi, rank_lo (int32 [L=%d][E=%d]), b (float [L][E]) and bounds (float [L][2]) are required",
+                    "%s(LO): sel_hi, rank_lo (int32 [L=%d][E=%d]), q_out, b (float [L][E]) and bounds (float [L][2]) are required",
                     fn, L, E);
       n_bins = 256;
       break;
     case QB_SELECT_UNIFORM:
-      if (!b || !bounds)
-        return fail(QB_EINVAL, "%s(UNIFORM): b (float [L=%d][E=%d]) and bounds (float [L][2]) are required",
-                    fn, L, E);
+      if (!q_out || !b || !bounds)
+        return fail(QB_EINVAL,
+                    "%s(UNIFORM): q_out, b (float [L=%d][E=%d]) and bounds (float [L][2]) are required", fn,
+                    L, E);
       if (n_bins < 1 || n_bins > 2048)
         return fail(QB_EINVAL, "%s(UNIFORM): n_bins=%d, expected 1 <= n_bins <= 2048", fn, n_bins);
       break;

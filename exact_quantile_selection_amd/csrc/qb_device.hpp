@@ -129,11 +129,22 @@ __device__ __forceinline__ void hist16_add_hi(uint32_t* lds, int quad, int c0, u
 }
 
 // Adds the packed LDS histogram into the global int32 histogram
-// out[E][256] (non-zero counters only, agent-scope atomics).
+// out[E][256] (non-zero counters only, agent-scope atomics).  The
+// workgroups of a pass finish together; each starts its walk at a different
+// block of nthreads dwords (`start`, e.g. its index) so that concurrent
+// flushes hit different global counters instead of queueing on the same
+// ones.
 template <int E>
-__device__ __forceinline__ void hist16_flush(const uint32_t* lds, int32_t* out, int tid, int nthreads) {
+__device__ __forceinline__ void hist16_flush(const uint32_t* lds, int32_t* out, int tid, int nthreads,
+                                             int start) {
   constexpr int HDW = (E / 2) * 256;
-  for (int d = tid; d < HDW; d += nthreads) {
+  const int nblk = (HDW + nthreads - 1) / nthreads;
+  const int b0 = start % nblk;
+  for (int k = 0; k < nblk; ++k) {
+    int blk = b0 + k;
+    blk = blk >= nblk ? blk - nblk : blk;
+    const int d = blk * nthreads + tid;
+    if (d >= HDW) continue;
     const uint32_t v = lds[d];
     if (v) {
       const int pair = d >> 8;

@@ -6,21 +6,19 @@
 
 namespace qbk {
 
-// Work split of a row-chunked pass: blocks = L * wg_per_layer, each block
-// owns rows [g * rows_per_wg, min(N, (g+1) * rows_per_wg)) of one layer.
+// Block-cyclic work split of a pass over rows.  A workgroup "trip" is
+// `step` consecutive rows; trip t of a layer goes to workgroup t % G, so the
+// workgroups in flight at any moment read neighbouring blocks (all HBM
+// channels busy) instead of each streaming its own distant chunk.  G is
+// chosen so that L * G is a multiple of the CU count where possible, and
+// large enough that no workgroup sees more than `max_rows` rows (the packed
+// 16-bit LDS counters hold < 65536 per flush).
 struct RowSplit {
-  int rows_per_wg;
-  int wg_per_layer;
-  int64_t blocks;
+  int64_t trips;     // trips per layer = ceil(N / step)
+  int wg_per_layer;  // G
+  int64_t blocks;    // L * G
 };
-
-// step = rows one workgroup consumes per loop trip (its rows_per_wg is a
-// multiple of it); cap bounds the packed 16-bit LDS counters (< 65536 tokens
-// per workgroup flush) and keeps layers load-balanced.
-RowSplit split_rows(int L, int64_t N, int step, int cap);
-// N rows of one layer in about `chunks` pieces (multiples of `step`);
-// blocks counts one layer.
-RowSplit split_rows_chunks(int64_t N, int64_t chunks, int step);
+RowSplit split_rows(int L, int64_t N, int step, int64_t max_rows);
 
 int device_cu_count();
 

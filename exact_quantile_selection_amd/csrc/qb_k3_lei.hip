@@ -29,8 +29,7 @@ constexpr int kUHStep = kUHWaves * kUHRPI * kUHUnroll;
 
 __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
     const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int E,
-    const float* __restrict__ bounds, int n_bins, int rows_per_wg, int wg_per_layer,
-    int32_t* __restrict__ hist_u) {
+    const float* __restrict__ bounds, int n_bins, int wg_per_layer, int32_t* __restrict__ hist_u) {
   extern __shared__ int32_t lds_u[];  // [kUHSlice][n_bins]
   const int n_slices = E / kUHSlice;
   const int per_layer = n_slices * wg_per_layer;
@@ -38,8 +37,6 @@ __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
   const int rem = blockIdx.x - layer * per_layer;
   const int slice = rem % n_slices;
   const int g = rem / n_slices;
-  const int64_t row0 = int64_t(g) * rows_per_wg;
-  const int64_t row_end = min(N, row0 + int64_t(rows_per_wg));
   s += int64_t(layer) * N * E + slice * kUHSlice;
   alpha += int64_t(layer) * N;
   const int tid = threadIdx.x;
@@ -56,20 +53,21 @@ __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
   const int q4 = lane & 3;
   const int rsub = lane >> 2;
   int32_t* cnt = lds_u + 4 * q4 * n_bins;
-  for (int64_t base = row0 + int64_t(wave) * kUHRPI * kUHUnroll; base < row_end;
-       base += int64_t(kUHStep)) {
+  // Block-cyclic trips of kUHStep rows: this workgroup takes g, g + G, ...
+  for (int64_t base = int64_t(g) * kUHStep + int64_t(wave) * kUHRPI * kUHUnroll; base < N;
+       base += int64_t(wg_per_layer) * kUHStep) {
     float4 x[kUHUnroll];
     float a[kUHUnroll];
 #pragma unroll
     for (int u = 0; u < kUHUnroll; ++u) {
       int64_t row = base + u * kUHRPI + rsub;
-      row = row < row_end ? row : row_end - 1;
+      row = row < N ? row : N - 1;
       x[u] = ld4(s + row * E + 4 * q4);
       a[u] = alpha[row];
     }
 #pragma unroll
     for (int u = 0; u < kUHUnroll; ++u) {
-      if (base + u * kUHRPI + rsub < row_end) {
+      if (base + u * kUHRPI + rsub < N) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float r = a[u] - comp(x[u], c);
@@ -88,13 +86,14 @@ __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
 
 int launch_uniform_hist(const float* s, const float* alpha, int L, int64_t N, int E,
                         const float* bounds, int n_bins, int32_t* hist_u, hipStream_t st) {
-  // Row chunks per layer so that all layers' slices make about two
-  // workgroups per CU.
+  // Row-trip workgroups per (layer, slice) so that all layers' slices make
+  // about two workgroups per CU.
   const int n_slices = E / kUHSlice;
-  const int64_t chunks = std::max<int64_t>(
+  const int64_t trips = (N + kUHStep - 1) / kUHStep;
+  const int64_t per = std::max<int64_t>(
       1, (2 * int64_t(device_cu_count()) + int64_t(L) * n_slices - 1) / (int64_t(L) * n_slices));
-  const RowSplit sp = split_rows_chunks(N, chunks, kUHStep);
-  const int64_t blocks = int64_t(L) * n_slices * sp.wg_per_layer;
+  const int G = int(std::min<int64_t>(per, trips));
+  const int64_t blocks = int64_t(L) * n_slices * G;
   const size_t lds = size_t(kUHSlice) * size_t(n_bins) * sizeof(int32_t);
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uniform_hist),
@@ -102,7 +101,7 @@ int launch_uniform_hist(const float* s, const float* alpha, int L, int64_t N, in
     if (e != hipSuccess) return int(e);
   }
   hipLaunchKernelGGL(k_uniform_hist, dim3(unsigned(blocks)), dim3(kUHThreads), lds, st, s, alpha, N,
-                     E, bounds, n_bins, sp.rows_per_wg, sp.wg_per_layer, hist_u);
+                     E, bounds, n_bins, G, hist_u);
   return int(hipGetLastError());
 }
 

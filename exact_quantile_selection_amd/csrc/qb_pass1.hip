@@ -21,11 +21,18 @@
 //   * histogram: keys of both halves of a packed bf16 pair are made in three
 //     integer ops; counters are 16-bit pairs in LDS (E*512 bytes), flushed to
 //     the global int32 histogram once per workgroup (<= 65535 rows each).
+//   * work split: a workgroup trip is 16 waves x (64/LPR) rows; trips are
+//     block-cyclic over the workgroups, so the workgroups in flight read
+//     neighbouring rows (all HBM channels busy).  A full trip addresses its
+//     rows from a wave-uniform base with 32-bit lane offsets; only the last,
+//     partial trip clamps rows.
 #include "qb_device.hpp"
 #include "qb_internal.hpp"
 
 namespace qbk {
 
+// 16 waves per workgroup (<= 128 VGPRs each); the load-counting variant
+// keeps more state per lane and runs 8 waves (<= 256 VGPRs each).
 // 16 waves per workgroup (<= 128 VGPRs each); the load-counting variant
 // keeps more state per lane and runs 8 waves (<= 256 VGPRs each).
 template <bool LOAD>
@@ -107,11 +114,86 @@ __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], c
   }
 }
 
+// Loads one trip's rows (this lane's V scores of row base + rho) into x.
+// Loads one trip's rows (this lane's V scores of row base + rho) into x.
+// `base` is wave-uniform: a full trip addresses its rows from a uniform base
+// pointer with 32-bit lane offsets; a partial last trip clamps the row.
+template <int E>
+__device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N, int rho, int ql,
+                                        float4 (&x)[P1Shape<E>::F4]) {
+  using S = P1Shape<E>;
+  // The per-slot bias values, addresses and swizzles are loop-invariant;
+  // kept invariant they would be hoisted out of the row loop and occupy ~100
+  // VGPRs.  An opaque copy of the rotation makes them cheap per-trip work.
+  int rot = rho;
+  asm volatile("" : "+v"(rot));
+  if (base + S::RPW <= N) {
+    const float* ws = s + base * E;
+    const uint32_t lane_off = uint32_t(rho * E + 4 * ql);
+#pragma unroll
+    for (int t = 0; t < S::F4; ++t)
+      x[t] = ld4(ws + (lane_off + uint32_t(4 * S::LPR * ((t + rot) & (S::F4 - 1)))));
+  } else {
+    const int64_t row = base + rho;
+    const float* src = s + (row < N ? row : N - 1) * E;
+#pragma unroll
+    for (int t = 0; t < S::F4; ++t) {
+      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+      x[t] = ld4(src + 4 * quad);
+    }
+  }
+}
+
+// alpha, loads and the high-byte histogram of one trip's rows.
+template <int E, int P, bool HIST, bool LOAD>
+__device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64_t base, int64_t N,
+                                        int rho, int ql, int lane, int K, const float* lds_b,
+                                        uint32_t* lds_hist, int32_t* lds_load, float* alpha) {
+  using S = P1Shape<E>;
+  const int64_t row = base + rho;
+  const bool valid = row < N;
+  int rot = rho;
+  asm volatile("" : "+v"(rot));
+  float top[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) top[k] = -__builtin_inff();
+#pragma unroll
+  for (int t = 0; t < S::F4; ++t) {
+    const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+    const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
+    top_insert<P>(top, x[t].x + bb.x);
+    top_insert<P>(top, x[t].y + bb.y);
+    top_insert<P>(top, x[t].z + bb.z);
+    top_insert<P>(top, x[t].w + bb.w);
+  }
+  float a;
+  if constexpr (S::LPR == 1) {
+    a = top[P - 1];
+  } else if constexpr (S::LPR == 2) {
+    a = top_merge_last<P, kQuadXor1>(top);
+  } else {
+    top_merge<P, kQuadXor1>(top);
+    a = top_merge_last<P, kQuadXor2>(top);
+  }
+  if (valid && ql == 0) alpha[row] = a;
+  if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, lane, a, K, valid, lds_load);
+  if constexpr (HIST) {
+    if (valid) {
+#pragma unroll
+      for (int t = 0; t < S::F4; ++t) {
+        const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+        const uint32_t swz = hist16_swizzle2(quad);
+        hist16_add_hi(lds_hist, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
+        hist16_add_hi(lds_hist, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
+      }
+    }
+  }
+}
+
 template <int E, int P, bool HIST, bool LOAD>
 __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
-    const float* __restrict__ s, const float* __restrict__ b, int64_t N, int rows_per_wg,
-    int wg_per_layer, int K, float* __restrict__ alpha, int32_t* __restrict__ load,
-    int32_t* __restrict__ hist_hi) {
+    const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int K,
+    float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi) {
   using S = P1Shape<E>;
   constexpr int kWaves = p1_waves<LOAD>();
   constexpr int kThreads = kWaves * kWave;
@@ -122,8 +204,6 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
   const int tid = threadIdx.x;
   const int layer = blockIdx.x / wg_per_layer;
   const int g = blockIdx.x - layer * wg_per_layer;
-  const int64_t row0 = int64_t(g) * rows_per_wg;
-  const int64_t row_end = min(N, row0 + int64_t(rows_per_wg));
   s += int64_t(layer) * N * E;
   b += int64_t(layer) * E;
   alpha += int64_t(layer) * N;
@@ -136,63 +216,21 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
   __syncthreads();
 
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int rho = lane / S::LPR;
   const int ql = lane % S::LPR;
+  // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
+  constexpr int64_t kTrip = int64_t(kWaves) * S::RPW;
+  const int64_t stride = int64_t(wg_per_layer) * kTrip;
+  int64_t base = int64_t(g) * kTrip + int64_t(wave) * S::RPW;
 
-  for (int64_t base = row0 + int64_t(wave) * S::RPW; base < row_end;
-       base += int64_t(kWaves) * S::RPW) {
-    const int64_t row = base + rho;
-    const bool valid = row < row_end;
-    const float* src = s + (valid ? row : row_end - 1) * E;
-    // The per-slot bias values, addresses and swizzles are loop-invariant;
-    // kept invariant they would be hoisted out of this loop and occupy ~100
-    // VGPRs.  An opaque copy of the rotation makes them cheap per-trip work.
-    int rot = rho;
-    asm volatile("" : "+v"(rot));
+  for (; base < N; base += stride) {
     float4 x[S::F4];
-#pragma unroll
-    for (int t = 0; t < S::F4; ++t) {
-      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
-      x[t] = ld4(src + 4 * quad);
-    }
-    float top[P];
-#pragma unroll
-    for (int k = 0; k < P; ++k) top[k] = -__builtin_inff();
-#pragma unroll
-    for (int t = 0; t < S::F4; ++t) {
-      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
-      const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
-      top_insert<P>(top, x[t].x + bb.x);
-      top_insert<P>(top, x[t].y + bb.y);
-      top_insert<P>(top, x[t].z + bb.z);
-      top_insert<P>(top, x[t].w + bb.w);
-    }
-    float a;
-    if constexpr (S::LPR == 1) {
-      a = top[P - 1];
-    } else if constexpr (S::LPR == 2) {
-      a = top_merge_last<P, kQuadXor1>(top);
-    } else {
-      top_merge<P, kQuadXor1>(top);
-      a = top_merge_last<P, kQuadXor2>(top);
-    }
-    if (valid && ql == 0) alpha[row] = a;
-    if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, lane, a, K, valid, lds_load);
-    if constexpr (HIST) {
-      if (valid) {
-#pragma unroll
-        for (int t = 0; t < S::F4; ++t) {
-          const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
-          const uint32_t swz = hist16_swizzle2(quad);
-          hist16_add_hi(lds_hist, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
-          hist16_add_hi(lds_hist, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
-        }
-      }
-    }
+    p1_load<E>(s, base, N, rho, ql, x);
+    p1_rows<E, P, HIST, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha);
   }
   __syncthreads();
-  if constexpr (HIST) hist16_flush<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads);
+  if constexpr (HIST) hist16_flush<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
   if constexpr (LOAD) {
     for (int j = tid; j < E; j += kThreads)
       if (lds_load[j]) atomicAdd(load + int64_t(layer) * E + j, lds_load[j]);
@@ -203,9 +241,9 @@ template <int E, int P, bool HIST, bool LOAD>
 static int launch_p1_v(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st) {
   constexpr int kThreads = p1_waves<LOAD>() * kWave;
-  const RowSplit sp = split_rows(L, N, p1_waves<LOAD>() * P1Shape<E>::RPW, 4096);
+  const RowSplit sp = split_rows(L, N, p1_waves<LOAD>() * P1Shape<E>::RPW, 65535);
   hipLaunchKernelGGL((k_margins_topk<E, P, HIST, LOAD>), dim3(unsigned(sp.blocks)), dim3(kThreads),
-                     0, st, s, b, N, sp.rows_per_wg, sp.wg_per_layer, K, alpha, load, hist_hi);
+                     0, st, s, b, N, sp.wg_per_layer, K, alpha, load, hist_hi);
   return int(hipGetLastError());
 }
 

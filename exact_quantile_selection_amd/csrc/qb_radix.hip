@@ -9,11 +9,13 @@
 //
 // Layout on gfx950: lane l of a wave owns float4 column block (quad)
 // l % (E/4) of its row, so one load instruction covers 64*16 contiguous bytes
-// (one row at E=256).  Each lane keeps kUnroll rows of loads in flight.
-// Counters are the packed 16-bit LDS histogram of qb_device.hpp (bank
-// swizzle by quad), flushed once per workgroup.  A lane's experts are fixed
-// for the whole kernel, so the low-byte pass keeps their selected high bytes
-// in registers and filters with one compare per element.
+// (one row at E=256) and a wave trip reads kRHUnroll consecutive rows.  Trips
+// are block-cyclic over the workgroups, so the workgroups in flight read
+// neighbouring rows.  Each lane keeps two register sets of rows in flight.
+// Counters are the packed 16-bit LDS histogram of qb_device.hpp (bank swizzle
+// by quad), flushed once per workgroup.  A lane's experts are fixed for the
+// whole kernel, so the low-byte pass keeps their selected high bytes in
+// registers and filters with one compare per element.
 #include <algorithm>
 
 #include "qb_device.hpp"
@@ -23,7 +25,7 @@ namespace qbk {
 
 constexpr int kRHWaves = 16;
 constexpr int kRHThreads = kRHWaves * kWave;
-constexpr int kRHUnroll = 8;
+constexpr int kRHUnroll = 8;  // rows per lane per register set
 
 template <int E>
 struct RHShape {
@@ -36,22 +38,20 @@ struct RHShape {
 
 template <int E, bool LO>
 __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
-    const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int rows_per_wg,
-    int wg_per_layer, const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist) {
+    const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int wg_per_layer,
+    const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist) {
   using S = RHShape<E>;
   __shared__ uint32_t lds_hist[(E / 2) * 256];
   const int tid = threadIdx.x;
   const int layer = blockIdx.x / wg_per_layer;
   const int g = blockIdx.x - layer * wg_per_layer;
-  const int64_t row0 = int64_t(g) * rows_per_wg;
-  const int64_t row_end = min(N, row0 + int64_t(rows_per_wg));
   s += int64_t(layer) * N * E;
   alpha += int64_t(layer) * N;
 
   hist16_zero<E>(lds_hist, tid, kRHThreads);
 
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int quad = lane % S::QPR;
   const int rsub = lane / S::QPR;
   const uint32_t swz = hist16_swizzle2(quad);               // high bytes of a key pair
@@ -69,50 +69,70 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
   }
   __syncthreads();
 
-  for (int64_t base = row0 + int64_t(wave) * S::RPW; base < row_end;
-       base += int64_t(kRHWaves) * S::RPW) {
-    float4 x[kRHUnroll];
-    float a[kRHUnroll];
+  auto load = [&](int64_t base, float4 (&x)[kRHUnroll], float (&a)[kRHUnroll]) {
 #pragma unroll
     for (int u = 0; u < kRHUnroll; ++u) {
       int64_t row = base + u * S::RPI + rsub;
-      row = row < row_end ? row : row_end - 1;
+      row = row < N ? row : N - 1;
       x[u] = ld4(s + row * E + 4 * quad);
       a[u] = alpha[row];
     }
-#pragma unroll
-    for (int u = 0; u < kRHUnroll; ++u) {
-      if (base + u * S::RPI + rsub < row_end) {
-        const uint32_t k01 = key2(bf16x2_rne(a[u] - x[u].x, a[u] - x[u].y));
-        const uint32_t k23 = key2(bf16x2_rne(a[u] - x[u].z, a[u] - x[u].w));
-        if constexpr (!LO) {
-          hist16_add_hi(lds_hist, quad, 0, k01 ^ swz);
-          hist16_add_hi(lds_hist, quad, 2, k23 ^ swz);
-        } else {
-          // low byte of the key, swizzled like the high-byte histogram
-          const uint32_t l01 = k01 ^ swzl, l23 = k23 ^ swzl;
-          if (((k01 >> 8) & 0xFFu) == sel[0]) atomicAdd(rowp + (l01 & 0xFFu), 1u);
-          if ((k01 >> 24) == sel[1]) atomicAdd(rowp + ((l01 >> 16) & 0xFFu), 0x10000u);
-          if (((k23 >> 8) & 0xFFu) == sel[2]) atomicAdd(rowp + 256 + (l23 & 0xFFu), 1u);
-          if ((k23 >> 24) == sel[3]) atomicAdd(rowp + 256 + ((l23 >> 16) & 0xFFu), 0x10000u);
-        }
-      }
+  };
+  auto count1 = [&](const float4& x, float a) {
+    const uint32_t k01 = key2(bf16x2_rne(a - x.x, a - x.y));
+    const uint32_t k23 = key2(bf16x2_rne(a - x.z, a - x.w));
+    if constexpr (!LO) {
+      hist16_add_hi(lds_hist, quad, 0, k01 ^ swz);
+      hist16_add_hi(lds_hist, quad, 2, k23 ^ swz);
+    } else {
+      // low byte of the key, swizzled like the high-byte histogram
+      const uint32_t l01 = k01 ^ swzl, l23 = k23 ^ swzl;
+      if (((k01 >> 8) & 0xFFu) == sel[0]) atomicAdd(rowp + (l01 & 0xFFu), 1u);
+      if ((k01 >> 24) == sel[1]) atomicAdd(rowp + ((l01 >> 16) & 0xFFu), 0x10000u);
+      if (((k23 >> 8) & 0xFFu) == sel[2]) atomicAdd(rowp + 256 + (l23 & 0xFFu), 1u);
+      if ((k23 >> 24) == sel[3]) atomicAdd(rowp + 256 + ((l23 >> 16) & 0xFFu), 0x10000u);
     }
+  };
+  auto count = [&](int64_t base, const float4 (&x)[kRHUnroll], const float (&a)[kRHUnroll]) {
+    if (base + S::RPW <= N) {
+#pragma unroll
+      for (int u = 0; u < kRHUnroll; ++u) count1(x[u], a[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kRHUnroll; ++u)
+        if (base + u * S::RPI + rsub < N) count1(x[u], a[u]);
+    }
+  };
+  // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
+  // Two register sets: the next trip's rows are in flight while this trip's
+  // keys are counted.
+  const int64_t stride = int64_t(wg_per_layer) * S::STEP;
+  int64_t base = int64_t(g) * S::STEP + int64_t(wave) * S::RPW;
+  float4 xa[kRHUnroll], xb[kRHUnroll];
+  float aa[kRHUnroll], ab[kRHUnroll];
+  if (base < N) load(base, xa, aa);
+  for (; base < N; base += 2 * stride) {
+    const int64_t nb = base + stride;
+    if (nb < N) load(nb, xb, ab);
+    count(base, xa, aa);
+    if (nb >= N) break;
+    if (nb + stride < N) load(nb + stride, xa, aa);
+    count(nb, xb, ab);
   }
   __syncthreads();
-  hist16_flush<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads);
+  hist16_flush<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads, g);
 }
 
 template <int E>
 static int launch_rh(bool lo, const float* s, const float* alpha, int L, int64_t N,
                      const int32_t* sel_hi, int32_t* hist, hipStream_t st) {
-  const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, 4096);
+  const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, 65535);
   if (lo)
     hipLaunchKernelGGL((k_radix_hist<E, true>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
-                       s, alpha, N, sp.rows_per_wg, sp.wg_per_layer, sel_hi, hist);
+                       s, alpha, N, sp.wg_per_layer, sel_hi, hist);
   else
     hipLaunchKernelGGL((k_radix_hist<E, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
-                       s, alpha, N, sp.rows_per_wg, sp.wg_per_layer, sel_hi, hist);
+                       s, alpha, N, sp.wg_per_layer, sel_hi, hist);
   return int(hipGetLastError());
 }
 

@@ -10,12 +10,13 @@
 // Mixture-of-Experts" (summary page), EQB paragraph (find the bin holding the
 // rank in the high-byte histogram, then the low byte inside it).
 //
-// Each wave scans one expert row at a time: lane l owns a contiguous block of
-// ceil(n_bins/64) bins, the lane totals are prefix-summed across the wave
-// (shuffles), a ballot finds the first lane whose running count reaches the
-// rank, and that lane walks its block.  Everything that fixes floating-point
-// rounding (the float64 mean, min/max) runs sequentially on one thread in
-// expert order, so the result does not depend on the launch shape.
+// The rank scans run one wave per expert row (E/16 workgroups per layer):
+// lane l owns a contiguous block of ceil(n_bins/64) bins, the lane totals
+// are prefix-summed across the wave (shuffles), a ballot finds the first
+// lane whose running count reaches the rank, and that lane walks its block.
+// A small per-layer kernel then forms the bias update; the float64 mean runs
+// sequentially on one thread in expert order, so the result does not
+// depend on the launch shape.
 #include <algorithm>
 
 #include "qb_device.hpp"
@@ -24,9 +25,9 @@
 
 namespace qbk {
 
-constexpr int kSelThreads = 256;
-constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kMaxE = 256;
+constexpr int kRowWaves = 16;                   // experts per workgroup (one per wave)
+constexpr int kRowThreads = kRowWaves * kWave;
+constexpr int kFinThreads = 256;                // >= E: one thread per expert
 
 // Inclusive prefix sum of v over the wave.
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
@@ -38,153 +39,200 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
   return v;
 }
 
-struct RankHit {
-  int bin;         // first bin whose running count reaches the rank, -1 if none
-  int64_t before;  // count of the bins below it
-  int count;       // count of that bin
-  int64_t total;   // row total
-};
-
-// Scan one histogram row for the first bin whose running count reaches
-// `rank` (1-based).  All lanes of the wave return the same result.
-__device__ RankHit scan_row(const int32_t* row, int n_bins, int64_t rank, int lane) {
-  const int per = (n_bins + kWave - 1) / kWave;
-  const int b0 = min(n_bins, lane * per);
-  const int b1 = min(n_bins, b0 + per);
-  int64_t mine = 0;
-  for (int h = b0; h < b1; ++h) mine += row[h];
-  const int64_t incl = wave_incl_scan(mine, lane);
-  const int64_t excl = incl - mine;
-  RankHit r;
-  r.total = __shfl(incl, kWave - 1);
-  const uint64_t hit = __ballot(incl >= rank && mine > 0);
-  r.bin = -1;
-  r.before = 0;
-  r.count = 0;
-  if (hit == 0) return r;
-  const int f = __ffsll((unsigned long long)hit) - 1;
-  int bin = -1;
-  int64_t before = 0;
-  int cnt = 0;
-  if (lane == f) {
-    int64_t run = excl;
-    for (int h = b0; h < b1; ++h) {
-      const int c = row[h];
-      if (run + c >= rank) {
-        bin = h;
-        before = run;
-        cnt = c;
-        break;
-      }
-      run += c;
-    }
-  }
-  r.bin = __shfl(bin, f);
-  r.before = __shfl(before, f);
-  r.count = __shfl(cnt, f);
-  return r;
+__device__ __forceinline__ int64_t wave_sum(int64_t v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d);
+  return v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select(
-    int phase, int E, int K, const int32_t* __restrict__ hist, int n_bins,
+// PER consecutive bins of a row owned by this lane (zero past n_bins); the
+// 64 lanes of the wave read the row contiguously.
+template <int PER>
+__device__ __forceinline__ void load_bins(const int32_t* row, int n_bins, bool vec, int lane,
+                                          int (&c)[PER]) {
+  const int b0 = lane * PER;
+  if (vec && b0 + PER <= n_bins) {
+#pragma unroll
+    for (int k = 0; k < PER; k += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(row + b0 + k);
+      c[k] = v.x;
+      c[k + 1] = v.y;
+      c[k + 2] = v.z;
+      c[k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) c[k] = (b0 + k < n_bins) ? row[b0 + k] : 0;
+  }
+}
+
+// Per-expert rank scans, one wave per expert row, E/16 workgroups per layer.
+//   HI: sel_hi / rank_lo from the high-byte histogram.
+//   LO: key (sel_hi << 8 | low byte) and its bf16 value into q_out.
+//   UNIFORM: in-bin linear interpolation into q_out.
+// A failed row writes sel_hi = -1 (HI) or q = NaN (LO, UNIFORM), which the
+// finalize kernel turns into "layer left unchanged".
+template <int PER>
+__global__ __launch_bounds__(kRowThreads) void k_select_rows(
+    int phase, int E, int K, const int32_t* __restrict__ hist, int n_bins, int vec,
     int32_t* __restrict__ sel_hi, int32_t* __restrict__ rank_lo, uint16_t* __restrict__ key_out,
-    float* __restrict__ q_out, float* __restrict__ b, float* __restrict__ bounds,
-    int32_t* __restrict__ err) {
-  __shared__ int64_t s_total;
-  __shared__ int s_err;
-  __shared__ float s_q[kMaxE];
-  __shared__ float s_bn[kMaxE];
+    float* __restrict__ q_out, const float* __restrict__ bounds, int32_t* __restrict__ err) {
+  const int layer = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = blockIdx.x * kRowWaves + int(threadIdx.x / kWave);
+  if (j >= E) return;  // whole wave; no workgroup barrier follows
+  const int64_t le = int64_t(layer) * E;
+  const int32_t* lh = hist + le * n_bins;
+
+  int64_t rank;
+  int hi_byte = 0;
+  int bits = 0;
+  if (phase == QB_SELECT_LO) {
+    hi_byte = sel_hi[le + j];
+    rank = rank_lo[le + j];
+  }
+  int c[PER];
+  load_bins<PER>(lh + int64_t(j) * n_bins, n_bins, vec != 0, lane, c);
+  int64_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) mine += c[k];
+  if (phase == QB_SELECT_LO) {
+    if (hi_byte < 0 || hi_byte > 255 || rank < 1) {
+      if (lane == 0) {
+        q_out[le + j] = __builtin_nanf("");
+        if (err) atomicOr(err, QB_ERR_RANK);
+      }
+      return;
+    }
+  } else {
+    // token total from expert 0's row (each token adds one margin per expert)
+    int c0[PER];
+    load_bins<PER>(lh, n_bins, vec != 0, lane, c0);
+    int64_t t0 = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) t0 += c0[k];
+    const int64_t total = wave_sum(t0);
+    if (total == 0) bits |= QB_ERR_EMPTY;
+    if (wave_sum(mine) != total) bits |= QB_ERR_ROW_TOTALS;
+    rank = (int64_t(K) * total + E - 1) / E;  // 1-based rank ceil(K*N/E)
+  }
+
+  const int64_t incl = wave_incl_scan(mine, lane);
+  const uint64_t hit = __ballot(incl >= rank && mine > 0);
+  int bin = -1, cnt = 0;
+  int64_t before = 0;
+  if (hit != 0) {
+    const int f = __ffsll((unsigned long long)hit) - 1;
+    if (lane == f) {
+      int64_t run = incl - mine;
+      bool found = false;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        if (!found && run + c[k] >= rank) {
+          found = true;
+          bin = lane * PER + k;
+          before = run;
+          cnt = c[k];
+        }
+        if (!found) run += c[k];
+      }
+    }
+    bin = __shfl(bin, f);
+    before = __shfl(before, f);
+    cnt = __shfl(cnt, f);
+  }
+  if (lane != 0) return;
+  if (bin < 0) bits |= QB_ERR_RANK;
+  if (bits && err) atomicOr(err, bits);
+  if (phase == QB_SELECT_HI) {
+    sel_hi[le + j] = bin < 0 ? -1 : bin;
+    rank_lo[le + j] = bin < 0 ? 0 : int32_t(rank - before);
+  } else if (phase == QB_SELECT_LO) {
+    if (bin < 0) {
+      q_out[le + j] = __builtin_nanf("");
+      return;
+    }
+    const uint32_t key = (uint32_t(hi_byte) << 8) | uint32_t(bin);
+    q_out[le + j] = __builtin_bit_cast(float, unkey16(key) << 16);
+    if (key_out) key_out[le + j] = uint16_t(key);
+  } else {
+    if (bin < 0 || bits) {
+      q_out[le + j] = __builtin_nanf("");
+      return;
+    }
+    const double lo = double(bounds[2 * layer]);
+    const double w = (double(bounds[2 * layer + 1]) - lo) / double(n_bins);
+    const double frac = double(rank - before) / double(cnt);
+    q_out[le + j] = float(lo + w * (double(bin) + frac));
+  }
+}
+
+// b_next = q - mean(q) (float64 sum in expert order on one thread, one
+// rounding to fp32), written over b; bounds = [min - 1, max + 1] (min and
+// max as a parallel reduction: any order gives the same values up to the
+// sign of a zero, which the -1 / +1 removes).  A layer with a NaN quantile
+// (failed rank search) keeps its b and bounds.  One workgroup per layer.
+__global__ __launch_bounds__(kFinThreads) void k_finalize(int E, const float* __restrict__ q,
+                                                          float* __restrict__ b,
+                                                          float* __restrict__ bounds,
+                                                          int32_t* __restrict__ err) {
+  __shared__ __align__(16) float sq[kFinThreads];
   __shared__ double s_mean;
-  __shared__ float s_lohi[2];
+  __shared__ int s_bad;
+  __shared__ float s_min[kFinThreads / kWave], s_max[kFinThreads / kWave];
   const int layer = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int nb = phase == QB_SELECT_UNIFORM ? n_bins : 256;
-  hist += int64_t(layer) * E * nb;
   const int64_t le = int64_t(layer) * E;
-
-  if (wave == 0) {
-    int64_t t = 0;
-    for (int h = lane; h < nb; h += kWave) t += hist[h];
-    t = wave_incl_scan(t, lane);
-    if (lane == kWave - 1) s_total = t;
-  }
-  if (tid == 0) {
-    s_err = 0;
-    s_lohi[0] = 0.0f;
-    s_lohi[1] = 1.0f;
-    if (phase == QB_SELECT_UNIFORM) {
-      s_lohi[0] = bounds[2 * layer];
-      s_lohi[1] = bounds[2 * layer + 1];
-    }
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (tid < E) {
+    const float v = q[le + tid];
+    sq[tid] = v;
+    if (v != v) atomicOr(&s_bad, 1);
   }
   __syncthreads();
-  const int64_t total = s_total;
-  const int64_t m = (int64_t(K) * total + E - 1) / E;  // 1-based rank ceil(K*N/E)
-  if (tid == 0 && total == 0 && phase != QB_SELECT_LO) atomicOr(&s_err, QB_ERR_EMPTY);
-  const double lo = double(s_lohi[0]);
-  const double w = (double(s_lohi[1]) - lo) / double(n_bins);
-
-  for (int j = wave; j < E; j += kSelWaves) {
-    const int32_t* row = hist + int64_t(j) * nb;
-    int64_t rank = m;
-    int hi_byte = 0;
-    if (phase == QB_SELECT_LO) {
-      hi_byte = sel_hi[le + j];
-      rank = rank_lo[le + j];
-      if (hi_byte < 0 || hi_byte > 255 || rank < 1) {
-        if (lane == 0) atomicOr(&s_err, QB_ERR_RANK);
-        continue;
-      }
-    }
-    const RankHit h = scan_row(row, nb, rank, lane);
-    if (lane != 0) continue;
-    if (phase != QB_SELECT_LO && h.total != total) atomicOr(&s_err, QB_ERR_ROW_TOTALS);
-    if (h.bin < 0) {
-      atomicOr(&s_err, QB_ERR_RANK);
-      if (phase == QB_SELECT_HI) {
-        sel_hi[le + j] = -1;
-        rank_lo[le + j] = 0;
-      }
-      continue;
-    }
-    if (phase == QB_SELECT_HI) {
-      sel_hi[le + j] = h.bin;
-      rank_lo[le + j] = int32_t(rank - h.before);
-    } else if (phase == QB_SELECT_LO) {
-      const uint32_t key = (uint32_t(hi_byte) << 8) | uint32_t(h.bin);
-      s_q[j] = __builtin_bit_cast(float, unkey16(key) << 16);
-      if (key_out) key_out[le + j] = uint16_t(key);
-    } else {
-      const double frac = double(rank - h.before) / double(h.count);
-      s_q[j] = float(lo + w * (double(h.bin) + frac));
-    }
-  }
-  __syncthreads();
-  if (phase == QB_SELECT_HI || s_err != 0) {
-    if (tid == 0 && s_err && err) atomicOr(err, s_err);
+  if (s_bad) {
+    if (tid == 0 && err) atomicOr(err, QB_ERR_RANK);
     return;
   }
-  // b_next = q - mean(q): float64 sum in expert order, one rounding to fp32.
   if (tid == 0) {
+    // E is a multiple of 4; vector LDS reads keep the in-order float64 chain
+    // from waiting on one LDS round trip per term.
     double sum = 0.0;
-    for (int j = 0; j < E; ++j) sum += double(s_q[j]);
+    const float4* q4 = reinterpret_cast<const float4*>(sq);
+#pragma unroll 8
+    for (int k = 0; k < E / 4; ++k) {
+      const float4 v = q4[k];
+      sum += double(v.x);
+      sum += double(v.y);
+      sum += double(v.z);
+      sum += double(v.w);
+    }
     s_mean = sum / double(E);
   }
   __syncthreads();
-  for (int j = tid; j < E; j += kSelThreads) {
-    const float bn = float(double(s_q[j]) - s_mean);
-    s_bn[j] = bn;
-    b[le + j] = bn;
-    if (q_out) q_out[le + j] = s_q[j];
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  if (tid < E) {
+    const float bn = float(double(sq[tid]) - s_mean);
+    b[le + tid] = bn;
+    mn = bn;
+    mx = bn;
+  }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, d));
+    mx = fmaxf(mx, __shfl_xor(mx, d));
+  }
+  if (lane == 0) {
+    s_min[tid / kWave] = mn;
+    s_max[tid / kWave] = mx;
   }
   __syncthreads();
   if (tid == 0) {
-    float mn = s_bn[0], mx = s_bn[0];
-    for (int j = 1; j < E; ++j) {
-      if (s_bn[j] < mn) mn = s_bn[j];
-      if (s_bn[j] > mx) mx = s_bn[j];
+    for (int w = 1; w < kFinThreads / kWave; ++w) {
+      mn = fminf(mn, s_min[w]);
+      mx = fmaxf(mx, s_max[w]);
     }
     bounds[2 * layer] = mn - 1.0f;
     bounds[2 * layer + 1] = mx + 1.0f;
@@ -194,8 +242,21 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 int launch_select(int phase, int L, int E, int K, const int32_t* hist, int n_bins,
                   int32_t* sel_hi, int32_t* rank_lo, uint16_t* key_out, float* q_out, float* b,
                   float* bounds, int32_t* err, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(unsigned(L)), dim3(kSelThreads), 0, st, phase, E, K, hist,
-                     n_bins, sel_hi, rank_lo, key_out, q_out, b, bounds, err);
+  const int vec = ((n_bins % 4) == 0 && (reinterpret_cast<uintptr_t>(hist) & 15u) == 0) ? 1 : 0;
+  const dim3 grid{unsigned((E + kRowWaves - 1) / kRowWaves), unsigned(L), 1u};
+  const dim3 block{unsigned(kRowThreads), 1u, 1u};
+  if (n_bins <= 256)
+    hipLaunchKernelGGL(k_select_rows<4>, grid, block, 0, st, phase, E, K, hist, n_bins, vec, sel_hi,
+                       rank_lo, key_out, q_out, bounds, err);
+  else if (n_bins <= 1024)
+    hipLaunchKernelGGL(k_select_rows<16>, grid, block, 0, st, phase, E, K, hist, n_bins, vec, sel_hi,
+                       rank_lo, key_out, q_out, bounds, err);
+  else
+    hipLaunchKernelGGL(k_select_rows<32>, grid, block, 0, st, phase, E, K, hist, n_bins, vec, sel_hi,
+                       rank_lo, key_out, q_out, bounds, err);
+  int rc = int(hipGetLastError());
+  if (rc != int(hipSuccess) || phase == QB_SELECT_HI) return rc;
+  hipLaunchKernelGGL(k_finalize, dim3(unsigned(L)), dim3(kFinThreads), 0, st, E, q_out, b, bounds, err);
   return int(hipGetLastError());
 }
 

@@ -186,31 +186,36 @@ def qb_lei_grad(g, load, K, eta, stream=None):
 # Composition of the calls above for one global batch (no arithmetic here).
 
 class EqbBuffers:
-    """Device buffers of one EQB update over L layers of E experts."""
+    """Device buffers of one EQB update over L layers of E experts.
+
+    The two histograms and the error word share one int32 block so that the
+    in-place reset is a single fill launch."""
 
     def __init__(self, L: int, E: int, device="cuda", lead: bool = True):
         shp = (L,) if lead else ()
         kw = dict(device=device)
-        self.hist_hi = torch.zeros(shp + (E, 256), dtype=torch.int32, **kw)
-        self.hist_lo = torch.zeros(shp + (E, 256), dtype=torch.int32, **kw)
+        nh = L * E * 256
+        self.block = torch.zeros(2 * nh + 4, dtype=torch.int32, **kw)
+        self.hist_hi = self.block[:nh].view(shp + (E, 256))
+        self.hist_lo = self.block[nh:2 * nh].view(shp + (E, 256))
+        self.err = self.block[2 * nh:2 * nh + 1]
         self.sel_hi = torch.zeros(shp + (E,), dtype=torch.int32, **kw)
         self.rank_lo = torch.zeros(shp + (E,), dtype=torch.int32, **kw)
         self.key = torch.zeros(shp + (E,), dtype=torch.uint16, **kw)
         self.q = torch.zeros(shp + (E,), dtype=torch.float32, **kw)
         self.bounds = torch.zeros(shp + (2,), dtype=torch.float32, **kw)
-        self.err = torch.zeros((1,), dtype=torch.int32, **kw)
 
     def reset(self, stream=None):
-        """In-place reset of the accumulated histograms (addresses unchanged)."""
-        qb_fill_i32(self.hist_hi, 0, stream)
-        qb_fill_i32(self.hist_lo, 0, stream)
-        qb_fill_i32(self.err, 0, stream)
+        """In-place reset of both histograms and the error word (addresses
+        unchanged), one fill kernel."""
+        qb_fill_i32(self.block, 0, stream)
 
 
 def eqb_update(s, b, K, alpha, buf: EqbBuffers, load=None, stream=None):
     """One exact quantile-balancing update: pass 1 (alpha + high-byte
     histogram), high-byte select, pass 2 (low-byte histogram), low-byte select
-    and the in-place bias update.  Histograms must be zero on entry."""
+    and the in-place bias update.  Histograms must be zero on entry
+    (buf.reset() clears them in place)."""
     qb_margins_topk(s, b, K, alpha, load=load, hist_hi=buf.hist_hi, stream=stream)
     qb_select_update(QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
                      err=buf.err, stream=stream)
@@ -220,7 +225,7 @@ def eqb_update(s, b, K, alpha, buf: EqbBuffers, load=None, stream=None):
                      stream=stream)
 
 
-def k3_update(s, b, K, alpha, bounds, hist_u, q_out=None, err=None, stream=None):
+def k3_update(s, b, K, alpha, bounds, hist_u, q_out, err=None, stream=None):
     """One K3 update: alpha pass, uniform-bin pass over the current bounds,
     select + in-place bias/bounds update.  hist_u must be zero on entry."""
     qb_margins_topk(s, b, K, alpha, stream=stream)

@@ -34,7 +34,7 @@
  *       b       float  [L][E]
  *       alpha   float  [L][N]
  *       load    int32  [L][E]
- *       hist_hi int32  [L][E][256], hist_lo int32 [L][E][256]
+ *       hist_hi int32  [L][E][256], hist_lo int32 [L][E][256]  (8-byte aligned)
  *       hist_u  int32  [L][E][n_bins]
  *       sel_hi, rank_lo int32 [L][E];  key_out uint16 [L][E]; q_out float [L][E]
  *       bounds  float  [L][2]  ({lo, hi})
@@ -137,8 +137,11 @@ QB_API int qb_margin_keys(const float* s, const float* alpha, int L, int64_t N, 
  *                  (read, then overwritten with the next range); q = lo + w *
  *                  (c + (m - below) / count[c]) in float64 (w = (hi-lo)/n_bins,
  *                  c = first bin reaching m), then centring as above.
- *   key_out, q_out, err: nullable.  err receives QB_ERR_* bits (atomic OR);
- *   a layer with an error keeps its b and bounds unchanged.
+ *   q_out: required for LO and UNIFORM (receives q; NaN marks an expert
+ *   whose rank search failed).  key_out, err: nullable.  err receives
+ *   QB_ERR_* bits (atomic OR); a layer with a failed expert keeps its b and
+ *   bounds unchanged.  HI is one launch (one wave per expert row); LO and
+ *   UNIFORM add a per-layer launch for the mean and the bounds.
  */
 QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist, int n_bins,
                             int32_t* sel_hi, int32_t* rank_lo, uint16_t* key_out,

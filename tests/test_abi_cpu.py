@@ -75,9 +75,12 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
     rc = libqb.qb_select_update(qb.QB_SELECT_LO, 1, 256, 6, fake, 256, fake, fake, None, None, None,
                                 fake, None, None)
     assert rc == qb.QB_EINVAL and "[L=1][E=256]" in _last(libqb)
-    rc = libqb.qb_select_update(qb.QB_SELECT_UNIFORM, 1, 256, 6, fake, 4096, None, None, None, None,
+    rc = libqb.qb_select_update(qb.QB_SELECT_UNIFORM, 1, 256, 6, fake, 4096, None, None, None, fake,
                                 fake, fake, None, None)
     assert rc == qb.QB_EINVAL and "n_bins=4096" in _last(libqb)
+    rc = libqb.qb_select_update(qb.QB_SELECT_UNIFORM, 1, 256, 6, fake, 1000, None, None, None, None,
+                                fake, fake, None, None)
+    assert rc == qb.QB_EINVAL and "q_out" in _last(libqb)
     rc = libqb.qb_uniform_hist(fake, fake, 1, 10, 256, None, 1000, fake, None)
     assert rc == qb.QB_EINVAL
     rc = libqb.qb_lei_grad(fake, fake, 10, 100, 6, C.c_float(1e-5), None)

@@ -207,11 +207,14 @@ def test_select_error_flags_keep_bias():
     bounds = G.dev(np.array([7.0, 8.0], np.float32))
     err.zero_()
     lo = torch.zeros((E, 256), dtype=torch.int32, device=G.DEV)
-    qb.qb_select_update(qb.QB_SELECT_LO, K, lo, sel_hi=sel, rank_lo=rank, b=b, bounds=bounds, err=err)
+    q = torch.zeros(E, dtype=torch.float32, device=G.DEV)
+    qb.qb_select_update(qb.QB_SELECT_LO, K, lo, sel_hi=sel, rank_lo=rank, q_out=q, b=b, bounds=bounds,
+                        err=err)
     torch.cuda.synchronize()
     assert int(err.item()) & qb.QB_ERR_RANK
     np.testing.assert_array_equal(G.host(b), b0)
     np.testing.assert_array_equal(G.host(bounds), [7.0, 8.0])
+    assert np.isnan(G.host(q)).all()
     # empty high-byte histogram
     err.zero_()
     qb.qb_select_update(qb.QB_SELECT_HI, K, lo, sel_hi=sel, rank_lo=rank, err=err)
