@@ -327,7 +327,73 @@ def suite(torch, qb, synth, dev, args):
                                  GBps=round(L * N * (8 * E + 8) / sec / 1e9, 1))
     del s, st
     torch.cuda.empty_cache()
+    res["router"] = router_suite(torch, qb, synth, dev, args)
     return res
+
+
+def router_suite(torch, qb, synth, dev, args):
+    """Fused-router workload: hidden [262144 x 2048] bf16 x w [256 x 2048]
+    bf16 on MFMA + sigmoid + pass 1 (qb_router_fused), then the rest of the
+    EQB update on the produced scores and the LEI gradient offset."""
+    p = synth.WORKLOADS["router"]
+    N, H, E, K = p["N"], p["H"], p["E"], p["K"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    hidden = torch.randn((N, H), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn((E, H), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    grad = torch.randn((N, E), generator=g, device=dev)
+    b0 = torch.zeros(E, dtype=torch.float32, device=dev)
+    b = b0.clone()
+    s = torch.empty((N, E), dtype=torch.float32, device=dev)
+    alpha = torch.empty(N, dtype=torch.float32, device=dev)
+    load = torch.zeros(E, dtype=torch.int32, device=dev)
+    buf = qb.EqbBuffers(1, E, device=dev, lead=False)
+
+    def reps(f, n):
+        f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    n = max(3, args.steps // 2)
+    t_fused = reps(lambda: qb.qb_router_fused(hidden, w, b, K, s, alpha), n)
+    t_pass1 = reps(lambda: qb.qb_margins_topk(s, b, K, alpha), n)
+    t_gemm = t_fused - t_pass1
+
+    class Chain:
+        def run(self_):
+            b.copy_(b0)
+            buf.reset()
+            qb.qb_fill_i32(load, 0)
+            qb.qb_router_fused(hidden, w, b, K, s, alpha, load=load, hist_hi=buf.hist_hi)
+            qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi,
+                                rank_lo=buf.rank_lo, err=buf.err)
+            qb.qb_radix_hist_lo(s, alpha, buf.sel_hi, buf.hist_lo)
+            qb.qb_select_update(qb.QB_SELECT_LO, K, buf.hist_lo, sel_hi=buf.sel_hi,
+                                rank_lo=buf.rank_lo, key_out=buf.key, q_out=buf.q, b=b,
+                                bounds=buf.bounds, err=buf.err)
+            qb.qb_lei_grad(grad, load, K, 1e-5)
+
+    sec, _ = time_graph(Chain(), torch, n, 1)
+    flops = 2.0 * N * H * E
+    gemm_bytes = N * H * 2 + N * E * 4 + E * H * 2
+    out = dict(N=N, H=H, E=E, K=K,
+               gemm_sigmoid_us=round(t_gemm * 1e6, 2),
+               gemm_mfma_TFLOPs=round(flops / t_gemm / 1e12, 1),
+               gemm_mfma_frac_of_2500=round(flops / t_gemm / 2.5e15, 4),
+               gemm_hbm_GBps=round(gemm_bytes / t_gemm / 1e9, 1),
+               pass1_on_scores_us=round(t_pass1 * 1e6, 2),
+               chain_us=round(sec * 1e6, 2), chain_tokens_per_s=N / sec,
+               chain="router GEMM + sigmoid + pass 1, select HI, pass 2, select LO, LEI")
+    del hidden, w, grad, s
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

@@ -232,6 +232,32 @@ QB_API int qb_fill_i32(int32_t* dst, int64_t count, int32_t value, qb_stream_t s
   return hip_status(qbk::launch_fill_i32(dst, count, value, stream), fn);
 }
 
+QB_API int qb_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E,
+                           int K, const float* b, float* s_out, float* logits_out, float* alpha,
+                           int32_t* load, int32_t* hist_hi, qb_stream_t stream) {
+  const char* fn = "qb_router_fused";
+  if (!hidden || !w || !b || !s_out || !alpha)
+    return fail(QB_EINVAL,
+                "%s: hidden (bf16 [N][H]), w (bf16 [E][H]), b (float [E]), s_out (float [N][E]) and alpha "
+                "(float [N]) are required",
+                fn);
+  if (N < 1 || N > INT32_MAX)
+    return fail(QB_EINVAL, "%s: N=%lld, expected 1 <= N < 2^31", fn, (long long)N);
+  if (H < 64 || H % 64 != 0) return fail(QB_EINVAL, "%s: H=%d, expected a positive multiple of 64", fn, H);
+  if (E != 32 && E != 64 && E != 128 && E != 256)
+    return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {32, 64, 128, 256}", fn, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (!aligned16(hidden) || !aligned16(w) || !aligned16(s_out))
+    return fail(QB_EINVAL, "%s: hidden, w and s_out must be 16-byte aligned", fn);
+  if ((logits_out && !aligned4(logits_out)) || !aligned4(b) || !aligned4(alpha) || (load && !aligned4(load)))
+    return fail(QB_EINVAL, "%s: logits_out, b, alpha and load must be 4-byte aligned", fn);
+  if (hist_hi && !aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
+  int rc = qbk::launch_router_gemm(hidden, w, N, H, E, s_out, logits_out, stream);
+  if (rc != int(hipSuccess)) return hip_status(rc, fn);
+  return hip_status(qbk::launch_margins_topk(s_out, b, 1, N, E, K, alpha, load, hist_hi, stream), fn);
+}
+
 QB_API int qb_lei_grad(float* g, const int32_t* load, int64_t N, int E, int K, float eta,
                        qb_stream_t stream) {
   const char* fn = "qb_lei_grad";

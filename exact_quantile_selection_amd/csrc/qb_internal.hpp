@@ -36,6 +36,8 @@ int launch_uniform_hist(const float* s, const float* alpha, int L, int64_t N, in
                         const float* bounds, int n_bins, int32_t* hist_u, hipStream_t st);
 int launch_bias_bounds(const float* b, int L, int E, float* bounds, hipStream_t st);
 int launch_fill_i32(int32_t* dst, int64_t count, int32_t value, hipStream_t st);
+int launch_router_gemm(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E,
+                       float* s_out, float* logits_out, hipStream_t st);
 int launch_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta,
                hipStream_t st);
 

@@ -55,6 +55,7 @@ def lib() -> C.CDLL:
             "qb_bias_bounds": [vp, i32, i32, vp, vp],
             "qb_fill_i32": [vp, i64, C.c_int32, vp],
             "qb_lei_grad": [vp, vp, i64, i32, i32, f32, vp],
+            "qb_router_fused": [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -174,6 +175,21 @@ def qb_bias_bounds(b, bounds, stream=None):
 
 def qb_fill_i32(t, value=0, stream=None):
     _check(lib().qb_fill_i32(_ptr(t, torch.int32, "t"), t.numel(), int(value), _stream(stream)))
+
+
+def qb_router_fused(hidden, w, b, K, s_out, alpha, logits_out=None, load=None, hist_hi=None,
+                    stream=None):
+    """hidden: bf16 [N, H]; w: bf16 [E, H] (nn.Linear layout).  Writes s_out
+    = sigmoid(hidden @ w.T) and runs pass 1 on it."""
+    N, H = hidden.shape
+    E = w.shape[0]
+    _check(lib().qb_router_fused(
+        _ptr(hidden, torch.bfloat16, "hidden"), _ptr(w, torch.bfloat16, "w", (E, H)), N, H, E, K,
+        _ptr(b, torch.float32, "b", (E,)), _ptr(s_out, torch.float32, "s_out", (N, E)),
+        _ptr(logits_out, torch.float32, "logits_out", (N, E), opt=True),
+        _ptr(alpha, torch.float32, "alpha", (N,)),
+        _ptr(load, torch.int32, "load", (E,), opt=True),
+        _ptr(hist_hi, torch.int32, "hist_hi", (E, 256), opt=True), _stream(stream)))
 
 
 def qb_lei_grad(g, load, K, eta, stream=None):

@@ -18,8 +18,8 @@ Workloads (every generator is seeded; seed 0 unless stated):
 * ``step``   48 layers of N=262,144, E=256, K=6; layer l draws from
   ``default_rng([0, l])``: mu_l ~ U(-1,1), b_l ~ U(-0.1,0.1), logits ~ N(mu_l, 1).
 * ``router`` hidden bf16 [262144 x 2048] ~ N(0,1), router weight bf16
-  [2048 x 256] ~ N(0, std 0.02), b = 0, upstream score gradient g ~ N(0,1)
-  fp32, eta = 1e-5.
+  [2048 x 256] ~ N(0, std 0.02) (stored [256 x 2048]), b = 0, upstream score
+  gradient g ~ N(0,1) fp32, eta = 1e-5.
 
 The model these shapes come from (256 routed experts, top-6, 48 MoE layers) is
 the 7.5B testbed of "Exact Quantile Balancing and Load-Error Injection for
@@ -115,9 +115,11 @@ def step_layer(layer: int, N: int | None = None, out: np.ndarray | None = None):
 
 
 def router(seed: int = 0, N: int | None = None, H: int | None = None, E: int | None = None):
-    """Returns (hidden_bf16_bits uint16 [N,H], w_bf16_bits uint16 [H,E], b, g, K, eta).
+    """Returns (hidden_bf16_bits uint16 [N,H], w_bf16_bits uint16 [E,H], b, g, K, eta).
 
-    bf16 values are float32 draws rounded to nearest-even (torch's CPU cast)."""
+    The router weight is drawn as [H, E] and stored transposed, [E, H] (the
+    nn.Linear weight layout; logits = hidden @ w.T).  bf16 values are float32
+    draws rounded to nearest-even (torch's CPU cast)."""
     import torch
 
     p = WORKLOADS["router"]
@@ -131,7 +133,8 @@ def router(seed: int = 0, N: int | None = None, H: int | None = None, E: int | N
         r1 = min(N, r0 + _CHUNK_ROWS // 4)
         x = rng.standard_normal((r1 - r0, H), dtype=np.float32)
         hidden[r0:r1] = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    wb = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    wb = np.ascontiguousarray(
+        torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).T)
     g = np.empty((N, E), dtype=np.float32)
     for r0 in range(0, N, _CHUNK_ROWS):
         r1 = min(N, r0 + _CHUNK_ROWS)

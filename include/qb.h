@@ -171,6 +171,25 @@ QB_API int qb_bias_bounds(const float* b, int L, int E, float* bounds, qb_stream
 QB_API int qb_fill_i32(int32_t* dst, int64_t count, int32_t value, qb_stream_t stream);
 
 /*
+ * Router forward fused with pass 1, for one layer: logits = hidden . w^T on
+ * MFMA (bf16 inputs, fp32 accumulation), s = sigmoid(logits) with the device
+ * expf, written to s_out; then exactly qb_margins_topk on s_out (alpha,
+ * optional top-K loads, optional high-byte histogram).  The sigmoid scores
+ * are those of "[Dev] Add global-batch quantile balancing", section
+ * "Quantile estimator"; the router forward is the one its Validation section
+ * exercises.
+ *   hidden  uint16 bf16 bit patterns [N][H], 16-byte aligned, H % 64 == 0
+ *   w       uint16 bf16 bit patterns [E][H] (nn.Linear weight layout)
+ *   b       float [E]; s_out float [N][E] (16-byte aligned);
+ *   logits_out nullable float [N][E]; alpha float [N]; load nullable int32 [E];
+ *   hist_hi nullable int32 [E][256] (8-byte aligned).
+ *   E in {32, 64, 128, 256}; 1 <= K <= 7.
+ */
+QB_API int qb_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E,
+                           int K, const float* b, float* s_out, float* logits_out, float* alpha,
+                           int32_t* load, int32_t* hist_hi, qb_stream_t stream);
+
+/*
  * LEI ("Exact Quantile Balancing and Load-Error Injection for
  * Mixture-of-Experts", summary page, LEI paragraph): with M = N*K/E,
  * rho_e = fl32((load_e - M) / M) in float64, add_e = fl32(eta * rho_e),

@@ -168,10 +168,11 @@ def lei(g, load, K: int, eta) -> np.ndarray:
 
 
 def router_logits(hidden_bits, w_bits, rows) -> np.ndarray:
+    """logits of the selected rows, float64; w_bits is [E, H]."""
     hidden_bits = np.ascontiguousarray(hidden_bits, dtype=np.uint16)
     w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
-    H, E = w_bits.shape
+    E, H = w_bits.shape
     out = np.zeros((rows.size, E), np.float64)
     lib().oq_router_logits(hidden_bits, w_bits, H, E, rows, rows.size, out)
     return out

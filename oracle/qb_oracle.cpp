@@ -269,16 +269,17 @@ void oq_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta) {
     for (int e = 0; e < E; ++e) g[i * E + e] = g[i * E + e] + add[e];
 }
 
-// Router logits of selected rows, bf16 inputs, float64 accumulation:
-// out[r * E + e] = sum_h hidden[rows[r]][h] * w[h][e].
+// Router logits of selected rows, bf16 inputs, float64 accumulation; the
+// weight is stored [E][H] (nn.Linear layout):
+// out[r * E + e] = sum_h hidden[rows[r]][h] * w[e][h].
 void oq_router_logits(const uint16_t* hidden, const uint16_t* w, int H, int E,
                       const int64_t* rows, int n_rows, double* out) {
   for (int r = 0; r < n_rows; ++r) {
     const uint16_t* x = hidden + rows[r] * int64_t(H);
     for (int e = 0; e < E; ++e) {
+      const uint16_t* we = w + int64_t(e) * H;
       double acc = 0.0;
-      for (int h = 0; h < H; ++h)
-        acc += double(bf16_value(x[h])) * double(bf16_value(w[int64_t(h) * E + e]));
+      for (int h = 0; h < H; ++h) acc += double(bf16_value(x[h])) * double(bf16_value(we[h]));
       out[int64_t(r) * E + e] = acc;
     }
   }

@@ -1,0 +1,109 @@
+"""GPU checks of the fused router path (MFMA GEMM + sigmoid + pass 1), and of
+the whole EQB + LEI chain on the scores it produces.
+
+Logits: within |d| <= 1e-2 * |ref| + 1e-4 * rms(ref) of a float64 host GEMM
+of the same bf16 inputs (bf16 x bf16 products are exact in fp32; the only
+error is the fp32 accumulation order over H terms).  Scores: the device's
+sigmoid of its own logits is within 4 ulp of float32(1/(1+exp(-x))) taken
+in float64 on the host.  Everything downstream (alpha, loads, histograms,
+keys, b_next, bounds, LEI) is checked bit for bit against the oracle run on
+the GPU-produced scores."""
+import numpy as np
+import pytest
+import torch
+
+from exact_quantile_selection_amd import qb, synth
+
+import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qb.lib()
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(G.DEV).view(torch.bfloat16)
+
+
+def check_logits(O, hidden, w, got_rows, rows):
+    """got_rows[i] holds the GPU logits of token rows[i]."""
+    ref = O.router_logits(hidden, w, rows)
+    got = got_rows.astype(np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    bad = np.abs(got - ref) > 1e-2 * np.abs(ref) + 1e-4 * rms
+    assert not bad.any(), f"{bad.sum()} logits out of tolerance; worst {np.abs(got - ref).max()}"
+
+
+def check_scores(s, logits):
+    host = (1.0 / (1.0 + np.exp(-logits.astype(np.float64)))).astype(np.float32)
+    ulp = np.spacing(np.abs(host))
+    assert (np.abs(s.astype(np.float64) - host) <= 4 * ulp).all()
+
+
+def run_router(hidden_np, w_np, b_np, K, with_logits=True):
+    N, H = hidden_np.shape
+    E = w_np.shape[0]
+    hidden, w, b = bf16_dev(hidden_np), bf16_dev(w_np), G.dev(b_np)
+    s = torch.empty((N, E), dtype=torch.float32, device=G.DEV)
+    logits = torch.empty((N, E), dtype=torch.float32, device=G.DEV) if with_logits else None
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    load = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+    buf = qb.EqbBuffers(1, E, device=G.DEV, lead=False)
+    qb.qb_router_fused(hidden, w, b, K, s, alpha, logits_out=logits, load=load, hist_hi=buf.hist_hi)
+    return s, logits, alpha, load, buf, b
+
+
+@pytest.mark.parametrize("N,H,E,K", [(1000, 256, 256, 6), (333, 128, 64, 4), (129, 64, 32, 2),
+                                     (4096, 512, 128, 7)])
+def test_router_small(O, N, H, E, K):
+    hidden_np, w_np, b_np, _, _, _ = synth.router(seed=3, N=N, H=H, E=E)
+    G.say(f"router N={N} H={H} E={E} K={K}")
+    s, logits, alpha, load, buf, b = run_router(hidden_np, w_np, b_np, K)
+    torch.cuda.synchronize()
+    s_np, lg = G.host(s), G.host(logits)
+    check_logits(O, hidden_np, w_np, lg, np.arange(N))
+    check_scores(s_np, lg)
+    ref_a, ref_load = O.alpha(s_np, b_np, K)
+    G.assert_same("alpha", G.host(alpha), ref_a)
+    G.assert_same("load", G.host(load), ref_load)
+    ref = O.eqb_layer(s_np, b_np, K)
+    G.assert_same("hist_hi", G.host(buf.hist_hi), ref["hist_hi"])
+
+
+@pytest.mark.timeout(900)
+def test_router_full_size_chain(O):
+    """hidden [262144 x 2048] bf16, E=256, K=6: router, EQB update and LEI on
+    the produced scores; logits checked on 4096 sampled rows."""
+    p = synth.WORKLOADS["router"]
+    G.say("router full size: generating")
+    hidden_np, w_np, b_np, g_np, K, eta = synth.router()
+    N, E = p["N"], p["E"]
+    G.say("router full size: GPU")
+    s, logits, alpha, load, buf, b = run_router(hidden_np, w_np, b_np, K)
+    qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                        err=buf.err)
+    qb.qb_radix_hist_lo(s, alpha, buf.sel_hi, buf.hist_lo)
+    qb.qb_select_update(qb.QB_SELECT_LO, K, buf.hist_lo, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                        key_out=buf.key, q_out=buf.q, b=b, bounds=buf.bounds, err=buf.err)
+    g = G.dev(g_np)
+    qb.qb_lei_grad(g, load, K, eta)
+    torch.cuda.synchronize()
+    assert int(buf.err.item()) == 0
+    rows = np.random.default_rng(1).choice(N, 4096, replace=False)
+    s_np = G.host(s)
+    lg_rows = G.host(logits[torch.from_numpy(rows).to(G.DEV)])
+    G.say("router full size: oracle")
+    check_logits(O, hidden_np, w_np, lg_rows, rows)
+    check_scores(s_np[rows], lg_rows)
+    ref = O.eqb_layer(s_np, b_np, K)
+    got = dict(alpha=G.host(alpha), load=G.host(load), hist_hi=G.host(buf.hist_hi),
+               sel_hi=G.host(buf.sel_hi), rank_lo=G.host(buf.rank_lo), hist_lo=G.host(buf.hist_lo),
+               key=G.host(buf.key), q=G.host(buf.q), b_next=G.host(b), bounds=G.host(buf.bounds),
+               err=0)
+    G.compare_eqb(got, ref, tag="router ")
+    G.assert_same("lei g", G.host(g), O.lei(g_np, ref["load"], K, eta))

@@ -401,9 +401,9 @@ def test_lei_relative_error(O):
 def test_router_logits_vs_torch(O):
     rng = np.random.default_rng(12)
     h = rng.standard_normal((50, 96), dtype=np.float32)
-    w = rng.normal(0, 0.02, (96, 24)).astype(np.float32)
+    w = rng.normal(0, 0.02, (24, 96)).astype(np.float32)  # [E, H]
     hb, wb = torch_bf16_bits(h).reshape(h.shape), torch_bf16_bits(w).reshape(w.shape)
     rows = np.array([0, 7, 49, 3])
     out = O.router_logits(hb, wb, rows)
-    ref = (torch.from_numpy(bf16_values(hb)[rows]) @ torch.from_numpy(bf16_values(wb))).numpy()
+    ref = (torch.from_numpy(bf16_values(hb)[rows]) @ torch.from_numpy(bf16_values(wb)).T).numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
