@@ -205,6 +205,8 @@ def main():
     ap.add_argument("--suite", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1048576)
+    ap.add_argument("--router", action="store_true",
+                    help="time only the fused-router workload and print its JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the update shards over "
@@ -219,6 +221,12 @@ def main():
     qb.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.router:
+        log("router workload")
+        print(json.dumps({"workload": "router", "router": router_suite(torch, qb, synth, dev, args)}),
+              flush=True)
+        return
 
     p = synth.WORKLOADS["skew"]
     N, E, K = p["N"], p["E"], p["K"]

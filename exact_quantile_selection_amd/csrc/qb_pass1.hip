@@ -33,8 +33,6 @@ namespace qbk {
 
 // 16 waves per workgroup (<= 128 VGPRs each); the load-counting variant
 // keeps more state per lane and runs 8 waves (<= 256 VGPRs each).
-// 16 waves per workgroup (<= 128 VGPRs each); the load-counting variant
-// keeps more state per lane and runs 8 waves (<= 256 VGPRs each).
 template <bool LOAD>
 constexpr int p1_waves() { return LOAD ? 8 : 16; }
 
@@ -53,34 +51,49 @@ __device__ __forceinline__ uint64_t low_bits(int n) {
   return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
 }
 
+// Rotates the low V bits of m left by n (0 <= n < V).
+template <int V>
+__device__ __forceinline__ uint64_t rotl_v(uint64_t m, int n) {
+  if constexpr (V == 64) {
+    return n == 0 ? m : (m << n) | (m >> (64 - n));
+  } else {
+    constexpr uint64_t kMask = (1ull << V) - 1ull;
+    return n == 0 ? m : (((m << n) | (m >> (V - n))) & kMask);
+  }
+}
+
 // Top-K membership of this lane's scores for one row, added to the LDS load
 // counters.  Members are v > alpha plus, when alpha's value occurs more than
 // once, the lowest-index elements equal to alpha up to K in total.  A lane's
-// element (u, c) has expert j = 4*(LPR*u + ql) + c; `eq` holds bit 4u+c for
-// elements equal to alpha, so bit order is j order within a lane.
+// element (u, c) has expert j = 4*(LPR*u + ql) + c and mask bit 4u + c, so
+// bit order is j order within a lane.  The masks are first built in load
+// order (bit 4t + c, constant positions) and then rotated by the lane's
+// column rotation; the counters take one LDS atomic per member.
 template <int E, int P>
 __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], const float* lds_b,
-                                            int rho, int ql, int lane, float a, int K, bool valid,
+                                            int rho, int ql, float a, int K, bool valid,
                                             int32_t* lds_load) {
   using S = P1Shape<E>;
-  int gt = 0;
-  uint64_t eq = 0;
+  uint64_t gt_t = 0, eq_t = 0;
 #pragma unroll
   for (int t = 0; t < S::F4; ++t) {
-    const int u = (t + rho) & (S::F4 - 1);
-    const int quad = S::LPR * u + ql;
+    const int quad = S::LPR * ((t + rho) & (S::F4 - 1)) + ql;
     const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float v = comp(x[t], c) + comp(bb, c);
-      gt += v > a;
-      if (v == a) eq |= 1ull << (4 * u + c);
+      gt_t |= v > a ? 1ull << (4 * t + c) : 0ull;
+      eq_t |= v == a ? 1ull << (4 * t + c) : 0ull;
     }
   }
-  int G = gt;
+  const int rot = 4 * (rho & (S::F4 - 1));
+  uint64_t mem = rotl_v<S::V>(gt_t, rot);
+  const uint64_t eq = rotl_v<S::V>(eq_t, rot);
+  int G = __popcll(gt_t);
   if constexpr (S::LPR >= 2) G += quad_mov_i<kQuadXor1>(G);
   if constexpr (S::LPR == 4) G += quad_mov_i<kQuadXor2>(G);
   const int need = K - G;  // equal-to-alpha elements that still belong to the top K
+  // equal-to-alpha masks of the row's lanes (exchanged with every lane active)
   uint64_t M[S::LPR];
 #pragma unroll
   for (int q2 = 0; q2 < S::LPR; ++q2) {
@@ -89,32 +102,31 @@ __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], c
     const uint32_t hi = __shfl(uint32_t(eq >> 32), src);
     M[q2] = (uint64_t(hi) << 32) | lo;
   }
-  (void)lane;
   if (!valid) return;
+  if (need > 0) {
+    // an element equal to alpha is a member when fewer than `need` equal
+    // elements of the row precede it in expert order
+    uint64_t e = eq;
+    while (e) {
+      const int bit = __builtin_ctzll(e);
+      e &= e - 1;
+      const int u = bit >> 2, c = bit & 3;
+      int r = 0;
 #pragma unroll
-  for (int t = 0; t < S::F4; ++t) {
-    const int u = (t + rho) & (S::F4 - 1);
-    const int quad = S::LPR * u + ql;
-    const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float v = comp(x[t], c) + comp(bb, c);
-      bool member = v > a;
-      if (!member && need > 0 && v == a) {
-        int r = 0;
-#pragma unroll
-        for (int q2 = 0; q2 < S::LPR; ++q2) {
-          const int nb = q2 < ql ? 4 * (u + 1) : (q2 > ql ? 4 * u : 4 * u + c);
-          r += __popcll(M[q2] & low_bits(nb));
-        }
-        member = r < need;
+      for (int q2 = 0; q2 < S::LPR; ++q2) {
+        const int nb = q2 < ql ? 4 * (u + 1) : (q2 > ql ? 4 * u : 4 * u + c);
+        r += __popcll(M[q2] & low_bits(nb));
       }
-      if (member) atomicAdd(&lds_load[4 * quad + c], 1);
+      if (r < need) mem |= 1ull << bit;
     }
+  }
+  while (mem) {
+    const int bit = __builtin_ctzll(mem);
+    mem &= mem - 1;
+    atomicAdd(&lds_load[4 * (S::LPR * (bit >> 2) + ql) + (bit & 3)], 1);
   }
 }
 
-// Loads one trip's rows (this lane's V scores of row base + rho) into x.
 // Loads one trip's rows (this lane's V scores of row base + rho) into x.
 // `base` is wave-uniform: a full trip addresses its rows from a uniform base
 // pointer with 32-bit lane offsets; a partial last trip clamps the row.
@@ -176,7 +188,7 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
     a = top_merge_last<P, kQuadXor2>(top);
   }
   if (valid && ql == 0) alpha[row] = a;
-  if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, lane, a, K, valid, lds_load);
+  if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load);
   if constexpr (HIST) {
     if (valid) {
 #pragma unroll
