@@ -336,7 +336,46 @@ def suite(torch, qb, synth, dev, args):
     del s, st
     torch.cuda.empty_cache()
     res["router"] = router_suite(torch, qb, synth, dev, args)
+    res["controller"] = controller_suite(torch, qb, synth, dev, args)
     return res
+
+
+def controller_suite(torch, qb, synth, dev, args, T=8):
+    """Closed-loop bias controller on the batch stream (262,144 tokens x 256
+    experts, K = 6, 4096-token microbatches): each step routes a fresh batch
+    with the current bias, measures global / local MaxVio and replaces the
+    bias by the batch's EQB update.  The batches follow synth.stream_batch's
+    recipe, drawn on the device with torch's seeded generator."""
+    import numpy as np
+    from exact_quantile_selection_amd.controller import BiasController
+
+    p = synth.WORKLOADS["stream"]
+    N, E, K, n_mb = p["N"], p["E"], p["K"], p["n_mb"]
+    off = torch.from_numpy(synth.zipf_offsets(np.random.default_rng([0, 1000]), E)).to(dev, torch.float32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    batches = [torch.sigmoid(torch.randn((N, E), generator=g, device=dev) + off) for _ in range(T)]
+    ctl = BiasController(1, N, E, K, n_mb, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(T + 1)]
+    traj = []
+    torch.cuda.synchronize()
+    ev[0].record()
+    for t in range(T):
+        ctl.step(batches[t])
+        ev[t + 1].record()
+        traj.append((ctl.worst_global.clone(), ctl.worst_local.clone()))
+    torch.cuda.synchronize()
+    step_us = [ev[t].elapsed_time(ev[t + 1]) * 1e3 for t in range(T)]
+    out = dict(N=N, E=E, K=K, n_mb=n_mb, steps=T,
+               step_us_median=round(float(np.median(step_us)), 2),
+               global_maxvio=[round(float(a[0]), 4) for a, _ in traj],
+               local_maxvio_mean=[round(float(b[1]), 4) for _, b in traj],
+               local_maxvio_max=[round(float(b[0]), 4) for _, b in traj],
+               step="pass 1 (alpha, loads, hist_hi), microbatch loads, 2 x MaxVio, select HI, "
+                    "pass 2, select LO (b updated in place)")
+    del batches
+    torch.cuda.empty_cache()
+    return out
 
 
 def router_suite(torch, qb, synth, dev, args):

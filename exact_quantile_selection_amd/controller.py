@@ -1,0 +1,71 @@
+"""Closed-loop bias controller: each global batch is routed with the current
+bias, its loads give the balance metrics, and the EQB update of that batch
+becomes the bias of the next one.
+
+The loop is the one the pages describe: the bias is updated in place once per
+global batch from the K/E quantile of that batch's routing margins ("[Dev] Add
+global-batch quantile balancing", sections "Quantile estimator" and
+"Implementation"), and balance is reported as global MaxVio (all tokens of the
+step) and local MaxVio (per microbatch) ("Exact Quantile Balancing and
+Load-Error Injection for Mixture-of-Experts", summary page, background and
+testbed paragraphs).
+
+Every step below is a libqb call; this module only owns buffers and orders
+the calls.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import qb
+
+
+class BiasController:
+    """EQB bias state and metric buffers for L router layers of E experts."""
+
+    def __init__(self, L: int, N: int, E: int, K: int, n_mb: int, b0=None, device="cuda"):
+        if N % n_mb:
+            raise ValueError(f"n_mb={n_mb} must divide N={N}")
+        self.L, self.N, self.E, self.K, self.n_mb = L, N, E, K, n_mb
+        self.C = N // n_mb
+        kw = dict(device=device)
+        self.b = (torch.zeros((L, E), dtype=torch.float32, **kw) if b0 is None
+                  else b0.to(device=device, dtype=torch.float32).reshape(L, E).clone())
+        self.buf = qb.EqbBuffers(L, E, device=device)
+        self.alpha = torch.empty((L, N), dtype=torch.float32, **kw)
+        # one int32 block: global loads [L][E] then microbatch loads [L][C][E],
+        # cleared by one fill per step
+        self.loads = torch.zeros(L * E * (1 + self.C), dtype=torch.int32, **kw)
+        self.load = self.loads[:L * E].view(L, E)
+        self.load_mb = self.loads[L * E:].view(L, self.C, E)
+        self.mv_global = torch.empty((L, 1), dtype=torch.float32, **kw)
+        self.mv_local = torch.empty((L, self.C), dtype=torch.float32, **kw)
+        self.summary_global = torch.empty((L, 2), dtype=torch.float32, **kw)
+        self.summary_local = torch.empty((L, 2), dtype=torch.float32, **kw)
+        self.worst_global = torch.empty(2, dtype=torch.float32, **kw)
+        self.worst_local = torch.empty(2, dtype=torch.float32, **kw)
+
+    def step(self, s: torch.Tensor, stream=None):
+        """Route batch s ([L, N, E] or [N, E] when L == 1) with the current
+        bias, record its loads and MaxVio, then replace the bias by the EQB
+        update of this batch.  Everything stays on the device; read
+        `worst_global` / `worst_local` (and the per-layer arrays) afterwards."""
+        L, N, E, K = self.L, self.N, self.E, self.K
+        s3 = s.view(L, N, E)
+        buf = self.buf
+        buf.reset(stream)
+        qb.qb_fill_i32(self.loads, 0, stream)
+        # pass 1 with the bias in force: alpha, loads, high-byte histogram
+        qb.qb_margins_topk(s3, self.b, K, self.alpha, load=self.load, hist_hi=buf.hist_hi, stream=stream)
+        qb.qb_microbatch_loads(s3, self.b, K, self.n_mb, self.alpha, self.load_mb, stream=stream)
+        qb.qb_maxvio(self.load.view(L, 1, E), K, N, self.mv_global, self.summary_global,
+                     self.worst_global, stream=stream)
+        qb.qb_maxvio(self.load_mb, K, self.n_mb, self.mv_local, self.summary_local, self.worst_local,
+                     stream=stream)
+        # EQB update of this batch, written over b
+        qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                            err=buf.err, stream=stream)
+        qb.qb_radix_hist_lo(s3, self.alpha, buf.sel_hi, buf.hist_lo, stream=stream)
+        qb.qb_select_update(qb.QB_SELECT_LO, K, buf.hist_lo, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                            key_out=buf.key, q_out=buf.q, b=self.b, bounds=buf.bounds, err=buf.err,
+                            stream=stream)

@@ -11,24 +11,26 @@
 #include <string>
 
 #include "../../include/qb.h"
+#include <climits>
+
 #include "qb_internal.hpp"
 
 namespace qbk {
 
-int launch_margins_topk_e16(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
-int launch_margins_topk_e32(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
-int launch_margins_topk_e64(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
-int launch_margins_topk_e128(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
-int launch_margins_topk_e256(const float*, const float*, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e16(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e32(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e64(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e128(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e256(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
 
 int launch_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
-                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st) {
+                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv) {
   switch (E) {
-    case 16: return launch_margins_topk_e16(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 32: return launch_margins_topk_e32(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 64: return launch_margins_topk_e64(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 128: return launch_margins_topk_e128(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 256: return launch_margins_topk_e256(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 16: return launch_margins_topk_e16(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 32: return launch_margins_topk_e32(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 64: return launch_margins_topk_e64(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 128: return launch_margins_topk_e128(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 256: return launch_margins_topk_e256(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
   }
   return int(hipErrorInvalidValue);
 }
@@ -128,6 +130,46 @@ QB_API int qb_margins_topk(const float* s, const float* b, int L, int64_t N, int
     return fail(QB_EINVAL, "%s: b, alpha and load must be 4-byte aligned", fn);
   if (hist_hi && !aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
   return hip_status(qbk::launch_margins_topk(s, b, L, N, E, K, alpha, load, hist_hi, stream), fn);
+}
+
+QB_API int qb_microbatch_loads(const float* s, const float* b, int L, int64_t N, int E, int K,
+                               int64_t n_mb, float* alpha, int32_t* load_mb, qb_stream_t stream) {
+  const char* fn = "qb_microbatch_loads";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!b) return fail(QB_EINVAL, "%s: b is NULL (expected float [L=%d][E=%d])", fn, L, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (n_mb < 1 || N % n_mb != 0)
+    return fail(QB_EINVAL, "%s: n_mb=%lld must be >= 1 and divide N=%lld", fn, (long long)n_mb,
+                (long long)N);
+  const int64_t C = N / n_mb;
+  if (int64_t(L) * C > int64_t(INT_MAX))
+    return fail(QB_EINVAL, "%s: L * (N / n_mb) = %lld microbatches is too many", fn,
+                (long long)(int64_t(L) * C));
+  if (!alpha || !load_mb)
+    return fail(QB_EINVAL, "%s: alpha (float [L=%d][N=%lld]) and load_mb (int32 [L=%d][C=%lld][E=%d]) are required",
+                fn, L, (long long)N, L, (long long)C, E);
+  if (!aligned4(b) || !aligned4(alpha) || !aligned4(load_mb))
+    return fail(QB_EINVAL, "%s: b, alpha and load_mb must be 4-byte aligned", fn);
+  return hip_status(qbk::launch_margins_topk(s, b, int(L * C), n_mb, E, K, alpha, load_mb, nullptr, stream,
+                                             int(C)),
+                    fn);
+}
+
+QB_API int qb_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_tok, float* maxvio,
+                     float* summary, float* worst, qb_stream_t stream) {
+  const char* fn = "qb_maxvio";
+  if (L < 1 || C < 1 || E < 1 || K < 1 || K > E || n_tok < 1)
+    return fail(QB_EINVAL, "%s: L=%d, C=%d, E=%d, K=%d, n_tok=%lld; expected all >= 1 and K <= E", fn, L, C,
+                E, K, (long long)n_tok);
+  if (int64_t(L) * C > int64_t(INT_MAX))
+    return fail(QB_EINVAL, "%s: L * C = %lld rows is too many", fn, (long long)(int64_t(L) * C));
+  if (!load || !maxvio)
+    return fail(QB_EINVAL, "%s: load (int32 [L=%d][C=%d][E=%d]) and maxvio (float [L][C]) are required", fn, L,
+                C, E);
+  if (!aligned4(load) || !aligned4(maxvio) || (summary && !aligned4(summary)) || (worst && !aligned4(worst)))
+    return fail(QB_EINVAL, "%s: load, maxvio, summary and worst must be 4-byte aligned", fn);
+  return hip_status(qbk::launch_maxvio(load, L, C, E, K, n_tok, maxvio, summary, worst, stream), fn);
 }
 
 QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N, int E,

@@ -23,8 +23,12 @@ RowSplit split_rows(int L, int64_t N, int step, int64_t max_rows);
 int device_cu_count();
 
 // Launchers (return hipError_t as int).  Shapes were validated by the caller.
+// bdiv: that many consecutive layers share one bias row (1: one row per
+// layer; C: layers are the C microbatches of one layer).
 int launch_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
-                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st);
+                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv = 1);
+int launch_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_tok, float* v,
+                  float* summary, float* worst, hipStream_t st);
 int launch_radix_hist(bool lo, const float* s, const float* alpha, int L, int64_t N, int E,
                       const int32_t* sel_hi, int32_t* hist, hipStream_t st);
 int launch_margin_keys(const float* s, const float* alpha, int L, int64_t N, int E, uint16_t* keys,

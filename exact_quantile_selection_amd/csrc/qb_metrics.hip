@@ -1,0 +1,92 @@
+// qb_metrics.hip -- the load-balance metric MaxVio over expert loads.
+//
+// "Exact Quantile Balancing and Load-Error Injection for Mixture-of-Experts"
+// (summary page): the background paragraph separates global balance (all
+// tokens of an optimizer step) from local balance (inside each microbatch);
+// the testbed paragraph defines MaxVio as how far the busiest expert of the
+// worst layer exceeds the uniform share (a value of 5.96 is about 7x that
+// share).  For a row of loads over n_tok tokens the uniform share is
+// n_tok * K / E, and
+//     v = fl32((double)max_e load_e / ((double)n_tok * K / E) - 1).
+// Per layer the rows are its C microbatches (C = 1 for the global metric);
+// the summary is [max over c, mean over c] (float64 sum in microbatch
+// order), and `worst` the maximum of each over layers.
+#include <climits>
+
+#include "qb_device.hpp"
+#include "qb_internal.hpp"
+
+namespace qbk {
+
+constexpr int kMvThreads = 256;
+
+// One wave per row of E loads.
+__global__ __launch_bounds__(kMvThreads) void k_maxvio_rows(const int32_t* __restrict__ load,
+                                                            int64_t R, int E, int K, int64_t n_tok,
+                                                            float* __restrict__ v) {
+  const int64_t r = int64_t(blockIdx.x) * (kMvThreads / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (r >= R) return;  // wave-uniform
+  const int32_t* row = load + r * E;
+  int m = INT_MIN;
+  for (int e = lane; e < E; e += kWave) m = max(m, row[e]);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
+  if (lane == 0) {
+    const double share = double(n_tok) * double(K) / double(E);
+    v[r] = float(double(m) / share - 1.0);
+  }
+}
+
+// Per-layer summary and the worst layer; one workgroup.
+__global__ __launch_bounds__(kMvThreads) void k_maxvio_summary(const float* __restrict__ v, int L,
+                                                               int C, float* __restrict__ summary,
+                                                               float* __restrict__ worst) {
+  __shared__ float s_max[kMvThreads], s_mean[kMvThreads];
+  float wmax = -__builtin_inff(), wmean = -__builtin_inff();
+  for (int l = threadIdx.x; l < L; l += kMvThreads) {
+    const float* row = v + int64_t(l) * C;
+    float mx = row[0];
+    double sum = 0.0;
+    for (int c = 0; c < C; ++c) {
+      mx = fmaxf(mx, row[c]);
+      sum += double(row[c]);
+    }
+    const float mean = float(sum / double(C));
+    if (summary) {
+      summary[2 * l] = mx;
+      summary[2 * l + 1] = mean;
+    }
+    wmax = fmaxf(wmax, mx);
+    wmean = fmaxf(wmean, mean);
+  }
+  s_max[threadIdx.x] = wmax;
+  s_mean[threadIdx.x] = wmean;
+  __syncthreads();
+  if (threadIdx.x == 0 && worst) {
+    float a = s_max[0], b = s_mean[0];
+    for (int t = 1; t < kMvThreads; ++t) {
+      a = fmaxf(a, s_max[t]);
+      b = fmaxf(b, s_mean[t]);
+    }
+    worst[0] = a;
+    worst[1] = b;
+  }
+}
+
+int launch_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_tok, float* v,
+                  float* summary, float* worst, hipStream_t st) {
+  const int64_t R = int64_t(L) * C;
+  constexpr int kRowsPerBlock = kMvThreads / kWave;
+  const dim3 grid{unsigned((R + kRowsPerBlock - 1) / kRowsPerBlock), 1u, 1u};
+  const dim3 block{unsigned(kMvThreads), 1u, 1u};
+  hipLaunchKernelGGL(k_maxvio_rows, grid, block, 0, st, load, R, E, K, n_tok, v);
+  if (int rc = int(hipGetLastError())) return rc;
+  if (summary || worst) {
+    hipLaunchKernelGGL(k_maxvio_summary, dim3(1u), block, 0, st, v, L, C, summary, worst);
+    return int(hipGetLastError());
+  }
+  return 0;
+}
+
+}  // namespace qbk

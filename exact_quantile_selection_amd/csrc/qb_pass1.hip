@@ -204,7 +204,7 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
 
 template <int E, int P, bool HIST, bool LOAD>
 __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
-    const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int K,
+    const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int bdiv, int K,
     float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi) {
   using S = P1Shape<E>;
   constexpr int kWaves = p1_waves<LOAD>();
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
   const int layer = blockIdx.x / wg_per_layer;
   const int g = blockIdx.x - layer * wg_per_layer;
   s += int64_t(layer) * N * E;
-  b += int64_t(layer) * E;
+  b += int64_t(layer / bdiv) * E;  // bdiv consecutive layers share a bias row
   alpha += int64_t(layer) * N;
 
   if constexpr (HIST) hist16_zero<E>(lds_hist, tid, kThreads);
@@ -250,35 +250,35 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
 }
 
 template <int E, int P, bool HIST, bool LOAD>
-static int launch_p1_v(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
+static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st) {
   constexpr int kThreads = p1_waves<LOAD>() * kWave;
   const RowSplit sp = split_rows(L, N, p1_waves<LOAD>() * P1Shape<E>::RPW, 65535);
   hipLaunchKernelGGL((k_margins_topk<E, P, HIST, LOAD>), dim3(unsigned(sp.blocks)), dim3(kThreads),
-                     0, st, s, b, N, sp.wg_per_layer, K, alpha, load, hist_hi);
+                     0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi);
   return int(hipGetLastError());
 }
 
 template <int E, int P>
-static int launch_p1(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
+static int launch_p1(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                      int32_t* load, int32_t* hist_hi, hipStream_t st) {
-  if (hist_hi && load) return launch_p1_v<E, P, true, true>(s, b, L, N, K, alpha, load, hist_hi, st);
-  if (hist_hi) return launch_p1_v<E, P, true, false>(s, b, L, N, K, alpha, load, hist_hi, st);
-  if (load) return launch_p1_v<E, P, false, true>(s, b, L, N, K, alpha, load, hist_hi, st);
-  return launch_p1_v<E, P, false, false>(s, b, L, N, K, alpha, load, hist_hi, st);
+  if (hist_hi && load) return launch_p1_v<E, P, true, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  if (hist_hi) return launch_p1_v<E, P, true, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  if (load) return launch_p1_v<E, P, false, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  return launch_p1_v<E, P, false, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
 }
 
 template <int E>
-static int launch_p1_k(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
+static int launch_p1_k(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st) {
   switch (K + 1) {
-    case 2: return launch_p1<E, 2>(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 3: return launch_p1<E, 3>(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 4: return launch_p1<E, 4>(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 5: return launch_p1<E, 5>(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 6: return launch_p1<E, 6>(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 7: return launch_p1<E, 7>(s, b, L, N, K, alpha, load, hist_hi, st);
-    case 8: return launch_p1<E, 8>(s, b, L, N, K, alpha, load, hist_hi, st);
+    case 2: return launch_p1<E, 2>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 3: return launch_p1<E, 3>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 4: return launch_p1<E, 4>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 5: return launch_p1<E, 5>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 6: return launch_p1<E, 6>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 7: return launch_p1<E, 7>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 8: return launch_p1<E, 8>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
   }
   return int(hipErrorInvalidValue);
 }
@@ -289,10 +289,10 @@ static int launch_p1_k(const float* s, const float* b, int L, int64_t N, int K, 
 
 #define QB_P1_CAT2(a, b) a##b
 #define QB_P1_CAT(a, b) QB_P1_CAT2(a, b)
-int QB_P1_CAT(launch_margins_topk_e, QB_P1_E)(const float* s, const float* b, int L, int64_t N,
-                                               int K, float* alpha, int32_t* load,
+int QB_P1_CAT(launch_margins_topk_e, QB_P1_E)(const float* s, const float* b, int L, int bdiv,
+                                               int64_t N, int K, float* alpha, int32_t* load,
                                                int32_t* hist_hi, hipStream_t st) {
-  return launch_p1_k<QB_P1_E>(s, b, L, N, K, alpha, load, hist_hi, st);
+  return launch_p1_k<QB_P1_E>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
 }
 
 }  // namespace qbk

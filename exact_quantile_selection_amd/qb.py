@@ -56,6 +56,8 @@ def lib() -> C.CDLL:
             "qb_fill_i32": [vp, i64, C.c_int32, vp],
             "qb_lei_grad": [vp, vp, i64, i32, i32, f32, vp],
             "qb_router_fused": [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
+            "qb_microbatch_loads": [vp, vp, i32, i64, i32, i32, i64, vp, vp, vp],
+            "qb_maxvio": [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -196,6 +198,28 @@ def qb_lei_grad(g, load, K, eta, stream=None):
     N, E = g.shape
     _check(lib().qb_lei_grad(_ptr(g, torch.float32, "g"), _ptr(load, torch.int32, "load", (E,)),
                              N, E, K, float(eta), _stream(stream)))
+
+
+def qb_microbatch_loads(s, b, K, n_mb, alpha, load_mb, stream=None):
+    """load_mb [C, E] (or [L, C, E]) += top-K loads of each n_mb-token microbatch."""
+    L, N, E, lead = _lne(s)
+    if n_mb < 1 or N % n_mb:
+        raise ValueError(f"n_mb={n_mb} must divide N={N}")
+    _check(lib().qb_microbatch_loads(
+        _ptr(s, torch.float32, "s"), _ptr(b, torch.float32, "b", lead + (E,)), L, N, E, K, n_mb,
+        _ptr(alpha, torch.float32, "alpha", lead + (N,)),
+        _ptr(load_mb, torch.int32, "load_mb", lead + (N // n_mb, E)), _stream(stream)))
+
+
+def qb_maxvio(load, K, n_tok, maxvio, summary=None, worst=None, stream=None):
+    """load int32 [L, C, E] -> maxvio [L, C]; optional summary [L, 2], worst [2]."""
+    if load.dim() != 3:
+        raise ValueError(f"load must be [L, C, E], got {tuple(load.shape)}")
+    L, Cm, E = load.shape
+    _check(lib().qb_maxvio(
+        _ptr(load, torch.int32, "load"), L, Cm, E, K, n_tok, _ptr(maxvio, torch.float32, "maxvio", (L, Cm)),
+        _ptr(summary, torch.float32, "summary", (L, 2), opt=True),
+        _ptr(worst, torch.float32, "worst", (2,), opt=True), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

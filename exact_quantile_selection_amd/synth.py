@@ -17,6 +17,10 @@ Workloads (every generator is seeded; seed 0 unless stated):
   margins collide after rounding to bf16; b ~ U(-0.2, 0.2).
 * ``step``   48 layers of N=262,144, E=256, K=6; layer l draws from
   ``default_rng([0, l])``: mu_l ~ U(-1,1), b_l ~ U(-0.1,0.1), logits ~ N(mu_l, 1).
+* ``stream`` a sequence of batches for the closed-loop bias controller:
+  batch t draws logits N(0,1) + fixed per-expert Zipf(1.1) offsets scaled to
+  [0, 2] (layer l's offsets from ``default_rng([seed, 1000 + l])``, noise
+  from ``default_rng([seed, t, l])``); the bias is the controller's own state.
 * ``router`` hidden bf16 [262144 x 2048] ~ N(0,1), router weight bf16
   [2048 x 256] ~ N(0, std 0.02) (stored [256 x 2048]), b = 0, upstream score
   gradient g ~ N(0,1) fp32, eta = 1e-5.
@@ -39,6 +43,7 @@ WORKLOADS = {
     "skew": dict(N=1048576, E=256, K=6, L=1),
     "step": dict(N=262144, E=256, K=6, L=48),
     "router": dict(N=262144, E=256, K=6, L=1, H=2048),
+    "stream": dict(N=262144, E=256, K=6, L=1, n_mb=4096),
 }
 
 _CHUNK_ROWS = 65536
@@ -112,6 +117,16 @@ def step_layer(layer: int, N: int | None = None, out: np.ndarray | None = None):
     s = np.empty((N, E), dtype=np.float32) if out is None else out
     _fill_scores(s, rng, mu, None)
     return s, b, p["K"]
+
+
+def stream_batch(step: int, N: int, E: int, L: int = 1, seed: int = 0):
+    """Scores [L, N, E] of batch `step` of the controller stream; layer l
+    uses its own fixed offsets (``default_rng([seed, 1000 + l])``)."""
+    out = np.empty((L, N, E), dtype=np.float32)
+    for l in range(L):
+        off = zipf_offsets(np.random.default_rng([seed, 1000 + l]), E)
+        _fill_scores(out[l], np.random.default_rng([seed, step, l]), off, None)
+    return out
 
 
 def router(seed: int = 0, N: int | None = None, H: int | None = None, E: int | None = None):

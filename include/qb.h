@@ -190,6 +190,37 @@ QB_API int qb_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N,
                            int32_t* load, int32_t* hist_hi, qb_stream_t stream);
 
 /*
+ * Top-K expert loads per microbatch, for the local-balance metric
+ * ("Exact Quantile Balancing and Load-Error Injection for Mixture-of-Experts",
+ * summary page, background paragraph: global balance over all tokens of a
+ * step, local balance inside each microbatch).  Each layer's N tokens are cut
+ * into C = N / n_mb consecutive microbatches; load_mb[l][c][e] += number of
+ * tokens of microbatch c whose top-K set of s + b[l] (ties: lower expert
+ * index) contains e.  This is qb_margins_topk's load counting run per
+ * microbatch, with the layer's bias shared by its microbatches.
+ *   s float [L][N][E]; b float [L][E]; n_mb >= 1 must divide N;
+ *   alpha float [L][N] receives the same values qb_margins_topk writes;
+ *   load_mb int32 [L][C][E], accumulated (+=).
+ */
+QB_API int qb_microbatch_loads(const float* s, const float* b, int L, int64_t N, int E, int K,
+                               int64_t n_mb, float* alpha, int32_t* load_mb, qb_stream_t stream);
+
+/*
+ * MaxVio ("Exact Quantile Balancing and Load-Error Injection for
+ * Mixture-of-Experts", summary page, testbed paragraph: how far the busiest
+ * expert of the worst layer exceeds the uniform load).  For each of the L*C
+ * rows of load (layer l, microbatch c; C = 1 for the whole batch), over
+ * n_tok tokens each:
+ *   maxvio[l][c] = fl32((double)max_e load[l][c][e] / ((double)n_tok * K / E) - 1)
+ *   summary[l]   = {max over c, fl32(float64 sum over c in order / C)}  (nullable)
+ *   worst        = {max over l of summary[l][0], max over l of summary[l][1]}  (nullable)
+ *   load int32 [L][C][E]; maxvio float [L][C]; summary float [L][2]; worst float [2].
+ *   Any E >= 1, 1 <= K <= E, n_tok >= 1.
+ */
+QB_API int qb_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_tok, float* maxvio,
+                     float* summary, float* worst, qb_stream_t stream);
+
+/*
  * LEI ("Exact Quantile Balancing and Load-Error Injection for
  * Mixture-of-Experts", summary page, LEI paragraph): with M = N*K/E,
  * rho_e = fl32((load_e - M) / M) in float64, add_e = fl32(eta * rho_e),

@@ -71,6 +71,9 @@ def lib():
         L.oq_bounds_of.argtypes = [f32p, C.c_int, f32p]
         L.oq_lei.restype = None
         L.oq_lei.argtypes = [f32p, i32p, C.c_int64, C.c_int, C.c_int, C.c_float]
+        L.oq_maxvio.restype = None
+        L.oq_maxvio.argtypes = [i32p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, f32p,
+                                C.c_void_p, C.c_void_p]
         L.oq_router_logits.restype = None
         L.oq_router_logits.argtypes = [u16p, u16p, C.c_int, C.c_int, i64p, C.c_int, f64p]
         _lib = L
@@ -176,3 +179,26 @@ def router_logits(hidden_bits, w_bits, rows) -> np.ndarray:
     out = np.zeros((rows.size, E), np.float64)
     lib().oq_router_logits(hidden_bits, w_bits, H, E, rows, rows.size, out)
     return out
+
+
+def microbatch_loads(s, b, K: int, n_mb: int) -> np.ndarray:
+    """Top-K loads of each consecutive n_mb-token microbatch, [C, E]: the
+    oracle's top-K selection run on each chunk of rows."""
+    s = _f32(s)
+    N, E = s.shape
+    assert N % n_mb == 0
+    out = np.zeros((N // n_mb, E), np.int32)
+    for c in range(N // n_mb):
+        _, out[c] = alpha(s[c * n_mb:(c + 1) * n_mb], b, K)
+    return out
+
+
+def maxvio(load, K: int, n_tok: int):
+    """load [L, C, E] -> (v [L, C], summary [L, 2], worst [2])."""
+    load = np.ascontiguousarray(load, dtype=np.int32)
+    L, C, E = load.shape
+    v = np.zeros((L, C), np.float32)
+    summary = np.zeros((L, 2), np.float32)
+    worst = np.zeros(2, np.float32)
+    lib().oq_maxvio(load, L, C, E, K, n_tok, v, summary.ctypes.data, worst.ctypes.data)
+    return v, summary, worst

@@ -285,4 +285,40 @@ void oq_router_logits(const uint16_t* hidden, const uint16_t* w, int H, int E,
   }
 }
 
+// MaxVio ([EQB] testbed paragraph: how far the busiest expert exceeds the
+// uniform load; background paragraph: global vs per-microbatch balance).
+// Rows are (layer, microbatch) pairs of E loads over n_tok tokens each:
+//   v[r] = fl32(max_e load[r][e] / (n_tok * K / E) - 1) in float64;
+// per layer: summary = {max over its C rows, fl32(float64 sum / C)};
+// worst = {max over layers of each}.  summary / worst may be NULL.
+void oq_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_tok, float* v,
+               float* summary, float* worst) {
+  const double share = double(n_tok) * double(K) / double(E);
+  float wmax = -INFINITY, wmean = -INFINITY;
+  for (int l = 0; l < L; ++l) {
+    float mx = -INFINITY;
+    double sum = 0.0;
+    for (int c = 0; c < C; ++c) {
+      const int32_t* row = load + (int64_t(l) * C + c) * E;
+      int32_t m = row[0];
+      for (int e = 1; e < E; ++e) m = std::max(m, row[e]);
+      const float vi = float(double(m) / share - 1.0);
+      v[int64_t(l) * C + c] = vi;
+      mx = std::max(mx, vi);
+      sum += double(vi);
+    }
+    const float mean = float(sum / double(C));
+    if (summary) {
+      summary[2 * l] = mx;
+      summary[2 * l + 1] = mean;
+    }
+    wmax = std::max(wmax, mx);
+    wmean = std::max(wmean, mean);
+  }
+  if (worst) {
+    worst[0] = wmax;
+    worst[1] = wmean;
+  }
+}
+
 }  // extern "C"

@@ -87,6 +87,14 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
     assert rc == qb.QB_EUNSUPPORTED
     rc = libqb.qb_margin_keys(fake, fake, 1, 10, 256, fake + 2, None)
     assert rc == qb.QB_EINVAL and "8-byte aligned" in _last(libqb)
+    rc = libqb.qb_microbatch_loads(fake, fake, 1, 1000, 256, 6, 300, fake, fake, None)
+    assert rc == qb.QB_EINVAL and "divide N=1000" in _last(libqb)
+    rc = libqb.qb_microbatch_loads(fake, fake, 1, 1024, 256, 6, 256, fake, None, None)
+    assert rc == qb.QB_EINVAL and "[C=4][E=256]" in _last(libqb)
+    rc = libqb.qb_maxvio(fake, 1, 4, 256, 300, 1024, fake, None, None, None)
+    assert rc == qb.QB_EINVAL and "K=300" in _last(libqb)
+    rc = libqb.qb_maxvio(fake, 1, 4, 256, 6, 1024, None, None, None, None)
+    assert rc == qb.QB_EINVAL and "maxvio" in _last(libqb)
     assert libqb.qb_fill_i32(None, 0, 0, None) == qb.QB_OK  # empty fill is a no-op
     assert libqb.qb_fill_i32(None, 5, 0, None) == qb.QB_EINVAL
     for st in (0, -1, -2, -3):

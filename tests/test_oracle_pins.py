@@ -407,3 +407,55 @@ def test_router_logits_vs_torch(O):
     out = O.router_logits(hb, wb, rows)
     ref = (torch.from_numpy(bf16_values(hb)[rows]) @ torch.from_numpy(bf16_values(wb)).T).numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+# --- MaxVio and per-microbatch loads ("Exact Quantile Balancing and
+# Load-Error Injection for Mixture-of-Experts", summary page: testbed
+# paragraph for MaxVio, background paragraph for global vs local balance).
+
+def test_maxvio_closed_forms(O):
+    E, K, n = 64, 4, 1024
+    uniform = np.full((1, 1, E), n * K // E, np.int32)
+    v, summ, worst = O.maxvio(uniform, K, n)
+    assert v[0, 0] == 0.0 and worst[0] == 0.0 and worst[1] == 0.0
+    # K = 1 and every token on one expert: the busiest expert carries E times
+    # the uniform share
+    one = np.zeros((1, 1, E), np.int32)
+    one[0, 0, 17] = n
+    v, _, _ = O.maxvio(one, 1, n)
+    assert v[0, 0] == np.float32(E - 1)
+
+
+def test_maxvio_reading_of_the_page_example(O):
+    """The testbed paragraph: a MaxVio of 5.96 means roughly 7x the uniform
+    share, i.e. MaxVio + 1 is the busiest expert's load over the share."""
+    E, K, n = 256, 6, 4096            # share = 96 tokens
+    load = np.full((1, 1, E), 90, np.int32)
+    load[0, 0, 3] = 668               # 668 / 96 = 6.958...
+    v, _, _ = O.maxvio(load, K, n)
+    assert abs(float(v[0, 0]) - 5.96) < 5e-3
+    assert round(float(v[0, 0]) + 1.0) == 7
+
+
+def test_maxvio_summary_hand_example(O):
+    """Two layers, three microbatches of 8 tokens, E = 4, K = 2 (share 4)."""
+    load = np.array([[[4, 4, 4, 4], [8, 4, 2, 2], [6, 6, 2, 2]],
+                     [[5, 5, 3, 3], [4, 4, 4, 4], [4, 4, 4, 4]]], np.int32)
+    v, summ, worst = O.maxvio(load, 2, 8)
+    np.testing.assert_array_equal(v, np.array([[0.0, 1.0, 0.5], [0.25, 0.0, 0.0]], np.float32))
+    np.testing.assert_array_equal(summ, np.array([[1.0, 0.5], [0.25, np.float32(0.25 / 3)]], np.float32))
+    np.testing.assert_array_equal(worst, np.array([1.0, 0.5], np.float32))
+
+
+@pytest.mark.parametrize("N,E,K,n_mb,quant", [(2048, 16, 2, 256, None), (4096, 64, 4, 512, 8.0),
+                                             (1024, 32, 7, 128, None)])
+def test_microbatch_loads_vs_numpy_and_partition(O, N, E, K, n_mb, quant):
+    s, b, _ = synth.random_case(11, N, E, K, quant=quant)
+    mb = O.microbatch_loads(s, b, K, n_mb)
+    v = s + b
+    for c in range(N // n_mb):
+        top = np.argsort(-v[c * n_mb:(c + 1) * n_mb], axis=1, kind="stable")[:, :K]
+        np.testing.assert_array_equal(mb[c], np.bincount(top.ravel(), minlength=E))
+    assert (mb.sum(axis=1) == n_mb * K).all()
+    _, full = O.alpha(s, b, K)
+    np.testing.assert_array_equal(mb.sum(axis=0), full)
