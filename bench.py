@@ -337,7 +337,57 @@ def suite(torch, qb, synth, dev, args):
     torch.cuda.empty_cache()
     res["router"] = router_suite(torch, qb, synth, dev, args)
     res["controller"] = controller_suite(torch, qb, synth, dev, args)
+    res["sharding"] = sharding_suite(torch, qb, synth, dev, args)
     return res
+
+
+def sharding_suite(torch, qb, synth, dev, args, R=8):
+    """EQB over R emulated ranks vs rank-averaged QB on the skewed 1M-token
+    layer (R = 8 ranks of 131,072 tokens): stream times of both updates, the
+    largest difference between their biases, and the global MaxVio of the
+    same batch routed with each bias (and with the incoming bias)."""
+    from exact_quantile_selection_amd.shard import ShardedUpdate
+
+    s_np, b_np, K = synth.skew()
+    N, E = s_np.shape
+    s = torch.from_numpy(s_np).to(dev)
+    b0 = torch.from_numpy(b_np).to(dev)
+    sh = ShardedUpdate(R, N, E, K, device=dev)
+
+    def timed(f, n=5):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    t_eqb = timed(lambda: sh.eqb(s, b0))
+    b_eqb = sh.b[0].clone()
+    t_avg = timed(lambda: sh.rank_averaged(s, b0))
+    b_avg = sh.b_avg.clone()
+    alpha = torch.empty(N, dtype=torch.float32, device=dev)
+    load = torch.zeros((1, 1, E), dtype=torch.int32, device=dev)
+    mv = torch.empty((1, 1), dtype=torch.float32, device=dev)
+
+    def maxvio(bias):
+        load.zero_()
+        qb.qb_margins_topk(s, bias, K, alpha, load=load.view(E))
+        qb.qb_maxvio(load, K, N, mv)
+        return round(float(mv.item()), 4)
+
+    out = dict(N=N, E=E, K=K, ranks=R, tokens_per_rank=N // R,
+               eqb_sharded_us=round(t_eqb, 2), rank_averaged_us=round(t_avg, 2),
+               max_abs_bias_difference=float((b_avg - b_eqb).abs().max().item()),
+               global_maxvio={"incoming_bias": maxvio(b0), "eqb": maxvio(b_eqb),
+                              "rank_averaged": maxvio(b_avg)},
+               note="timings include the per-rank bias copies and histogram resets of the emulation")
+    del s, sh
+    torch.cuda.empty_cache()
+    return out
 
 
 def controller_suite(torch, qb, synth, dev, args, T=8):

@@ -34,7 +34,7 @@ EXPERTS = (16, 32, 64, 128, 256)
 def _units():
     units = [(f"qb_pass1_e{e}.o", "qb_pass1.hip", [f"-DQB_P1_E={e}"]) for e in EXPERTS]
     for src in ("qb_radix.hip", "qb_select.hip", "qb_k3_lei.hip", "qb_router.hip", "qb_metrics.hip",
-                "qb_api.hip"):
+                "qb_shard.hip", "qb_api.hip"):
         units.append((src.replace(".hip", ".o"), src, []))
     return units
 

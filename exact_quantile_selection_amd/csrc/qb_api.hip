@@ -172,6 +172,26 @@ QB_API int qb_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_
   return hip_status(qbk::launch_maxvio(load, L, C, E, K, n_tok, maxvio, summary, worst, stream), fn);
 }
 
+QB_API int qb_allreduce_sum_i32(int32_t* buf, int R, int64_t M, qb_stream_t stream) {
+  const char* fn = "qb_allreduce_sum_i32";
+  if (R < 1 || M < 0) return fail(QB_EINVAL, "%s: R=%d, M=%lld; expected R >= 1, M >= 0", fn, R, (long long)M);
+  if (M == 0) return QB_OK;
+  if (!buf) return fail(QB_EINVAL, "%s: buf is NULL (expected int32 [R=%d][M=%lld])", fn, R, (long long)M);
+  if (!aligned4(buf)) return fail(QB_EINVAL, "%s: buf must be 4-byte aligned", fn);
+  return hip_status(qbk::launch_allreduce_sum(buf, R, M, stream), fn);
+}
+
+QB_API int qb_rank_average(const float* q, int R, int E, float* b, float* bounds, qb_stream_t stream) {
+  const char* fn = "qb_rank_average";
+  if (R < 1 || E < 1 || E > 16384)
+    return fail(QB_EINVAL, "%s: R=%d, E=%d; expected R >= 1, 1 <= E <= 16384", fn, R, E);
+  if (!q || !b)
+    return fail(QB_EINVAL, "%s: q (float [R=%d][E=%d]) and b (float [E]) are required", fn, R, E);
+  if (!aligned4(q) || !aligned4(b) || (bounds && !aligned4(bounds)))
+    return fail(QB_EINVAL, "%s: q, b and bounds must be 4-byte aligned", fn);
+  return hip_status(qbk::launch_rank_average(q, R, E, b, bounds, stream), fn);
+}
+
 QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N, int E,
                             int32_t* hist_hi, qb_stream_t stream) {
   const char* fn = "qb_radix_hist_hi";

@@ -58,6 +58,8 @@ def lib() -> C.CDLL:
             "qb_router_fused": [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "qb_microbatch_loads": [vp, vp, i32, i64, i32, i32, i64, vp, vp, vp],
             "qb_maxvio": [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp],
+            "qb_allreduce_sum_i32": [vp, i32, i64, vp],
+            "qb_rank_average": [vp, i32, i32, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -220,6 +222,20 @@ def qb_maxvio(load, K, n_tok, maxvio, summary=None, worst=None, stream=None):
         _ptr(load, torch.int32, "load"), L, Cm, E, K, n_tok, _ptr(maxvio, torch.float32, "maxvio", (L, Cm)),
         _ptr(summary, torch.float32, "summary", (L, 2), opt=True),
         _ptr(worst, torch.float32, "worst", (2,), opt=True), _stream(stream)))
+
+
+def qb_allreduce_sum_i32(buf, stream=None):
+    """buf int32 [R, ...]: every rank's copy (leading index) becomes the sum
+    of all copies, in place."""
+    R = buf.shape[0]
+    _check(lib().qb_allreduce_sum_i32(_ptr(buf, torch.int32, "buf"), R, buf.numel() // R, _stream(stream)))
+
+
+def qb_rank_average(q, b, bounds=None, stream=None):
+    """q float [R, E] rank-local quantiles -> b [E] (and bounds [2])."""
+    R, E = q.shape
+    _check(lib().qb_rank_average(_ptr(q, torch.float32, "q"), R, E, _ptr(b, torch.float32, "b", (E,)),
+                                 _ptr(bounds, torch.float32, "bounds", (2,), opt=True), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -221,6 +221,29 @@ QB_API int qb_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_
                      float* summary, float* worst, qb_stream_t stream);
 
 /*
+ * One-GPU emulation of data-parallel ranks ("Exact Quantile Balancing and
+ * Load-Error Injection for Mixture-of-Experts", summary page, background
+ * paragraph: rank-local quantiles averaged across ranks depend on the
+ * sharding, a histogram summed over ranks does not; EQB paragraph: two
+ * all-reduces of byte histograms per update).  R emulated ranks keep their
+ * copies of a per-rank buffer back to back, rank r's M elements at r * M.
+ *
+ * qb_allreduce_sum_i32: every rank's copy becomes the elementwise sum of all
+ * R copies (an all-reduce of int32 counts).  buf int32 [R][M], in place.
+ */
+QB_API int qb_allreduce_sum_i32(int32_t* buf, int R, int64_t M, qb_stream_t stream);
+
+/*
+ * qb_rank_average: the rank-averaged update of the MARIN implementation the
+ * same paragraph describes.  From rank-local quantiles q float [R][E]:
+ *   qbar_j = fl32(sum_r (double)q[r][j] / R)            (rank order)
+ *   b[j]   = fl32((double)qbar_j - mean_j (double)qbar_j) (float64 sum in expert order / E)
+ *   bounds = {fl32(min b - 1), fl32(max b + 1)}          (nullable)
+ * b float [E]; bounds float [2].  1 <= E <= 16384.
+ */
+QB_API int qb_rank_average(const float* q, int R, int E, float* b, float* bounds, qb_stream_t stream);
+
+/*
  * LEI ("Exact Quantile Balancing and Load-Error Injection for
  * Mixture-of-Experts", summary page, LEI paragraph): with M = N*K/E,
  * rho_e = fl32((load_e - M) / M) in float64, add_e = fl32(eta * rho_e),

@@ -71,6 +71,8 @@ def lib():
         L.oq_bounds_of.argtypes = [f32p, C.c_int, f32p]
         L.oq_lei.restype = None
         L.oq_lei.argtypes = [f32p, i32p, C.c_int64, C.c_int, C.c_int, C.c_float]
+        L.oq_rank_average.restype = None
+        L.oq_rank_average.argtypes = [f32p, C.c_int, C.c_int, f32p, f32p]
         L.oq_maxvio.restype = None
         L.oq_maxvio.argtypes = [i32p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, f32p,
                                 C.c_void_p, C.c_void_p]
@@ -202,3 +204,24 @@ def maxvio(load, K: int, n_tok: int):
     worst = np.zeros(2, np.float32)
     lib().oq_maxvio(load, L, C, E, K, n_tok, v, summary.ctypes.data, worst.ctypes.data)
     return v, summary, worst
+
+
+def rank_average(q) -> tuple:
+    """q [R, E] rank-local quantiles -> (b [E], bounds [2]) of the
+    rank-averaged update."""
+    q = _f32(q)
+    R, E = q.shape
+    b = np.zeros(E, np.float32)
+    bounds = np.zeros(2, np.float32)
+    lib().oq_rank_average(q, R, E, b, bounds)
+    return b, bounds
+
+
+def rank_local_quantiles(s, b, K: int, R: int) -> np.ndarray:
+    """The EQB quantile of each of R consecutive token shards, [R, E]: what
+    each data-parallel rank would find from its own tokens alone."""
+    s = _f32(s)
+    N, E = s.shape
+    assert N % R == 0
+    n = N // R
+    return np.stack([eqb_layer(s[r * n:(r + 1) * n], b, K)["q"] for r in range(R)])

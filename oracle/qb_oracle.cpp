@@ -285,6 +285,24 @@ void oq_router_logits(const uint16_t* hidden, const uint16_t* w, int H, int E,
   }
 }
 
+// Rank-averaged update ([EQB] background paragraph: the MARIN
+// implementation averages rank-local quantiles across data-parallel ranks):
+// qbar_j = fl32(sum_r (double)q[r][j] / R) in rank order, then the same
+// centring and bounds as the EQB update.
+void oq_rank_average(const float* q, int R, int E, float* b, float* bounds) {
+  std::vector<float> qbar(E);
+  for (int j = 0; j < E; ++j) {
+    double sum = 0.0;
+    for (int r = 0; r < R; ++r) sum += double(q[int64_t(r) * E + j]);
+    qbar[j] = float(sum / double(R));
+  }
+  double sum = 0.0;
+  for (int j = 0; j < E; ++j) sum += double(qbar[j]);
+  const double mean = sum / double(E);
+  for (int j = 0; j < E; ++j) b[j] = float(double(qbar[j]) - mean);
+  oq_bounds_of(b, E, bounds);
+}
+
 // MaxVio ([EQB] testbed paragraph: how far the busiest expert exceeds the
 // uniform load; background paragraph: global vs per-microbatch balance).
 // Rows are (layer, microbatch) pairs of E loads over n_tok tokens each:

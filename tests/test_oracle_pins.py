@@ -459,3 +459,40 @@ def test_microbatch_loads_vs_numpy_and_partition(O, N, E, K, n_mb, quant):
     assert (mb.sum(axis=1) == n_mb * K).all()
     _, full = O.alpha(s, b, K)
     np.testing.assert_array_equal(mb.sum(axis=0), full)
+
+
+# --- rank-averaged update ("Exact Quantile Balancing and Load-Error
+# Injection for Mixture-of-Experts", summary page, background paragraph:
+# MARIN averages rank-local quantiles).
+
+def test_rank_average_hand_example(O):
+    """Dyadic quantiles, R = 2, E = 4: averages 0.5, 0.25, -0.25, 1.5 have
+    mean 0.5, so b = (0, -0.25, -0.75, 1.0); bounds (-1.75, 2.0)."""
+    q = np.array([[0.75, 0.5, -0.5, 1.0], [0.25, 0.0, 0.0, 2.0]], np.float32)
+    b, bounds = O.rank_average(q)
+    np.testing.assert_array_equal(b, np.array([0.0, -0.25, -0.75, 1.0], np.float32))
+    np.testing.assert_array_equal(bounds, np.array([-1.75, 2.0], np.float32))
+
+
+def test_rank_average_closed_forms(O):
+    rng = np.random.default_rng(3)
+    q1 = (np.round(rng.normal(0, 1, 64) * 64) / 64).astype(np.float32)    # dyadic
+    b1, bo1 = O.rank_average(q1[None, :])
+    # equal rows on every rank: the average is that row
+    b8, bo8 = O.rank_average(np.repeat(q1[None, :], 8, axis=0))
+    np.testing.assert_array_equal(b8, b1)
+    np.testing.assert_array_equal(bo8, bo1)
+    # a constant per rank shifts every expert alike and is centred away
+    shifted = np.stack([q1 + np.float32(c) for c in (0.5, -0.25, 1.0, 0.75)])
+    bs, _ = O.rank_average(shifted)
+    np.testing.assert_array_equal(bs, b1)
+    assert abs(float(np.sum(b1.astype(np.float64)))) < 1e-6
+
+
+def test_rank_local_quantiles_one_rank_is_eqb(O):
+    s, b, K = synth.random_case(4, 2048, 64, 4, quant=16.0)
+    np.testing.assert_array_equal(O.rank_local_quantiles(s, b, K, 1)[0], O.eqb_layer(s, b, K)["q"])
+    bav, bounds = O.rank_average(O.rank_local_quantiles(s, b, K, 1))
+    ref = O.eqb_layer(s, b, K)
+    np.testing.assert_array_equal(bav, ref["b_next"])
+    np.testing.assert_array_equal(bounds, ref["bounds"])
