@@ -338,7 +338,46 @@ def suite(torch, qb, synth, dev, args):
     res["router"] = router_suite(torch, qb, synth, dev, args)
     res["controller"] = controller_suite(torch, qb, synth, dev, args)
     res["sharding"] = sharding_suite(torch, qb, synth, dev, args)
+    res["one_pass_full_hist"] = full_hist_suite(torch, qb, synth, dev, args)
     return res
+
+
+def full_hist_suite(torch, qb, synth, dev, args):
+    """The one-pass alternative on the skewed 1M-token layer: clear the
+    65,536-bin histogram, alpha + full-key histogram in one pass over s, the
+    quantile read from the 65,536 bins and the bias update; compared with
+    the two-pass EQB step on the same layer (same result bit for bit)."""
+    s_np, b_np, K = synth.skew()
+    N, E = s_np.shape
+    s = torch.from_numpy(s_np).to(dev)
+    b0 = torch.from_numpy(b_np).to(dev)
+    b = b0.clone()
+    alpha = torch.empty(N, dtype=torch.float32, device=dev)
+    hist = torch.zeros((E, 65536), dtype=torch.int32, device=dev)
+    key = torch.zeros(E, dtype=torch.uint16, device=dev)
+    q = torch.zeros(E, dtype=torch.float32, device=dev)
+    bounds = torch.zeros(2, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    class OnePass:
+        def run(self_):
+            b.copy_(b0)
+            qb.qb_fill_i32(hist, 0)
+            qb.qb_margins_full_hist(s, b, K, alpha, hist)
+            qb.qb_select_update(qb.QB_SELECT_FULL, K, hist, key_out=key, q_out=q, b=b, bounds=bounds, err=err)
+
+    sec, _ = time_graph(OnePass(), torch, max(5, args.steps // 2), 2)
+    assert int(err.item()) == 0
+    two = EqbStep(s, b0, K, qb, torch)
+    sec2, _ = time_graph(two, torch, max(5, args.steps // 2), 2)
+    same = bool(torch.equal(b, two.b))
+    out = dict(N=N, E=E, K=K, one_pass_us=round(sec * 1e6, 2), two_pass_us=round(sec2 * 1e6, 2),
+               one_pass_hist_MiB=E * 65536 * 4 / 2**20, two_pass_hist_MiB=2 * E * 256 * 4 / 2**20,
+               same_b_next=same,
+               note="one pass reads s once but makes one device atomic per score into a 64 MiB histogram")
+    del s, hist
+    torch.cuda.empty_cache()
+    return out
 
 
 def sharding_suite(torch, qb, synth, dev, args, R=8):
@@ -369,6 +408,14 @@ def sharding_suite(torch, qb, synth, dev, args, R=8):
     b_eqb = sh.b[0].clone()
     t_avg = timed(lambda: sh.rank_averaged(s, b0))
     b_avg = sh.b_avg.clone()
+    # heterogeneous ranks: the same tokens ordered by their preferred expert,
+    # so each rank sees a different mix (as ranks fed different data do)
+    s_het = s[torch.argsort(torch.argmax(s + b0, dim=1), stable=True)].contiguous()
+    sh.eqb(s_het, b0)
+    b_eqb_het = sh.b[0].clone()
+    sh.rank_averaged(s_het, b0)
+    b_avg_het = sh.b_avg.clone()
+    torch.cuda.synchronize()
     alpha = torch.empty(N, dtype=torch.float32, device=dev)
     load = torch.zeros((1, 1, E), dtype=torch.int32, device=dev)
     mv = torch.empty((1, 1), dtype=torch.float32, device=dev)
@@ -384,8 +431,12 @@ def sharding_suite(torch, qb, synth, dev, args, R=8):
                max_abs_bias_difference=float((b_avg - b_eqb).abs().max().item()),
                global_maxvio={"incoming_bias": maxvio(b0), "eqb": maxvio(b_eqb),
                               "rank_averaged": maxvio(b_avg)},
+               heterogeneous_ranks={
+                   "eqb_bias_unchanged": bool(torch.equal(b_eqb_het, b_eqb)),
+                   "max_abs_bias_difference": float((b_avg_het - b_eqb).abs().max().item()),
+                   "global_maxvio": {"eqb": maxvio(b_eqb_het), "rank_averaged": maxvio(b_avg_het)}},
                note="timings include the per-rank bias copies and histogram resets of the emulation")
-    del s, sh
+    del s, s_het, sh
     torch.cuda.empty_cache()
     return out
 

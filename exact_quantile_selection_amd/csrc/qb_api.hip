@@ -23,6 +23,12 @@ int launch_margins_topk_e64(const float*, const float*, int, int, int64_t, int, 
 int launch_margins_topk_e128(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
 int launch_margins_topk_e256(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
 
+int launch_margins_full_e16(const float*, const float*, int, int64_t, int, float*, int32_t*, hipStream_t);
+int launch_margins_full_e32(const float*, const float*, int, int64_t, int, float*, int32_t*, hipStream_t);
+int launch_margins_full_e64(const float*, const float*, int, int64_t, int, float*, int32_t*, hipStream_t);
+int launch_margins_full_e128(const float*, const float*, int, int64_t, int, float*, int32_t*, hipStream_t);
+int launch_margins_full_e256(const float*, const float*, int, int64_t, int, float*, int32_t*, hipStream_t);
+
 int launch_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
                         float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv) {
   switch (E) {
@@ -192,6 +198,28 @@ QB_API int qb_rank_average(const float* q, int R, int E, float* b, float* bounds
   return hip_status(qbk::launch_rank_average(q, R, E, b, bounds, stream), fn);
 }
 
+QB_API int qb_margins_full_hist(const float* s, const float* b, int L, int64_t N, int E, int K,
+                                float* alpha, int32_t* hist_full, qb_stream_t stream) {
+  const char* fn = "qb_margins_full_hist";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!b || !alpha || !hist_full)
+    return fail(QB_EINVAL, "%s: b (float [L=%d][E=%d]), alpha (float [L][N]) and hist_full (int32 [L][E][65536]) are required",
+                fn, L, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (!aligned4(b) || !aligned4(alpha) || !aligned16(hist_full))
+    return fail(QB_EINVAL, "%s: b and alpha must be 4-byte and hist_full 16-byte aligned", fn);
+  int rc;
+  switch (E) {
+    case 16: rc = qbk::launch_margins_full_e16(s, b, L, N, K, alpha, hist_full, stream); break;
+    case 32: rc = qbk::launch_margins_full_e32(s, b, L, N, K, alpha, hist_full, stream); break;
+    case 64: rc = qbk::launch_margins_full_e64(s, b, L, N, K, alpha, hist_full, stream); break;
+    case 128: rc = qbk::launch_margins_full_e128(s, b, L, N, K, alpha, hist_full, stream); break;
+    default: rc = qbk::launch_margins_full_e256(s, b, L, N, K, alpha, hist_full, stream); break;
+  }
+  return hip_status(rc, fn);
+}
+
 QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N, int E,
                             int32_t* hist_hi, qb_stream_t stream) {
   const char* fn = "qb_radix_hist_hi";
@@ -257,8 +285,16 @@ QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist,
       if (n_bins < 1 || n_bins > 2048)
         return fail(QB_EINVAL, "%s(UNIFORM): n_bins=%d, expected 1 <= n_bins <= 2048", fn, n_bins);
       break;
+    case QB_SELECT_FULL:
+      if (!q_out || !b || !bounds)
+        return fail(QB_EINVAL, "%s(FULL): q_out, b (float [L=%d][E=%d]) and bounds (float [L][2]) are required",
+                    fn, L, E);
+      if (!aligned16(hist)) return fail(QB_EINVAL, "%s(FULL): hist must be 16-byte aligned", fn);
+      n_bins = 65536;
+      break;
     default:
-      return fail(QB_EINVAL, "%s: phase=%d, expected QB_SELECT_HI, QB_SELECT_LO or QB_SELECT_UNIFORM", fn,
+      return fail(QB_EINVAL,
+                  "%s: phase=%d, expected QB_SELECT_HI, QB_SELECT_LO, QB_SELECT_UNIFORM or QB_SELECT_FULL", fn,
                   phase);
   }
   return hip_status(qbk::launch_select(phase, L, E, K, hist, n_bins, sel_hi, rank_lo, key_out, q_out, b,

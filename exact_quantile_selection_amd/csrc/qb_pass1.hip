@@ -21,6 +21,10 @@
 //   * histogram: keys of both halves of a packed bf16 pair are made in three
 //     integer ops; counters are 16-bit pairs in LDS (E*512 bytes), flushed to
 //     the global int32 histogram once per workgroup (<= 65535 rows each).
+//   * full-key mode (HM = 2): instead, every 16-bit key is counted into a
+//     global [E][65536] int32 histogram with one device atomic per element
+//     -- the one-pass alternative the EQB paragraph compares the two byte
+//     histograms against (128x their memory); kept for that comparison.
 //   * work split: a workgroup trip is 16 waves x (64/LPR) rows; trips are
 //     block-cyclic over the workgroups, so the workgroups in flight read
 //     neighbouring rows (all HBM channels busy).  A full trip addresses its
@@ -157,10 +161,11 @@ __device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N,
 }
 
 // alpha, loads and the high-byte histogram of one trip's rows.
-template <int E, int P, bool HIST, bool LOAD>
+template <int E, int P, int HM, bool LOAD>
 __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64_t base, int64_t N,
                                         int rho, int ql, int lane, int K, const float* lds_b,
-                                        uint32_t* lds_hist, int32_t* lds_load, float* alpha) {
+                                        uint32_t* lds_hist, int32_t* lds_load, float* alpha,
+                                        int32_t* ghist) {
   using S = P1Shape<E>;
   const int64_t row = base + rho;
   const bool valid = row < N;
@@ -189,7 +194,23 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
   }
   if (valid && ql == 0) alpha[row] = a;
   if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load);
-  if constexpr (HIST) {
+  if constexpr (HM == 2) {
+    // full 16-bit key histogram, [E][65536] int32 in global memory
+    if (valid) {
+#pragma unroll
+      for (int t = 0; t < S::F4; ++t) {
+        const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+        const uint32_t k01 = key2(bf16x2_rne(a - x[t].x, a - x[t].y));
+        const uint32_t k23 = key2(bf16x2_rne(a - x[t].z, a - x[t].w));
+        int32_t* h = ghist + int64_t(4 * quad) * 65536;
+        atomicAdd(h + (k01 & 0xFFFFu), 1);
+        atomicAdd(h + 65536 + (k01 >> 16), 1);
+        atomicAdd(h + 2 * 65536 + (k23 & 0xFFFFu), 1);
+        atomicAdd(h + 3 * 65536 + (k23 >> 16), 1);
+      }
+    }
+  }
+  if constexpr (HM == 1) {
     if (valid) {
 #pragma unroll
       for (int t = 0; t < S::F4; ++t) {
@@ -202,14 +223,14 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
   }
 }
 
-template <int E, int P, bool HIST, bool LOAD>
+template <int E, int P, int HM, bool LOAD>
 __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
     const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int bdiv, int K,
     float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi) {
   using S = P1Shape<E>;
   constexpr int kWaves = p1_waves<LOAD>();
   constexpr int kThreads = kWaves * kWave;
-  __shared__ uint32_t lds_hist[HIST ? S::HDW : 4];
+  __shared__ uint32_t lds_hist[HM == 1 ? S::HDW : 4];
   __shared__ float lds_b[E];
   __shared__ int32_t lds_load[E];
 
@@ -219,8 +240,9 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
   s += int64_t(layer) * N * E;
   b += int64_t(layer / bdiv) * E;  // bdiv consecutive layers share a bias row
   alpha += int64_t(layer) * N;
+  int32_t* ghist = HM == 2 ? hist_hi + int64_t(layer) * E * 65536 : nullptr;
 
-  if constexpr (HIST) hist16_zero<E>(lds_hist, tid, kThreads);
+  if constexpr (HM == 1) hist16_zero<E>(lds_hist, tid, kThreads);
   for (int j = tid; j < E; j += kThreads) {
     lds_b[j] = b[j];
     lds_load[j] = 0;
@@ -239,22 +261,22 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
   for (; base < N; base += stride) {
     float4 x[S::F4];
     p1_load<E>(s, base, N, rho, ql, x);
-    p1_rows<E, P, HIST, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha);
+    p1_rows<E, P, HM, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist);
   }
   __syncthreads();
-  if constexpr (HIST) hist16_flush<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
+  if constexpr (HM == 1) hist16_flush<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
   if constexpr (LOAD) {
     for (int j = tid; j < E; j += kThreads)
       if (lds_load[j]) atomicAdd(load + int64_t(layer) * E + j, lds_load[j]);
   }
 }
 
-template <int E, int P, bool HIST, bool LOAD>
+template <int E, int P, int HM, bool LOAD>
 static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st) {
   constexpr int kThreads = p1_waves<LOAD>() * kWave;
   const RowSplit sp = split_rows(L, N, p1_waves<LOAD>() * P1Shape<E>::RPW, 65535);
-  hipLaunchKernelGGL((k_margins_topk<E, P, HIST, LOAD>), dim3(unsigned(sp.blocks)), dim3(kThreads),
+  hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD>), dim3(unsigned(sp.blocks)), dim3(kThreads),
                      0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi);
   return int(hipGetLastError());
 }
@@ -262,10 +284,10 @@ static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t 
 template <int E, int P>
 static int launch_p1(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                      int32_t* load, int32_t* hist_hi, hipStream_t st) {
-  if (hist_hi && load) return launch_p1_v<E, P, true, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-  if (hist_hi) return launch_p1_v<E, P, true, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-  if (load) return launch_p1_v<E, P, false, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-  return launch_p1_v<E, P, false, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  if (hist_hi && load) return launch_p1_v<E, P, 1, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  if (hist_hi) return launch_p1_v<E, P, 1, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  if (load) return launch_p1_v<E, P, 0, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  return launch_p1_v<E, P, 0, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
 }
 
 template <int E>
@@ -283,6 +305,21 @@ static int launch_p1_k(const float* s, const float* b, int L, int bdiv, int64_t 
   return int(hipErrorInvalidValue);
 }
 
+template <int E>
+static int launch_full_k(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
+                         int32_t* hist_full, hipStream_t st) {
+  switch (K + 1) {
+    case 2: return launch_p1_v<E, 2, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+    case 3: return launch_p1_v<E, 3, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+    case 4: return launch_p1_v<E, 4, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+    case 5: return launch_p1_v<E, 5, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+    case 6: return launch_p1_v<E, 6, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+    case 7: return launch_p1_v<E, 7, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+    case 8: return launch_p1_v<E, 8, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+  }
+  return int(hipErrorInvalidValue);
+}
+
 #ifndef QB_P1_E
 #error "compile with -DQB_P1_E=<experts>: one translation unit per expert count"
 #endif
@@ -293,6 +330,11 @@ int QB_P1_CAT(launch_margins_topk_e, QB_P1_E)(const float* s, const float* b, in
                                                int64_t N, int K, float* alpha, int32_t* load,
                                                int32_t* hist_hi, hipStream_t st) {
   return launch_p1_k<QB_P1_E>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+}
+
+int QB_P1_CAT(launch_margins_full_e, QB_P1_E)(const float* s, const float* b, int L, int64_t N, int K,
+                                              float* alpha, int32_t* hist_full, hipStream_t st) {
+  return launch_full_k<QB_P1_E>(s, b, L, N, K, alpha, hist_full, st);
 }
 
 }  // namespace qbk

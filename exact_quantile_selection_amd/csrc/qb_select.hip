@@ -167,6 +167,64 @@ __global__ __launch_bounds__(kRowThreads) void k_select_rows(
   }
 }
 
+// Rank scan over a full 16-bit key histogram ([L][E][65536]): one
+// workgroup per (expert, layer); thread t owns bins [256 t, 256 t + 256).
+// The rank is ceil(K * T / E) with T the row's own total (every row of a
+// valid histogram holds one key per token); the bin holding it is the key.
+constexpr int kFullThreads = 256;
+__global__ __launch_bounds__(kFullThreads) void k_select_full(int E, int K, const int32_t* __restrict__ hist,
+                                                              uint16_t* __restrict__ key_out,
+                                                              float* __restrict__ q_out,
+                                                              int32_t* __restrict__ err) {
+  constexpr int PER = 65536 / kFullThreads;
+  __shared__ int64_t s_incl[kFullThreads];
+  __shared__ int s_owner;
+  const int j = blockIdx.x, layer = blockIdx.y, tid = threadIdx.x;
+  const int64_t le = int64_t(layer) * E;
+  const int32_t* row = hist + (le + j) * 65536 + int64_t(tid) * PER;
+  int64_t mine = 0;
+#pragma unroll 8
+  for (int k = 0; k < PER; k += 4) {
+    const int4 v = *reinterpret_cast<const int4*>(row + k);
+    mine += int64_t(v.x) + v.y + v.z + v.w;
+  }
+  s_incl[tid] = mine;
+  if (tid == 0) s_owner = -1;
+  __syncthreads();
+  // inclusive prefix over the 256 thread totals (Hillis-Steele in LDS)
+  for (int d = 1; d < kFullThreads; d <<= 1) {
+    const int64_t o = tid >= d ? s_incl[tid - d] : 0;
+    __syncthreads();
+    s_incl[tid] += o;
+    __syncthreads();
+  }
+  const int64_t total = s_incl[kFullThreads - 1];
+  const int64_t rank = (int64_t(K) * total + E - 1) / E;
+  const int64_t incl = s_incl[tid];
+  const int64_t excl = incl - mine;
+  if (rank >= 1 && excl < rank && incl >= rank) s_owner = tid;  // exactly one thread
+  __syncthreads();
+  if (tid != s_owner) {
+    if (tid == 0 && s_owner < 0) {
+      q_out[le + j] = __builtin_nanf("");
+      if (err) atomicOr(err, total == 0 ? QB_ERR_EMPTY : QB_ERR_RANK);
+    }
+    return;
+  }
+  int64_t run = excl;
+  int bin = -1;
+  for (int k = 0; k < PER; ++k) {
+    run += row[k];
+    if (run >= rank) {
+      bin = tid * PER + k;
+      break;
+    }
+  }
+  const uint32_t key = uint32_t(bin);
+  q_out[le + j] = __builtin_bit_cast(float, unkey16(key) << 16);
+  if (key_out) key_out[le + j] = uint16_t(key);
+}
+
 // b_next = q - mean(q) (float64 sum in expert order on one thread, one
 // rounding to fp32), written over b; bounds = [min - 1, max + 1] (min and
 // max as a parallel reduction: any order gives the same values up to the
@@ -242,6 +300,13 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(int E, const float* __
 int launch_select(int phase, int L, int E, int K, const int32_t* hist, int n_bins,
                   int32_t* sel_hi, int32_t* rank_lo, uint16_t* key_out, float* q_out, float* b,
                   float* bounds, int32_t* err, hipStream_t st) {
+  if (phase == QB_SELECT_FULL) {
+    hipLaunchKernelGGL(k_select_full, dim3(unsigned(E), unsigned(L)), dim3(kFullThreads), 0, st, E, K, hist,
+                       key_out, q_out, err);
+    if (int rc = int(hipGetLastError())) return rc;
+    hipLaunchKernelGGL(k_finalize, dim3(unsigned(L)), dim3(kFinThreads), 0, st, E, q_out, b, bounds, err);
+    return int(hipGetLastError());
+  }
   const int vec = ((n_bins % 4) == 0 && (reinterpret_cast<uintptr_t>(hist) & 15u) == 0) ? 1 : 0;
   const dim3 grid{unsigned((E + kRowWaves - 1) / kRowWaves), unsigned(L), 1u};
   const dim3 block{unsigned(kRowThreads), 1u, 1u};

@@ -20,7 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqb.so")
 
 QB_OK, QB_EINVAL, QB_EUNSUPPORTED, QB_EHIP = 0, -1, -2, -3
-QB_SELECT_HI, QB_SELECT_LO, QB_SELECT_UNIFORM = 0, 1, 2
+QB_SELECT_HI, QB_SELECT_LO, QB_SELECT_UNIFORM, QB_SELECT_FULL = 0, 1, 2, 3
 QB_ERR_ROW_TOTALS, QB_ERR_EMPTY, QB_ERR_RANK = 1, 2, 4
 
 SUPPORTED_E = (16, 32, 64, 128, 256)
@@ -59,6 +59,7 @@ def lib() -> C.CDLL:
             "qb_microbatch_loads": [vp, vp, i32, i64, i32, i32, i64, vp, vp, vp],
             "qb_maxvio": [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp],
             "qb_allreduce_sum_i32": [vp, i32, i64, vp],
+            "qb_margins_full_hist": [vp, vp, i32, i64, i32, i32, vp, vp, vp],
             "qb_rank_average": [vp, i32, i32, vp, vp, vp],
         }
         for name, args in sig.items():
@@ -222,6 +223,15 @@ def qb_maxvio(load, K, n_tok, maxvio, summary=None, worst=None, stream=None):
         _ptr(load, torch.int32, "load"), L, Cm, E, K, n_tok, _ptr(maxvio, torch.float32, "maxvio", (L, Cm)),
         _ptr(summary, torch.float32, "summary", (L, 2), opt=True),
         _ptr(worst, torch.float32, "worst", (2,), opt=True), _stream(stream)))
+
+
+def qb_margins_full_hist(s, b, K, alpha, hist_full, stream=None):
+    """alpha, and hist_full [E, 65536] (or [L, E, 65536]) += full 16-bit key histogram."""
+    L, N, E, lead = _lne(s)
+    _check(lib().qb_margins_full_hist(
+        _ptr(s, torch.float32, "s"), _ptr(b, torch.float32, "b", lead + (E,)), L, N, E, K,
+        _ptr(alpha, torch.float32, "alpha", lead + (N,)),
+        _ptr(hist_full, torch.int32, "hist_full", lead + (E, 65536)), _stream(stream)))
 
 
 def qb_allreduce_sum_i32(buf, stream=None):

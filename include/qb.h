@@ -72,7 +72,7 @@ enum {
   QB_EHIP = -3          /* the HIP runtime refused the launch */
 };
 
-enum { QB_SELECT_HI = 0, QB_SELECT_LO = 1, QB_SELECT_UNIFORM = 2 };
+enum { QB_SELECT_HI = 0, QB_SELECT_LO = 1, QB_SELECT_UNIFORM = 2, QB_SELECT_FULL = 3 };
 
 /* Device-side error bits OR-ed into qb_select_update's optional err word. */
 enum {
@@ -122,6 +122,21 @@ QB_API int qb_margin_keys(const float* s, const float* alpha, int L, int64_t N, 
                           uint16_t* keys, qb_stream_t stream);
 
 /*
+ * One-pass alternative to the two byte histograms, for comparison ("Exact
+ * Quantile Balancing and Load-Error Injection for Mixture-of-Experts",
+ * summary page, EQB paragraph: a full 65,536-bin histogram per expert would
+ * take 128x the memory of the two 256-bin ones).  Computes alpha as
+ * qb_margins_topk does and, in the same pass over s, hist_full[l][j][key] +=
+ * 1 for every element's 16-bit margin key (one device atomic per element);
+ * QB_SELECT_FULL then reads the quantile straight from it.
+ *   s float [L][N][E]; b float [L][E]; alpha float [L][N];
+ *   hist_full int32 [L][E][65536] (16-byte aligned; 64 MiB per layer at
+ *   E = 256), accumulated (+=).
+ */
+QB_API int qb_margins_full_hist(const float* s, const float* b, int L, int64_t N, int E, int K,
+                                float* alpha, int32_t* hist_full, qb_stream_t stream);
+
+/*
  * Rank scans and the bias update, one workgroup per layer.  The token count
  * is read from expert 0's histogram row (every token adds exactly one margin
  * per expert: review thread of Megatron-LM PR #6637); m = ceil(K * total / E).
@@ -137,7 +152,12 @@ QB_API int qb_margin_keys(const float* s, const float* alpha, int L, int64_t N, 
  *                  (read, then overwritten with the next range); q = lo + w *
  *                  (c + (m - below) / count[c]) in float64 (w = (hi-lo)/n_bins,
  *                  c = first bin reaching m), then centring as above.
- *   q_out: required for LO and UNIFORM (receives q; NaN marks an expert
+ *   QB_SELECT_FULL: hist = a full 16-bit key histogram [L][E][65536]
+ *                  (qb_margins_full_hist; n_bins is ignored; 16-byte
+ *                  aligned); key = first bin whose running count reaches
+ *                  m = ceil(K * T / E), T = the row's own total; q, b and
+ *                  bounds as in LO.
+ *   q_out: required for LO, UNIFORM and FULL (receives q; NaN marks an expert
  *   whose rank search failed).  key_out, err: nullable.  err receives
  *   QB_ERR_* bits (atomic OR); a layer with a failed expert keeps its b and
  *   bounds unchanged.  HI is one launch (one wave per expert row); LO and

@@ -225,3 +225,12 @@ def rank_local_quantiles(s, b, K: int, R: int) -> np.ndarray:
     assert N % R == 0
     n = N // R
     return np.stack([eqb_layer(s[r * n:(r + 1) * n], b, K)["q"] for r in range(R)])
+
+
+def full_hist(s, b, K: int) -> np.ndarray:
+    """Full 16-bit key histogram [E, 65536] of the bf16 margin keys (the
+    one-pass alternative of the EQB paragraph): counts of the oracle's keys."""
+    s = _f32(s)
+    N, E = s.shape
+    keys = margin_keys(s, alpha(s, b, K, with_load=False))
+    return np.stack([np.bincount(keys[j], minlength=65536).astype(np.int32) for j in range(E)])

@@ -496,3 +496,22 @@ def test_rank_local_quantiles_one_rank_is_eqb(O):
     ref = O.eqb_layer(s, b, K)
     np.testing.assert_array_equal(bav, ref["b_next"])
     np.testing.assert_array_equal(bounds, ref["bounds"])
+
+
+# --- one-pass full 16-bit histogram ("Exact Quantile Balancing and
+# Load-Error Injection for Mixture-of-Experts", summary page, EQB paragraph:
+# the two 256-bin histograms instead of one 65,536-bin histogram).
+
+@pytest.mark.parametrize("N,E,K,quant", [(1000, 16, 2, None), (3000, 64, 5, 16.0)])
+def test_full_histogram_agrees_with_the_byte_histograms(O, N, E, K, quant):
+    s, b, _ = synth.random_case(8, N, E, K, quant=quant)
+    full = O.full_hist(s, b, K)
+    ref = O.eqb_layer(s, b, K)
+    assert (full.sum(axis=1) == N).all()
+    np.testing.assert_array_equal(full.reshape(E, 256, 256).sum(axis=2), ref["hist_hi"])
+    m = (K * N + E - 1) // E
+    for j in range(E):
+        hi = ref["sel_hi"][j]
+        np.testing.assert_array_equal(full[j, hi * 256:(hi + 1) * 256], ref["hist_lo"][j])
+        key = int(np.argmax(np.cumsum(full[j]) >= m))   # first bin reaching rank m
+        assert key == int(ref["key"][j])
