@@ -339,7 +339,39 @@ def suite(torch, qb, synth, dev, args):
     res["controller"] = controller_suite(torch, qb, synth, dev, args)
     res["sharding"] = sharding_suite(torch, qb, synth, dev, args)
     res["one_pass_full_hist"] = full_hist_suite(torch, qb, synth, dev, args)
+    res["lei_backward"] = lei_backward_suite(torch, qb, synth, dev, args)
     return res
+
+
+def lei_backward_suite(torch, qb, synth, dev, args):
+    """Per-microbatch LEI (unbounded and bounded) with the gradient through
+    the sigmoid at the router shape: 262,144 x 256 scores, 4096-token
+    microbatches; reads g and s, writes g' and dlogits (16 B per score)."""
+    N, E, K, n_mb = 262144, 256, 6, 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    grad = torch.randn((N, E), generator=g, device=dev)
+    s = torch.sigmoid(torch.randn((N, E), generator=g, device=dev))
+    load = torch.randint(0, 2 * n_mb * K // E, (N // n_mb, E), generator=g, device=dev, dtype=torch.int32)
+    gout = torch.empty_like(grad)
+    d = torch.empty_like(grad)
+    out = dict(N=N, E=E, K=K, n_mb=n_mb, bytes_per_launch=16 * N * E)
+    for bounded in (False, True):
+        f = lambda: qb.qb_lei_backward(grad, load, K, n_mb, 1e-5, bounded=bounded, s=s, g_out=gout, dlogits=d)
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        out["bounded_us" if bounded else "unbounded_us"] = round(us, 2)
+        out["bounded_GBps" if bounded else "unbounded_GBps"] = round(16 * N * E / us / 1e3, 1)
+    del grad, s, gout, d
+    torch.cuda.empty_cache()
+    return out
 
 
 def full_hist_suite(torch, qb, synth, dev, args):

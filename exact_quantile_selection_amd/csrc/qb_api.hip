@@ -220,6 +220,30 @@ QB_API int qb_margins_full_hist(const float* s, const float* b, int L, int64_t N
   return hip_status(rc, fn);
 }
 
+QB_API int qb_lei_backward(const float* g, const float* s, const int32_t* load_mb, int64_t N, int E, int K,
+                           int64_t n_mb, float eta, int bounded, float* g_out, float* dlogits,
+                           qb_stream_t stream) {
+  const char* fn = "qb_lei_backward";
+  if (N < 1) return fail(QB_EINVAL, "%s: N=%lld, expected N >= 1", fn, (long long)N);
+  if (!qbk::supported_E(E))
+    return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {16, 32, 64, 128, 256}", fn, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (n_mb < 1 || N % n_mb != 0)
+    return fail(QB_EINVAL, "%s: n_mb=%lld must be >= 1 and divide N=%lld", fn, (long long)n_mb, (long long)N);
+  if (N / n_mb > 65535)
+    return fail(QB_EINVAL, "%s: N / n_mb = %lld microbatches, at most 65535", fn, (long long)(N / n_mb));
+  if (bounded != 0 && bounded != 1) return fail(QB_EINVAL, "%s: bounded=%d, expected 0 or 1", fn, bounded);
+  if (!g || !load_mb)
+    return fail(QB_EINVAL, "%s: g (float [N=%lld][E=%d]) and load_mb (int32 [N/n_mb][E]) are required", fn,
+                (long long)N, E);
+  if (!g_out && !dlogits) return fail(QB_EINVAL, "%s: nothing to write (g_out and dlogits are NULL)", fn);
+  if (dlogits && !s) return fail(QB_EINVAL, "%s: dlogits needs the scores s (float [N][E])", fn);
+  if (!aligned16(g) || (s && !aligned16(s)) || (g_out && !aligned16(g_out)) || (dlogits && !aligned16(dlogits)))
+    return fail(QB_EINVAL, "%s: g, s, g_out and dlogits must be 16-byte aligned", fn);
+  if (!aligned4(load_mb)) return fail(QB_EINVAL, "%s: load_mb must be 4-byte aligned", fn);
+  return hip_status(qbk::launch_lei_bwd(g, s, load_mb, N, E, K, n_mb, eta, bounded, g_out, dlogits, stream), fn);
+}
+
 QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N, int E,
                             int32_t* hist_hi, qb_stream_t stream) {
   const char* fn = "qb_radix_hist_hi";

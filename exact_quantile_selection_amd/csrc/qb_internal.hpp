@@ -27,6 +27,8 @@ int device_cu_count();
 // layer; C: layers are the C microbatches of one layer).
 int launch_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
                         float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv = 1);
+int launch_lei_bwd(const float* g, const float* s, const int32_t* load_mb, int64_t N, int E, int K,
+                   int64_t n_mb, float eta, int bounded, float* g_out, float* dlogits, hipStream_t st);
 int launch_allreduce_sum(int32_t* buf, int R, int64_t M, hipStream_t st);
 int launch_rank_average(const float* q, int R, int E, float* b, float* bounds, hipStream_t st);
 int launch_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_tok, float* v,

@@ -144,4 +144,84 @@ int launch_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta
   return int(hipGetLastError());
 }
 
+// LEI per microbatch, optionally bounded, and the gradient through the
+// sigmoid ("Exact Quantile Balancing and Load-Error Injection for
+// Mixture-of-Experts", summary page, LEI paragraph: add eta * rho_e to the
+// score gradient of expert e for every token of the local batch; the
+// shipped variant bounds the residual with a tanh rescale that keeps its
+// direction and zero-centring).  Microbatch c = rows [c n_mb, (c+1) n_mb):
+//   rho_e  = fl32(((double)load[c][e] - M) / M),  M = n_mb K / E
+//   bounded: rho_e = fl32((double)rho_e * tanh(|rho|) / |rho|), |rho| the
+//            L2 norm over experts in float64 (sum in expert order)
+//   add_e  = fl32(eta * rho_e)
+//   g'     = fl32(g + add_e);  dlogit = fl32(g' * fl32(s * fl32(1 - s)))
+// grid (G, C): blockIdx.y is the microbatch.
+__global__ __launch_bounds__(kLeiThreads) void k_lei_bwd(const float* __restrict__ g,
+                                                         const float* __restrict__ s,
+                                                         const int32_t* __restrict__ load_mb, int64_t n_mb,
+                                                         int E, int K, float eta, int bounded,
+                                                         float* g_out, float* __restrict__ dlogits) {
+  __shared__ float add[256];
+  __shared__ double s_lambda;
+  const int c = blockIdx.y;
+  const int32_t* load = load_mb + int64_t(c) * E;
+  const double M = double(n_mb) * double(K) / double(E);
+  for (int e = threadIdx.x; e < E; e += kLeiThreads) add[e] = float((double(load[e]) - M) / M);
+  __syncthreads();
+  if (bounded) {
+    if (threadIdx.x == 0) {
+      double n2 = 0.0;
+      for (int e = 0; e < E; ++e) n2 += double(add[e]) * double(add[e]);
+      const double norm = sqrt(n2);
+      s_lambda = norm > 0.0 ? tanh(norm) / norm : 1.0;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kLeiThreads) add[e] = float(double(add[e]) * s_lambda);
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < E; e += kLeiThreads) add[e] = eta * add[e];
+  __syncthreads();
+  // The float4 stride of the grid is a multiple of E/4, so every thread
+  // keeps the same four experts.
+  const int64_t n4 = n_mb * E / 4;
+  const int64_t base4 = int64_t(c) * n4;
+  const int64_t stride = int64_t(gridDim.x) * kLeiThreads;
+  const int64_t i0 = int64_t(blockIdx.x) * kLeiThreads + threadIdx.x;
+  const int e0 = int((i0 * 4) % E);
+  const float a0 = add[e0], a1 = add[e0 + 1], a2 = add[e0 + 2], a3 = add[e0 + 3];
+  const float4* g4 = reinterpret_cast<const float4*>(g) + base4;
+  const float4* s4 = s ? reinterpret_cast<const float4*>(s) + base4 : nullptr;
+  float4* go4 = g_out ? reinterpret_cast<float4*>(g_out) + base4 : nullptr;
+  float4* d4 = dlogits ? reinterpret_cast<float4*>(dlogits) + base4 : nullptr;
+  for (int64_t i = i0; i < n4; i += stride) {
+    float4 v = g4[i];
+    v.x = v.x + a0;
+    v.y = v.y + a1;
+    v.z = v.z + a2;
+    v.w = v.w + a3;
+    if (go4) go4[i] = v;
+    if (d4) {
+      const float4 p = s4[i];
+      float4 d;
+      d.x = v.x * (p.x * (1.0f - p.x));
+      d.y = v.y * (p.y * (1.0f - p.y));
+      d.z = v.z * (p.z * (1.0f - p.z));
+      d.w = v.w * (p.w * (1.0f - p.w));
+      d4[i] = d;
+    }
+  }
+}
+
+int launch_lei_bwd(const float* g, const float* s, const int32_t* load_mb, int64_t N, int E, int K,
+                   int64_t n_mb, float eta, int bounded, float* g_out, float* dlogits, hipStream_t st) {
+  const int64_t C = N / n_mb;
+  const int64_t n4 = n_mb * E / 4;
+  const int64_t want = std::max<int64_t>(1, (n4 + kLeiThreads - 1) / kLeiThreads);
+  const int64_t cap = std::max<int64_t>(1, int64_t(device_cu_count()) * 8 / C);
+  const unsigned gx = unsigned(std::min(want, cap));
+  hipLaunchKernelGGL(k_lei_bwd, dim3(gx, unsigned(C)), dim3(kLeiThreads), 0, st, g, s, load_mb, n_mb, E, K, eta,
+                     bounded, g_out, dlogits);
+  return int(hipGetLastError());
+}
+
 }  // namespace qbk

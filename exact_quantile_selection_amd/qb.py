@@ -60,6 +60,7 @@ def lib() -> C.CDLL:
             "qb_maxvio": [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp],
             "qb_allreduce_sum_i32": [vp, i32, i64, vp],
             "qb_margins_full_hist": [vp, vp, i32, i64, i32, i32, vp, vp, vp],
+            "qb_lei_backward": [vp, vp, vp, i64, i32, i32, i64, f32, i32, vp, vp, vp],
             "qb_rank_average": [vp, i32, i32, vp, vp, vp],
         }
         for name, args in sig.items():
@@ -232,6 +233,20 @@ def qb_margins_full_hist(s, b, K, alpha, hist_full, stream=None):
         _ptr(s, torch.float32, "s"), _ptr(b, torch.float32, "b", lead + (E,)), L, N, E, K,
         _ptr(alpha, torch.float32, "alpha", lead + (N,)),
         _ptr(hist_full, torch.int32, "hist_full", lead + (E, 65536)), _stream(stream)))
+
+
+def qb_lei_backward(g, load_mb, K, n_mb, eta, bounded=False, s=None, g_out=None, dlogits=None,
+                    stream=None):
+    """Per-microbatch LEI on the score gradient g [N, E] (optionally bounded),
+    written to g_out (may be g) and/or the logit gradient dlogits."""
+    N, E = g.shape
+    if n_mb < 1 or N % n_mb:
+        raise ValueError(f"n_mb={n_mb} must divide N={N}")
+    _check(lib().qb_lei_backward(
+        _ptr(g, torch.float32, "g"), _ptr(s, torch.float32, "s", (N, E), opt=True),
+        _ptr(load_mb, torch.int32, "load_mb", (N // n_mb, E)), N, E, K, n_mb, float(eta), int(bool(bounded)),
+        _ptr(g_out, torch.float32, "g_out", (N, E), opt=True),
+        _ptr(dlogits, torch.float32, "dlogits", (N, E), opt=True), _stream(stream)))
 
 
 def qb_allreduce_sum_i32(buf, stream=None):

@@ -241,6 +241,30 @@ QB_API int qb_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_
                      float* summary, float* worst, qb_stream_t stream);
 
 /*
+ * LEI per local batch, optionally bounded, and the gradient through the
+ * router sigmoid ("Exact Quantile Balancing and Load-Error Injection for
+ * Mixture-of-Experts", summary page, LEI paragraph: eta * rho_e is added to
+ * expert e's score gradient for every token of the local batch; the shipped
+ * "normalized" variant bounds the residual with a tanh rescale that keeps
+ * its direction and zero-centring -- the formula is not printed; the
+ * rescale used here is the plainest one with those properties).  The N rows
+ * form C = N / n_mb microbatches of n_mb rows; for microbatch c:
+ *   rho_e  = fl32(((double)load_mb[c][e] - M) / M),  M = n_mb * K / E
+ *   bounded == 1: rho_e = fl32((double)rho_e * tanh(|rho|) / |rho|), |rho| =
+ *            float64 L2 norm over the E experts (sum in expert order)
+ *   add_e  = fl32(eta * rho_e);  g' = fl32(g + add_e)
+ *   dlogit = fl32(g' * fl32(s * fl32(1 - s)))      (sigmoid derivative)
+ * With n_mb = N and bounded = 0, g' is exactly qb_lei_grad's result.
+ *   g float [N][E] (read); s float [N][E] (needed for dlogits);
+ *   load_mb int32 [C][E]; g_out float [N][E] (nullable; may be g);
+ *   dlogits float [N][E] (nullable); float arrays 16-byte aligned;
+ *   C <= 65535.
+ */
+QB_API int qb_lei_backward(const float* g, const float* s, const int32_t* load_mb, int64_t N, int E, int K,
+                           int64_t n_mb, float eta, int bounded, float* g_out, float* dlogits,
+                           qb_stream_t stream);
+
+/*
  * One-GPU emulation of data-parallel ranks ("Exact Quantile Balancing and
  * Load-Error Injection for Mixture-of-Experts", summary page, background
  * paragraph: rank-local quantiles averaged across ranks depend on the

@@ -71,6 +71,9 @@ def lib():
         L.oq_bounds_of.argtypes = [f32p, C.c_int, f32p]
         L.oq_lei.restype = None
         L.oq_lei.argtypes = [f32p, i32p, C.c_int64, C.c_int, C.c_int, C.c_float]
+        L.oq_lei_bwd.restype = None
+        L.oq_lei_bwd.argtypes = [f32p, C.c_void_p, i32p, C.c_int64, C.c_int, C.c_int, C.c_int64, C.c_float,
+                                 C.c_int, C.c_void_p, C.c_void_p]
         L.oq_rank_average.restype = None
         L.oq_rank_average.argtypes = [f32p, C.c_int, C.c_int, f32p, f32p]
         L.oq_maxvio.restype = None
@@ -234,3 +237,17 @@ def full_hist(s, b, K: int) -> np.ndarray:
     N, E = s.shape
     keys = margin_keys(s, alpha(s, b, K, with_load=False))
     return np.stack([np.bincount(keys[j], minlength=65536).astype(np.int32) for j in range(E)])
+
+
+def lei_backward(g, load_mb, K: int, n_mb: int, eta, bounded: bool = False, s=None):
+    """-> (g' [N, E], dlogits [N, E] or None)."""
+    g = _f32(g)
+    N, E = g.shape
+    load_mb = np.ascontiguousarray(load_mb, dtype=np.int32)
+    gout = np.zeros_like(g)
+    d = np.zeros_like(g) if s is not None else None
+    sp = _f32(s) if s is not None else None
+    lib().oq_lei_bwd(g, sp.ctypes.data if sp is not None else None, load_mb, N, E, K, n_mb,
+                     np.float32(eta), int(bool(bounded)), gout.ctypes.data,
+                     d.ctypes.data if d is not None else None)
+    return gout, d

@@ -269,6 +269,43 @@ void oq_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta) {
     for (int e = 0; e < E; ++e) g[i * E + e] = g[i * E + e] + add[e];
 }
 
+// LEI per microbatch ([EQB] LEI paragraph: eta * rho_e added to expert e's
+// score gradient for every token of the local batch), optionally with the
+// bounded ("normalized") residual -- a tanh rescale keeping direction and
+// zero-centring; the formula is not printed, so this reading (rho scaled by
+// tanh(|rho|) / |rho|, L2 norm in float64) is parity unpinned against the
+// pages -- and the gradient through the sigmoid:
+//   g' = fl32(g + fl32(eta * rho_e)), dlogit = fl32(g' * fl32(s * fl32(1 - s))).
+// g_out and dlogits may be NULL.
+void oq_lei_bwd(const float* g, const float* s, const int32_t* load_mb, int64_t N, int E, int K, int64_t n_mb,
+                float eta, int bounded, float* g_out, float* dlogits) {
+  const double M = double(n_mb) * double(K) / double(E);
+  std::vector<float> rho(E), add(E);
+  for (int64_t c = 0; c < N / n_mb; ++c) {
+    const int32_t* load = load_mb + c * E;
+    for (int e = 0; e < E; ++e) rho[e] = float((double(load[e]) - M) / M);
+    if (bounded) {
+      double n2 = 0.0;
+      for (int e = 0; e < E; ++e) n2 += double(rho[e]) * double(rho[e]);
+      const double norm = std::sqrt(n2);
+      const double lambda = norm > 0.0 ? std::tanh(norm) / norm : 1.0;
+      for (int e = 0; e < E; ++e) rho[e] = float(double(rho[e]) * lambda);
+    }
+    for (int e = 0; e < E; ++e) add[e] = eta * rho[e];
+    for (int64_t i = c * n_mb; i < (c + 1) * n_mb; ++i)
+      for (int e = 0; e < E; ++e) {
+        const int64_t k = i * E + e;
+        const float gp = g[k] + add[e];
+        if (g_out) g_out[k] = gp;
+        if (dlogits) {
+          const float one_minus = 1.0f - s[k];
+          const float ds = s[k] * one_minus;
+          dlogits[k] = gp * ds;
+        }
+      }
+  }
+}
+
 // Router logits of selected rows, bf16 inputs, float64 accumulation; the
 // weight is stored [E][H] (nn.Linear layout):
 // out[r * E + e] = sum_h hidden[rows[r]][h] * w[e][h].

@@ -515,3 +515,80 @@ def test_full_histogram_agrees_with_the_byte_histograms(O, N, E, K, quant):
         np.testing.assert_array_equal(full[j, hi * 256:(hi + 1) * 256], ref["hist_lo"][j])
         key = int(np.argmax(np.cumsum(full[j]) >= m))   # first bin reaching rank m
         assert key == int(ref["key"][j])
+
+
+# --- LEI per local batch, bounded variant, gradient through the sigmoid
+# ("Exact Quantile Balancing and Load-Error Injection for Mixture-of-Experts",
+# summary page, LEI paragraph).  The bounded formula is not printed; these
+# pins fix the reading (a tanh rescale of the residual vector), not the
+# pages' own implementation.
+
+def test_lei_backward_one_microbatch_is_lei(O):
+    rng = np.random.default_rng(12)
+    N, E, K = 512, 64, 4
+    g = rng.standard_normal((N, E), dtype=np.float32)
+    load = rng.multinomial(N * K, np.ones(E) / E).astype(np.int32)
+    got, _ = O.lei_backward(g, load[None, :], K, N, np.float32(1e-3))
+    np.testing.assert_array_equal(got, O.lei(g, load, K, np.float32(1e-3)))
+
+
+def _add_vector(O, load, K, n_mb, bounded, eta=1.0):
+    E = load.shape[-1]
+    g0 = np.zeros((n_mb, E), np.float32)
+    gp, _ = O.lei_backward(g0, load[None, :], K, n_mb, np.float32(eta), bounded)
+    return gp[0].astype(np.float64)
+
+
+def test_bounded_lei_hand_example(O):
+    """loads (3, 1, 1, 3) of 4 tokens, K = 2: M = 2, rho = (.5, -.5, -.5, .5),
+    |rho| = 1, so the bounded residual is rho * tanh(1)."""
+    add = _add_vector(O, np.array([3, 1, 1, 3], np.int32), 2, 4, True)
+    t = np.float32(0.5 * math.tanh(1.0))
+    np.testing.assert_array_equal(add, np.array([t, -t, -t, t], np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("skew", [0.0, 0.3, 3.0])
+def test_bounded_lei_direction_centring_bound(O, skew):
+    rng = np.random.default_rng(int(skew * 10) + 1)
+    E, K, n_mb = 256, 6, 4096
+    p = np.exp(skew * rng.standard_normal(E))
+    load = rng.multinomial(n_mb * K, p / p.sum()).astype(np.int32)
+    rho = (load.astype(np.float64) - n_mb * K / E) / (n_mb * K / E)
+    un = _add_vector(O, load, K, n_mb, False)
+    bo = _add_vector(O, load, K, n_mb, True)
+    nrm = np.linalg.norm(rho)
+    lam = math.tanh(nrm) / nrm
+    # same direction: the bounded add is the unbounded one times tanh(|rho|)/|rho|
+    assert np.allclose(bo, un * lam, rtol=2e-7, atol=1e-9)
+    assert abs(bo.sum()) <= 1e-6 * max(1.0, np.abs(bo).sum())         # zero-centred
+    # bounded: |rho~| = tanh(|rho|) <= 1 (up to the fp32 rounding of each term)
+    assert np.linalg.norm(bo) <= 1.0 + 1e-6
+    assert abs(np.linalg.norm(bo) - math.tanh(nrm)) < 1e-6
+
+
+def test_bounded_lei_extreme_and_near_uniform(O):
+    E, K, n_mb = 64, 4, 1024
+    load = np.zeros(E, np.int32)
+    load[:K] = n_mb                          # every token on the same K experts
+    bo = _add_vector(O, load, K, n_mb, True)
+    assert 0.999 < np.linalg.norm(bo) <= 1.0 + 1e-6   # saturated at the bound
+    near = np.full(E, n_mb * K // E, np.int32)
+    near[0] += 1
+    near[1] -= 1
+    un = _add_vector(O, near, K, n_mb, False)
+    bo = _add_vector(O, near, K, n_mb, True)
+    assert np.allclose(bo, un, rtol=1e-3)   # tanh(x)/x -> 1 for a small residual
+
+
+def test_dlogits_match_autograd_of_sigmoid(O):
+    rng = np.random.default_rng(13)
+    N, E, K = 256, 16, 2
+    x = rng.normal(0, 2, (N, E))
+    s = (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
+    g = rng.standard_normal((N, E), dtype=np.float32)
+    load = rng.multinomial(N * K, np.ones(E) / E).astype(np.int32)
+    gp, d = O.lei_backward(g, load[None, :], K, N, np.float32(1e-2), False, s=s)
+    xt = torch.tensor(np.log(s.astype(np.float64)) - np.log1p(-s.astype(np.float64)), requires_grad=True)
+    torch.sigmoid(xt).backward(torch.tensor(gp.astype(np.float64)))
+    ref = xt.grad.numpy()
+    assert np.allclose(d, ref, rtol=1e-6, atol=1e-12)
