@@ -55,9 +55,10 @@ class BiasController:
         buf = self.buf
         buf.reset(stream)
         qb.qb_fill_i32(self.loads, 0, stream)
-        # pass 1 with the bias in force: alpha, loads, high-byte histogram
-        qb.qb_margins_topk(s3, self.b, K, self.alpha, load=self.load, hist_hi=buf.hist_hi, stream=stream)
-        qb.qb_microbatch_loads(s3, self.b, K, self.n_mb, self.alpha, self.load_mb, stream=stream)
+        # pass 1 with the bias in force: alpha, loads, per-microbatch loads
+        # and the high-byte histogram in one read of the scores
+        qb.qb_margins_topk_mb(s3, self.b, K, self.alpha, self.load, self.n_mb, self.load_mb,
+                              hist_hi=buf.hist_hi, stream=stream)
         qb.qb_maxvio(self.load.view(L, 1, E), K, N, self.mv_global, self.summary_global,
                      self.worst_global, stream=stream)
         qb.qb_maxvio(self.load_mb, K, self.n_mb, self.mv_local, self.summary_local, self.worst_local,

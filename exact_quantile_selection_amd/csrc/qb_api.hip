@@ -17,11 +17,11 @@
 
 namespace qbk {
 
-int launch_margins_topk_e16(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
-int launch_margins_topk_e32(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
-int launch_margins_topk_e64(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
-int launch_margins_topk_e128(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
-int launch_margins_topk_e256(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t);
+int launch_margins_topk_e16(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t, int32_t*, int64_t);
+int launch_margins_topk_e32(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t, int32_t*, int64_t);
+int launch_margins_topk_e64(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t, int32_t*, int64_t);
+int launch_margins_topk_e128(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t, int32_t*, int64_t);
+int launch_margins_topk_e256(const float*, const float*, int, int, int64_t, int, float*, int32_t*, int32_t*, hipStream_t, int32_t*, int64_t);
 
 int launch_margins_full_e16(const float*, const float*, int, int64_t, int, float*, int32_t*, hipStream_t);
 int launch_margins_full_e32(const float*, const float*, int, int64_t, int, float*, int32_t*, hipStream_t);
@@ -30,13 +30,14 @@ int launch_margins_full_e128(const float*, const float*, int, int64_t, int, floa
 int launch_margins_full_e256(const float*, const float*, int, int64_t, int, float*, int32_t*, hipStream_t);
 
 int launch_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
-                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv) {
+                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv,
+                        int32_t* load_mb, int64_t n_mb) {
   switch (E) {
-    case 16: return launch_margins_topk_e16(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 32: return launch_margins_topk_e32(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 64: return launch_margins_topk_e64(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 128: return launch_margins_topk_e128(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 256: return launch_margins_topk_e256(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 16: return launch_margins_topk_e16(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 32: return launch_margins_topk_e32(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 64: return launch_margins_topk_e64(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 128: return launch_margins_topk_e128(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 256: return launch_margins_topk_e256(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
   }
   return int(hipErrorInvalidValue);
 }
@@ -136,6 +137,25 @@ QB_API int qb_margins_topk(const float* s, const float* b, int L, int64_t N, int
     return fail(QB_EINVAL, "%s: b, alpha and load must be 4-byte aligned", fn);
   if (hist_hi && !aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
   return hip_status(qbk::launch_margins_topk(s, b, L, N, E, K, alpha, load, hist_hi, stream), fn);
+}
+
+QB_API int qb_margins_topk_mb(const float* s, const float* b, int L, int64_t N, int E, int K, float* alpha,
+                              int32_t* load, int32_t* hist_hi, int64_t n_mb, int32_t* load_mb,
+                              qb_stream_t stream) {
+  const char* fn = "qb_margins_topk_mb";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!b || !alpha || !load || !load_mb)
+    return fail(QB_EINVAL, "%s: b (float [L=%d][E=%d]), alpha (float [L][N]), load (int32 [L][E]) and load_mb (int32 [L][N/n_mb][E]) are required",
+                fn, L, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (n_mb < 1 || N % n_mb != 0)
+    return fail(QB_EINVAL, "%s: n_mb=%lld must be >= 1 and divide N=%lld", fn, (long long)n_mb, (long long)N);
+  if (!aligned4(b) || !aligned4(alpha) || !aligned4(load) || !aligned4(load_mb))
+    return fail(QB_EINVAL, "%s: b, alpha, load and load_mb must be 4-byte aligned", fn);
+  if (hist_hi && !aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
+  return hip_status(qbk::launch_margins_topk(s, b, L, N, E, K, alpha, load, hist_hi, stream, 1, load_mb, n_mb),
+                    fn);
 }
 
 QB_API int qb_microbatch_loads(const float* s, const float* b, int L, int64_t N, int E, int K,

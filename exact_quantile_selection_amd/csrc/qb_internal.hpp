@@ -25,8 +25,11 @@ int device_cu_count();
 // Launchers (return hipError_t as int).  Shapes were validated by the caller.
 // bdiv: that many consecutive layers share one bias row (1: one row per
 // layer; C: layers are the C microbatches of one layer).
+// load_mb (nullable, needs load): also count each token's top-K experts
+// into load_mb[l][row / n_mb][e] with device atomics.
 int launch_margins_topk(const float* s, const float* b, int L, int64_t N, int E, int K,
-                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv = 1);
+                        float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv = 1,
+                        int32_t* load_mb = nullptr, int64_t n_mb = 1);
 int launch_lei_bwd(const float* g, const float* s, const int32_t* load_mb, int64_t N, int E, int K,
                    int64_t n_mb, float eta, int bounded, float* g_out, float* dlogits, hipStream_t st);
 int launch_allreduce_sum(int32_t* buf, int R, int64_t M, hipStream_t st);

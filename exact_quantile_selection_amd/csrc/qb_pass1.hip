@@ -33,6 +33,12 @@
 #include "qb_device.hpp"
 #include "qb_internal.hpp"
 
+// Rows per workgroup at most (16-bit LDS counters hold 65535); smaller
+// values give more, shorter-lived workgroups.
+#ifndef QB_P1_MAXROWS
+#define QB_P1_MAXROWS 65535
+#endif
+
 namespace qbk {
 
 // 16 waves per workgroup (<= 128 VGPRs each); the load-counting variant
@@ -76,7 +82,7 @@ __device__ __forceinline__ uint64_t rotl_v(uint64_t m, int n) {
 template <int E, int P>
 __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], const float* lds_b,
                                             int rho, int ql, float a, int K, bool valid,
-                                            int32_t* lds_load) {
+                                            int32_t* lds_load, int32_t* mb_row) {
   using S = P1Shape<E>;
   uint64_t gt_t = 0, eq_t = 0;
 #pragma unroll
@@ -127,7 +133,9 @@ __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], c
   while (mem) {
     const int bit = __builtin_ctzll(mem);
     mem &= mem - 1;
-    atomicAdd(&lds_load[4 * (S::LPR * (bit >> 2) + ql) + (bit & 3)], 1);
+    const int e = 4 * (S::LPR * (bit >> 2) + ql) + (bit & 3);
+    atomicAdd(&lds_load[e], 1);
+    if (mb_row) atomicAdd(mb_row + e, 1);  // this token's microbatch
   }
 }
 
@@ -165,7 +173,7 @@ template <int E, int P, int HM, bool LOAD>
 __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64_t base, int64_t N,
                                         int rho, int ql, int lane, int K, const float* lds_b,
                                         uint32_t* lds_hist, int32_t* lds_load, float* alpha,
-                                        int32_t* ghist) {
+                                        int32_t* ghist, int32_t* load_mb, int64_t n_mb) {
   using S = P1Shape<E>;
   const int64_t row = base + rho;
   const bool valid = row < N;
@@ -193,7 +201,10 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
     a = top_merge_last<P, kQuadXor2>(top);
   }
   if (valid && ql == 0) alpha[row] = a;
-  if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load);
+  if constexpr (LOAD) {
+    int32_t* mb_row = load_mb && valid ? load_mb + (row / n_mb) * E : nullptr;
+    count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load, mb_row);
+  }
   if constexpr (HM == 2) {
     // full 16-bit key histogram, [E][65536] int32 in global memory
     if (valid) {
@@ -226,7 +237,8 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
 template <int E, int P, int HM, bool LOAD>
 __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
     const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int bdiv, int K,
-    float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi) {
+    float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi,
+    int32_t* __restrict__ load_mb, int64_t n_mb) {
   using S = P1Shape<E>;
   constexpr int kWaves = p1_waves<LOAD>();
   constexpr int kThreads = kWaves * kWave;
@@ -241,6 +253,7 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
   b += int64_t(layer / bdiv) * E;  // bdiv consecutive layers share a bias row
   alpha += int64_t(layer) * N;
   int32_t* ghist = HM == 2 ? hist_hi + int64_t(layer) * E * 65536 : nullptr;
+  if (LOAD && load_mb) load_mb += int64_t(layer) * (N / n_mb) * E;
 
   if constexpr (HM == 1) hist16_zero<E>(lds_hist, tid, kThreads);
   for (int j = tid; j < E; j += kThreads) {
@@ -261,7 +274,8 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
   for (; base < N; base += stride) {
     float4 x[S::F4];
     p1_load<E>(s, base, N, rho, ql, x);
-    p1_rows<E, P, HM, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist);
+    p1_rows<E, P, HM, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist, load_mb,
+                            n_mb);
   }
   __syncthreads();
   if constexpr (HM == 1) hist16_flush<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
@@ -273,34 +287,36 @@ __global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
 
 template <int E, int P, int HM, bool LOAD>
 static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
-                       int32_t* load, int32_t* hist_hi, hipStream_t st) {
+                       int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb = nullptr,
+                       int64_t n_mb = 1) {
   constexpr int kThreads = p1_waves<LOAD>() * kWave;
-  const RowSplit sp = split_rows(L, N, p1_waves<LOAD>() * P1Shape<E>::RPW, 65535);
+  const RowSplit sp = split_rows(L, N, p1_waves<LOAD>() * P1Shape<E>::RPW, QB_P1_MAXROWS);
   hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD>), dim3(unsigned(sp.blocks)), dim3(kThreads),
-                     0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi);
+                     0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi, load_mb, n_mb);
   return int(hipGetLastError());
 }
 
 template <int E, int P>
 static int launch_p1(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
-                     int32_t* load, int32_t* hist_hi, hipStream_t st) {
-  if (hist_hi && load) return launch_p1_v<E, P, 1, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+                     int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb, int64_t n_mb) {
+  if (hist_hi && load)
+    return launch_p1_v<E, P, 1, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
   if (hist_hi) return launch_p1_v<E, P, 1, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-  if (load) return launch_p1_v<E, P, 0, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  if (load) return launch_p1_v<E, P, 0, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
   return launch_p1_v<E, P, 0, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
 }
 
 template <int E>
 static int launch_p1_k(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
-                       int32_t* load, int32_t* hist_hi, hipStream_t st) {
+                       int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb, int64_t n_mb) {
   switch (K + 1) {
-    case 2: return launch_p1<E, 2>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 3: return launch_p1<E, 3>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 4: return launch_p1<E, 4>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 5: return launch_p1<E, 5>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 6: return launch_p1<E, 6>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 7: return launch_p1<E, 7>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-    case 8: return launch_p1<E, 8>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    case 2: return launch_p1<E, 2>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 3: return launch_p1<E, 3>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 4: return launch_p1<E, 4>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 5: return launch_p1<E, 5>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 6: return launch_p1<E, 6>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 7: return launch_p1<E, 7>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    case 8: return launch_p1<E, 8>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
   }
   return int(hipErrorInvalidValue);
 }
@@ -328,8 +344,9 @@ static int launch_full_k(const float* s, const float* b, int L, int64_t N, int K
 #define QB_P1_CAT(a, b) QB_P1_CAT2(a, b)
 int QB_P1_CAT(launch_margins_topk_e, QB_P1_E)(const float* s, const float* b, int L, int bdiv,
                                                int64_t N, int K, float* alpha, int32_t* load,
-                                               int32_t* hist_hi, hipStream_t st) {
-  return launch_p1_k<QB_P1_E>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+                                               int32_t* hist_hi, hipStream_t st, int32_t* load_mb,
+                                               int64_t n_mb) {
+  return launch_p1_k<QB_P1_E>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
 }
 
 int QB_P1_CAT(launch_margins_full_e, QB_P1_E)(const float* s, const float* b, int L, int64_t N, int K,

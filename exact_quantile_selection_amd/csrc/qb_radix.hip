@@ -21,6 +21,12 @@
 #include "qb_device.hpp"
 #include "qb_internal.hpp"
 
+// Rows per workgroup at most (16-bit LDS counters hold 65535); smaller
+// values give more, shorter-lived workgroups.
+#ifndef QB_RH_MAXROWS
+#define QB_RH_MAXROWS 65535
+#endif
+
 namespace qbk {
 
 constexpr int kRHWaves = 16;
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
 template <int E>
 static int launch_rh(bool lo, const float* s, const float* alpha, int L, int64_t N,
                      const int32_t* sel_hi, int32_t* hist, hipStream_t st) {
-  const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, 65535);
+  const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, QB_RH_MAXROWS);
   if (lo)
     hipLaunchKernelGGL((k_radix_hist<E, true>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
                        s, alpha, N, sp.wg_per_layer, sel_hi, hist);

@@ -25,7 +25,10 @@
 
 namespace qbk {
 
-constexpr int kRowWaves = 16;                   // experts per workgroup (one per wave)
+#ifndef QB_SEL_WAVES
+#define QB_SEL_WAVES 16
+#endif
+constexpr int kRowWaves = QB_SEL_WAVES;         // experts per workgroup (one per wave)
 constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kFinThreads = 256;                // >= E: one thread per expert
 

@@ -57,6 +57,7 @@ def lib() -> C.CDLL:
             "qb_lei_grad": [vp, vp, i64, i32, i32, f32, vp],
             "qb_router_fused": [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "qb_microbatch_loads": [vp, vp, i32, i64, i32, i32, i64, vp, vp, vp],
+            "qb_margins_topk_mb": [vp, vp, i32, i64, i32, i32, vp, vp, vp, i64, vp, vp],
             "qb_maxvio": [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp],
             "qb_allreduce_sum_i32": [vp, i32, i64, vp],
             "qb_margins_full_hist": [vp, vp, i32, i64, i32, i32, vp, vp, vp],
@@ -212,6 +213,18 @@ def qb_microbatch_loads(s, b, K, n_mb, alpha, load_mb, stream=None):
     _check(lib().qb_microbatch_loads(
         _ptr(s, torch.float32, "s"), _ptr(b, torch.float32, "b", lead + (E,)), L, N, E, K, n_mb,
         _ptr(alpha, torch.float32, "alpha", lead + (N,)),
+        _ptr(load_mb, torch.int32, "load_mb", lead + (N // n_mb, E)), _stream(stream)))
+
+
+def qb_margins_topk_mb(s, b, K, alpha, load, n_mb, load_mb, hist_hi=None, stream=None):
+    """Pass 1 with global loads, per-microbatch loads and (optionally) hist_hi."""
+    L, N, E, lead = _lne(s)
+    if n_mb < 1 or N % n_mb:
+        raise ValueError(f"n_mb={n_mb} must divide N={N}")
+    _check(lib().qb_margins_topk_mb(
+        _ptr(s, torch.float32, "s"), _ptr(b, torch.float32, "b", lead + (E,)), L, N, E, K,
+        _ptr(alpha, torch.float32, "alpha", lead + (N,)), _ptr(load, torch.int32, "load", lead + (E,)),
+        _ptr(hist_hi, torch.int32, "hist_hi", lead + (E, 256), opt=True), n_mb,
         _ptr(load_mb, torch.int32, "load_mb", lead + (N // n_mb, E)), _stream(stream)))
 
 

@@ -226,6 +226,18 @@ QB_API int qb_microbatch_loads(const float* s, const float* b, int L, int64_t N,
                                int64_t n_mb, float* alpha, int32_t* load_mb, qb_stream_t stream);
 
 /*
+ * qb_margins_topk with loads and, in the same pass, the per-microbatch loads
+ * of qb_microbatch_loads (each top-K member of token i also adds 1 to
+ * load_mb[l][i / n_mb][e], one device atomic per member): the global and
+ * the local balance of a batch from one read of the scores.
+ *   load int32 [L][E] and load_mb int32 [L][N/n_mb][E] required,
+ *   accumulated (+=); hist_hi nullable; n_mb must divide N.
+ */
+QB_API int qb_margins_topk_mb(const float* s, const float* b, int L, int64_t N, int E, int K, float* alpha,
+                              int32_t* load, int32_t* hist_hi, int64_t n_mb, int32_t* load_mb,
+                              qb_stream_t stream);
+
+/*
  * MaxVio ("Exact Quantile Balancing and Load-Error Injection for
  * Mixture-of-Experts", summary page, testbed paragraph: how far the busiest
  * expert of the worst layer exceeds the uniform load).  For each of the L*C

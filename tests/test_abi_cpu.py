@@ -91,6 +91,8 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
     assert rc == qb.QB_EINVAL and "divide N=1000" in _last(libqb)
     rc = libqb.qb_microbatch_loads(fake, fake, 1, 1024, 256, 6, 256, fake, None, None)
     assert rc == qb.QB_EINVAL and "[C=4][E=256]" in _last(libqb)
+    rc = libqb.qb_margins_topk_mb(fake, fake, 1, 1024, 256, 6, fake, None, None, 256, fake, None)
+    assert rc == qb.QB_EINVAL and "load (int32" in _last(libqb)
     rc = libqb.qb_maxvio(fake, 1, 4, 256, 300, 1024, fake, None, None, None)
     assert rc == qb.QB_EINVAL and "K=300" in _last(libqb)
     rc = libqb.qb_maxvio(fake, 1, 4, 256, 6, 1024, None, None, None, None)

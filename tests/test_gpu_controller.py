@@ -135,3 +135,22 @@ def test_closed_loop_full_size(O):
     G.say("controller full size: oracle")
     want = oracle_loop(O, batches, np.zeros((1, E), np.float32), K, n_mb)
     compare_loop(got, want)
+
+
+@pytest.mark.parametrize("N,E,K,n_mb,quant", [(8192, 256, 6, 1024, None), (6000, 64, 4, 1000, 8.0),
+                                             (2048, 16, 2, 2048, None), (4096, 128, 7, 128, 16.0)])
+def test_fused_pass1_microbatch_loads(O, N, E, K, n_mb, quant):
+    """qb_margins_topk_mb: alpha, global loads, per-microbatch loads and the
+    high-byte histogram from one read of the scores."""
+    G.say(f"fused pass 1 + microbatch loads N={N} E={E} n_mb={n_mb}")
+    s, b, _ = synth.random_case(61, N, E, K, quant=quant)
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    load = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+    load_mb = torch.zeros((N // n_mb, E), dtype=torch.int32, device=G.DEV)
+    hist = torch.zeros((E, 256), dtype=torch.int32, device=G.DEV)
+    qb.qb_margins_topk_mb(G.dev(s), G.dev(b), K, alpha, load, n_mb, load_mb, hist_hi=hist)
+    ref = O.eqb_layer(s, b, K)
+    G.assert_same("alpha", G.host(alpha), ref["alpha"])
+    G.assert_same("load", G.host(load), ref["load"])
+    G.assert_same("hist_hi", G.host(hist), ref["hist_hi"])
+    G.assert_same("load_mb", G.host(load_mb), O.microbatch_loads(s, b, K, n_mb))
