@@ -504,7 +504,7 @@ def controller_suite(torch, qb, synth, dev, args, T=8):
                global_maxvio=[round(float(a[0]), 4) for a, _ in traj],
                local_maxvio_mean=[round(float(b[1]), 4) for _, b in traj],
                local_maxvio_max=[round(float(b[0]), 4) for _, b in traj],
-               step="pass 1 (alpha, loads, hist_hi), microbatch loads, 2 x MaxVio, select HI, "
+               step="pass 1 (alpha, loads, microbatch loads, hist_hi), 2 x MaxVio, select HI, "
                     "pass 2, select LO (b updated in place)")
     del batches
     torch.cuda.empty_cache()

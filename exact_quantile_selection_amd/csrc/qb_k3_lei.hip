@@ -193,21 +193,36 @@ __global__ __launch_bounds__(kLeiThreads) void k_lei_bwd(const float* __restrict
   const float4* s4 = s ? reinterpret_cast<const float4*>(s) + base4 : nullptr;
   float4* go4 = g_out ? reinterpret_cast<float4*>(g_out) + base4 : nullptr;
   float4* d4 = dlogits ? reinterpret_cast<float4*>(dlogits) + base4 : nullptr;
-  for (int64_t i = i0; i < n4; i += stride) {
-    float4 v = g4[i];
-    v.x = v.x + a0;
-    v.y = v.y + a1;
-    v.z = v.z + a2;
-    v.w = v.w + a3;
-    if (go4) go4[i] = v;
-    if (d4) {
-      const float4 p = s4[i];
-      float4 d;
-      d.x = v.x * (p.x * (1.0f - p.x));
-      d.y = v.y * (p.y * (1.0f - p.y));
-      d.z = v.z * (p.z * (1.0f - p.z));
-      d.w = v.w * (p.w * (1.0f - p.w));
-      d4[i] = d;
+  // four strided elements per thread and trip: all loads issued before any
+  // store, so each thread keeps 8 (or 4) 16-byte reads in flight
+  constexpr int U = 4;
+  for (int64_t i = i0; i < n4; i += U * stride) {
+    float4 v[U], p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = i + u * stride;
+      if (k < n4) {
+        v[u] = g4[k];
+        if (d4) p[u] = s4[k];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = i + u * stride;
+      if (k >= n4) continue;
+      v[u].x = v[u].x + a0;
+      v[u].y = v[u].y + a1;
+      v[u].z = v[u].z + a2;
+      v[u].w = v[u].w + a3;
+      if (go4) go4[k] = v[u];
+      if (d4) {
+        float4 d;
+        d.x = v[u].x * (p[u].x * (1.0f - p[u].x));
+        d.y = v[u].y * (p[u].y * (1.0f - p[u].y));
+        d.z = v[u].z * (p[u].z * (1.0f - p[u].z));
+        d.w = v[u].w * (p[u].w * (1.0f - p[u].w));
+        d4[k] = d;
+      }
     }
   }
 }
