@@ -50,9 +50,12 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef __attribute__((address_space(1))) void* glb_vptr;
 
-constexpr int kRgThreads = 512;
-constexpr int kRgWaves = kRgThreads / kWave;
-constexpr int kRgBM = 256;  // token rows per workgroup
+#ifndef QB_RG_WAVES
+#define QB_RG_WAVES 8
+#endif
+constexpr int kRgWaves = QB_RG_WAVES;
+constexpr int kRgThreads = kRgWaves * kWave;
+constexpr int kRgBM = 32 * kRgWaves;  // token rows per workgroup
 
 template <int E>
 struct RgShape {
@@ -93,7 +96,8 @@ __device__ __forceinline__ float rg_sigmoid(float x) {
 }
 
 template <int E, int BK, int S>
-__global__ __launch_bounds__(kRgThreads) void k_router_gemm(const uint16_t* __restrict__ hidden,
+__global__ __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void k_router_gemm(const uint16_t* __restrict__ hidden,
                                                             const uint16_t* __restrict__ w,
                                                             int64_t N, int H,
                                                             float* __restrict__ s_out,
