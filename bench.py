@@ -47,20 +47,25 @@ def cpu_model():
 class EqbStep:
     """Device state of one EQB layer update and its launch sequence."""
 
-    def __init__(self, s, b0, K, qb, torch, L=None):
+    def __init__(self, s, b0, K, qb, torch, L=None, ws=True):
         self.qb, self.torch = qb, torch
         self.s, self.b0, self.K = s, b0, K
         lead = s.dim() == 3
         N, E = s.shape[-2], s.shape[-1]
         Lx = s.shape[0] if lead else 1
+        self.N = N
         self.b = b0.clone()
         self.alpha = torch.empty(((Lx,) if lead else ()) + (N,), dtype=torch.float32, device=s.device)
         self.buf = qb.EqbBuffers(Lx, E, device=s.device, lead=lead)
+        # Pass 2 merges its histogram either through a workspace of per-
+        # workgroup partials (default) or with global atomics.
+        self.ws = (torch.empty(qb.qb_hist_lo_workspace_bytes(Lx, N, E), dtype=torch.uint8, device=s.device)
+                   if ws else None)
 
     def launches(self):
         """(name, callable) of the step, in stream order."""
         qb, buf = self.qb, self.buf
-        return [
+        head = [
             ("restore_bias", lambda: self.b.copy_(self.b0)),
             ("reset_hist", lambda: buf.reset()),
             ("pass1_topk_hist_hi", lambda: qb.qb_margins_topk(self.s, self.b, self.K, self.alpha,
@@ -68,6 +73,15 @@ class EqbStep:
             ("select_hi", lambda: qb.qb_select_update(qb.QB_SELECT_HI, self.K, buf.hist_hi,
                                                       sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
                                                       err=buf.err)),
+        ]
+        if self.ws is not None:
+            return head + [
+                ("pass2_hist_lo", lambda: qb.qb_radix_hist_lo_ws(self.s, self.alpha, buf.sel_hi, self.ws)),
+                ("select_lo", lambda: qb.qb_select_lo_ws(self.N, self.ws, buf.sel_hi, buf.rank_lo, buf.q,
+                                                         self.b, buf.bounds, hist_lo=buf.hist_lo,
+                                                         key_out=buf.key, err=buf.err)),
+            ]
+        return head + [
             ("pass2_hist_lo", lambda: qb.qb_radix_hist_lo(self.s, self.alpha, buf.sel_hi, buf.hist_lo)),
             ("select_lo", lambda: qb.qb_select_update(qb.QB_SELECT_LO, self.K, buf.hist_lo,
                                                       sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
@@ -240,7 +254,15 @@ def main():
     torch.cuda.synchronize()
     sec, _graph = time_graph(step, torch, args.steps, args.warmup)
     assert int(step.buf.err.item()) == 0
+    b_ws = step.b.clone()
     per_k = time_kernels(step, torch, max(5, args.steps))
+    del _graph
+    # The same step with pass 2 merged by global atomics, for contrast.
+    atomic = EqbStep(s, b0, K, qb, torch, ws=False)
+    sec_atomic, _graph = time_graph(atomic, torch, args.steps, args.warmup)
+    assert int(atomic.buf.err.item()) == 0 and torch.equal(atomic.b, b_ws)
+    per_k_atomic = time_kernels(atomic, torch, max(5, args.steps))
+    del _graph, atomic
     ceil = ceilings(torch, s)
 
     bpt = bytes_per_token(E)
@@ -275,6 +297,13 @@ def main():
                      "traffic": measured_traffic(dominant),
                      "algorithmic_bytes_per_launch": dom_bytes},
         "kernels": kernels,
+        "pass2_merge": {"workspace": {"step_us": round(sec * 1e6, 2),
+                                      "pass2_us": kernels["pass2_hist_lo"]["us"],
+                                      "select_lo_us": kernels["select_lo"]["us"]},
+                        "global_atomics": {"step_us": round(sec_atomic * 1e6, 2),
+                                           "pass2_us": round(per_k_atomic["pass2_hist_lo"] * 1e6, 2),
+                                           "select_lo_us": round(per_k_atomic["select_lo"] * 1e6, 2)},
+                        "same_b_next": True},
         "stream_ceilings": ceil,
     }
 

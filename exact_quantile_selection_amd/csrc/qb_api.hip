@@ -264,6 +264,43 @@ QB_API int qb_lei_backward(const float* g, const float* s, const int32_t* load_m
   return hip_status(qbk::launch_lei_bwd(g, s, load_mb, N, E, K, n_mb, eta, bounded, g_out, dlogits, stream), fn);
 }
 
+QB_API int64_t qb_hist_lo_workspace_bytes(int L, int64_t N, int E) {
+  if (L < 1 || N < 1 || !qbk::supported_E(E)) return QB_EINVAL;
+  return int64_t(L) * E * qbk::radix_wg_per_layer(L, N, E) * 256 * 2;
+}
+
+QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E, const int32_t* sel_hi,
+                               void* ws, int64_t ws_bytes, qb_stream_t stream) {
+  const char* fn = "qb_radix_hist_lo_ws";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!alpha || !sel_hi || !ws)
+    return fail(QB_EINVAL, "%s: alpha (float [L][N]), sel_hi (int32 [L=%d][E=%d]) and ws are required", fn, L, E);
+  const int64_t need = qb_hist_lo_workspace_bytes(L, N, E);
+  if (ws_bytes < need)
+    return fail(QB_EINVAL, "%s: ws_bytes=%lld, this shape needs %lld (qb_hist_lo_workspace_bytes)", fn,
+                (long long)ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(QB_EINVAL, "%s: ws must be 16-byte aligned", fn);
+  return hip_status(qbk::launch_radix_hist_lo_ws(s, alpha, L, N, E, sel_hi, static_cast<uint16_t*>(ws), stream), fn);
+}
+
+QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_t* sel_hi, const int32_t* rank_lo,
+                           int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* err,
+                           qb_stream_t stream) {
+  const char* fn = "qb_select_lo_ws";
+  if (L < 1 || N < 1) return fail(QB_EINVAL, "%s: L=%d, N=%lld, expected both >= 1", fn, L, (long long)N);
+  if (!qbk::supported_E(E))
+    return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {16, 32, 64, 128, 256}", fn, E);
+  if (!ws || !sel_hi || !rank_lo || !q_out || !b || !bounds)
+    return fail(QB_EINVAL,
+                "%s: ws, sel_hi, rank_lo (int32 [L=%d][E=%d]), q_out, b (float [L][E]) and bounds (float [L][2]) are required",
+                fn, L, E);
+  if (!aligned16(ws) || (hist_lo && !aligned4(hist_lo)))
+    return fail(QB_EINVAL, "%s: ws must be 16-byte aligned and hist_lo 4-byte aligned", fn);
+  return hip_status(qbk::launch_select_lo_ws(L, E, qbk::radix_wg_per_layer(L, N, E), static_cast<const uint16_t*>(ws),
+                                             sel_hi, rank_lo, hist_lo, key_out, q_out, b, bounds, err, stream),
+                    fn);
+}
+
 QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N, int E,
                             int32_t* hist_hi, qb_stream_t stream) {
   const char* fn = "qb_radix_hist_hi";

@@ -42,10 +42,14 @@ struct RHShape {
   static_assert(QPR <= kWave && (kWave % QPR) == 0, "row split");
 };
 
-template <int E, bool LO>
+// WS: instead of adding its counts into the global histogram with atomics,
+// the workgroup stores them, dense, as its own partial histogram
+// ws[layer][j][g][h] (uint16; at most 65535 rows per workgroup), for a
+// select that sums the partials (no atomics, no zeroing).
+template <int E, bool LO, bool WS>
 __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int wg_per_layer,
-    const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist) {
+    const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist, uint16_t* __restrict__ ws) {
   using S = RHShape<E>;
   __shared__ uint32_t lds_hist[(E / 2) * 256];
   const int tid = threadIdx.x;
@@ -126,7 +130,20 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     count(nb, xb, ab);
   }
   __syncthreads();
-  hist16_flush<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads, g);
+  if constexpr (WS) {
+    constexpr int HDW = (E / 2) * 256;
+    const int G = wg_per_layer;
+    uint16_t* w = ws + int64_t(layer) * E * G * 256;
+    for (int d = tid; d < HDW; d += kRHThreads) {
+      const uint32_t v = lds_hist[d];
+      const int pair = d >> 8;
+      const int h = (d & 255) ^ ((pair >> 1) & 63);
+      w[(int64_t(2 * pair) * G + g) * 256 + h] = uint16_t(v & 0xFFFFu);
+      w[(int64_t(2 * pair + 1) * G + g) * 256 + h] = uint16_t(v >> 16);
+    }
+  } else {
+    hist16_flush<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads, g);
+  }
 }
 
 template <int E>
@@ -134,12 +151,44 @@ static int launch_rh(bool lo, const float* s, const float* alpha, int L, int64_t
                      const int32_t* sel_hi, int32_t* hist, hipStream_t st) {
   const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, QB_RH_MAXROWS);
   if (lo)
-    hipLaunchKernelGGL((k_radix_hist<E, true>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
-                       s, alpha, N, sp.wg_per_layer, sel_hi, hist);
+    hipLaunchKernelGGL((k_radix_hist<E, true, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
+                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr);
   else
-    hipLaunchKernelGGL((k_radix_hist<E, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
-                       s, alpha, N, sp.wg_per_layer, sel_hi, hist);
+    hipLaunchKernelGGL((k_radix_hist<E, false, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
+                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr);
   return int(hipGetLastError());
+}
+
+template <int E>
+static int launch_rh_ws(const float* s, const float* alpha, int L, int64_t N, const int32_t* sel_hi,
+                        uint16_t* ws, hipStream_t st) {
+  const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, QB_RH_MAXROWS);
+  hipLaunchKernelGGL((k_radix_hist<E, true, true>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st, s,
+                     alpha, N, sp.wg_per_layer, sel_hi, nullptr, ws);
+  return int(hipGetLastError());
+}
+
+int radix_wg_per_layer(int L, int64_t N, int E) {
+  switch (E) {
+    case 16: return split_rows(L, N, RHShape<16>::STEP, QB_RH_MAXROWS).wg_per_layer;
+    case 32: return split_rows(L, N, RHShape<32>::STEP, QB_RH_MAXROWS).wg_per_layer;
+    case 64: return split_rows(L, N, RHShape<64>::STEP, QB_RH_MAXROWS).wg_per_layer;
+    case 128: return split_rows(L, N, RHShape<128>::STEP, QB_RH_MAXROWS).wg_per_layer;
+    case 256: return split_rows(L, N, RHShape<256>::STEP, QB_RH_MAXROWS).wg_per_layer;
+  }
+  return 0;
+}
+
+int launch_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E,
+                            const int32_t* sel_hi, uint16_t* ws, hipStream_t st) {
+  switch (E) {
+    case 16: return launch_rh_ws<16>(s, alpha, L, N, sel_hi, ws, st);
+    case 32: return launch_rh_ws<32>(s, alpha, L, N, sel_hi, ws, st);
+    case 64: return launch_rh_ws<64>(s, alpha, L, N, sel_hi, ws, st);
+    case 128: return launch_rh_ws<128>(s, alpha, L, N, sel_hi, ws, st);
+    case 256: return launch_rh_ws<256>(s, alpha, L, N, sel_hi, ws, st);
+  }
+  return int(hipErrorInvalidValue);
 }
 
 int launch_radix_hist(bool lo, const float* s, const float* alpha, int L, int64_t N, int E,

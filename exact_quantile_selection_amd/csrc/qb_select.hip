@@ -228,6 +228,93 @@ __global__ __launch_bounds__(kFullThreads) void k_select_full(int E, int K, cons
   if (key_out) key_out[le + j] = uint16_t(key);
 }
 
+// Low-byte select from per-workgroup partial histograms (the workspace of
+// qb_radix_hist_lo_ws): one workgroup per (expert, layer).  Expert j's G
+// partial rows are contiguous (G x 512 bytes); 32 lanes read one row with
+// 16-byte loads (8 bins each), so the workgroup reads kLoWsRows rows per
+// trip.  The per-thread sums meet in LDS and thread h adds bin h over the
+// row groups: integer sums, so the counts equal those of the atomic path.
+// The summed row optionally goes to hist_lo; then the first bin whose
+// running count reaches rank_lo is the low byte.
+constexpr int kLoWsThreads = 1024;
+constexpr int kLoWsRows = kLoWsThreads / 32;
+__global__ __launch_bounds__(kLoWsThreads) void k_select_lo_ws(int E, int G, const uint16_t* __restrict__ ws,
+                                                               const int32_t* __restrict__ sel_hi,
+                                                               const int32_t* __restrict__ rank_lo,
+                                                               int32_t* __restrict__ hist_lo,
+                                                               uint16_t* __restrict__ key_out,
+                                                               float* __restrict__ q_out,
+                                                               int32_t* __restrict__ err) {
+  __shared__ __align__(16) int32_t s_part[kLoWsRows][256];
+  __shared__ int64_t s_wave[256 / kWave];
+  __shared__ int s_bin;
+  const int j = blockIdx.x, layer = blockIdx.y, t = threadIdx.x;
+  const int64_t le = int64_t(layer) * E;
+  const int c8 = t & 31, r0 = t >> 5;
+  const uint4* rows = reinterpret_cast<const uint4*>(ws + (le + j) * G * 256) + c8;  // row g at rows[32 g]
+  int32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  auto add = [&](const uint4& v) {
+    acc[0] += int32_t(v.x & 0xFFFFu);
+    acc[1] += int32_t(v.x >> 16);
+    acc[2] += int32_t(v.y & 0xFFFFu);
+    acc[3] += int32_t(v.y >> 16);
+    acc[4] += int32_t(v.z & 0xFFFFu);
+    acc[5] += int32_t(v.z >> 16);
+    acc[6] += int32_t(v.w & 0xFFFFu);
+    acc[7] += int32_t(v.w >> 16);
+  };
+  int g = r0;
+  for (; g + 3 * kLoWsRows < G; g += 4 * kLoWsRows) {
+    const uint4 v0 = rows[int64_t(g) * 32];
+    const uint4 v1 = rows[int64_t(g + kLoWsRows) * 32];
+    const uint4 v2 = rows[int64_t(g + 2 * kLoWsRows) * 32];
+    const uint4 v3 = rows[int64_t(g + 3 * kLoWsRows) * 32];
+    add(v0);
+    add(v1);
+    add(v2);
+    add(v3);
+  }
+  for (; g < G; g += kLoWsRows) add(rows[int64_t(g) * 32]);
+  int4* dst = reinterpret_cast<int4*>(&s_part[r0][8 * c8]);
+  dst[0] = make_int4(acc[0], acc[1], acc[2], acc[3]);
+  dst[1] = make_int4(acc[4], acc[5], acc[6], acc[7]);
+  if (t == 0) s_bin = -1;
+  __syncthreads();
+  // Threads 0..255 (waves 0..3) own one bin each from here on; the other
+  // waves only meet the barriers.
+  const int h = t;
+  const int lane = t & (kWave - 1), wave = t / kWave;
+  int32_t c = 0;
+  int64_t incl = 0;
+  if (h < 256) {
+#pragma unroll 8
+    for (int r = 0; r < kLoWsRows; ++r) c += s_part[r][h];
+    if (hist_lo) hist_lo[(le + j) * 256 + h] = c;
+    // inclusive prefix over the 256 bins: wave scans, then wave offsets
+    incl = wave_incl_scan(int64_t(c), lane);
+    if (lane == kWave - 1) s_wave[wave] = incl;
+  }
+  __syncthreads();
+  const int hi_byte = sel_hi[le + j];
+  const int64_t rank = rank_lo[le + j];
+  const bool ok = hi_byte >= 0 && hi_byte <= 255 && rank >= 1;
+  if (h < 256) {
+    for (int w = 0; w < wave; ++w) incl += s_wave[w];
+    if (ok && c > 0 && incl >= rank && incl - c < rank) s_bin = h;  // exactly one bin
+  }
+  __syncthreads();
+  if (h != 0) return;
+  const int bin = s_bin;
+  if (!ok || bin < 0) {
+    q_out[le + j] = __builtin_nanf("");
+    if (err) atomicOr(err, QB_ERR_RANK);
+    return;
+  }
+  const uint32_t key = (uint32_t(hi_byte) << 8) | uint32_t(bin);
+  q_out[le + j] = __builtin_bit_cast(float, unkey16(key) << 16);
+  if (key_out) key_out[le + j] = uint16_t(key);
+}
+
 // b_next = q - mean(q) (float64 sum in expert order on one thread, one
 // rounding to fp32), written over b; bounds = [min - 1, max + 1] (min and
 // max as a parallel reduction: any order gives the same values up to the
@@ -324,6 +411,16 @@ int launch_select(int phase, int L, int E, int K, const int32_t* hist, int n_bin
                        rank_lo, key_out, q_out, bounds, err);
   int rc = int(hipGetLastError());
   if (rc != int(hipSuccess) || phase == QB_SELECT_HI) return rc;
+  hipLaunchKernelGGL(k_finalize, dim3(unsigned(L)), dim3(kFinThreads), 0, st, E, q_out, b, bounds, err);
+  return int(hipGetLastError());
+}
+
+int launch_select_lo_ws(int L, int E, int G, const uint16_t* ws, const int32_t* sel_hi, const int32_t* rank_lo,
+                        int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* err,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(k_select_lo_ws, dim3(unsigned(E), unsigned(L)), dim3(kLoWsThreads), 0, st, E, G, ws, sel_hi,
+                     rank_lo, hist_lo, key_out, q_out, err);
+  if (int rc = int(hipGetLastError())) return rc;
   hipLaunchKernelGGL(k_finalize, dim3(unsigned(L)), dim3(kFinThreads), 0, st, E, q_out, b, bounds, err);
   return int(hipGetLastError());
 }

@@ -62,12 +62,16 @@ def lib() -> C.CDLL:
             "qb_allreduce_sum_i32": [vp, i32, i64, vp],
             "qb_margins_full_hist": [vp, vp, i32, i64, i32, i32, vp, vp, vp],
             "qb_lei_backward": [vp, vp, vp, i64, i32, i32, i64, f32, i32, vp, vp, vp],
+            "qb_radix_hist_lo_ws": [vp, vp, i32, i64, i32, vp, vp, i64, vp],
+            "qb_select_lo_ws": [i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "qb_rank_average": [vp, i32, i32, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = C.c_int
+        L.qb_hist_lo_workspace_bytes.argtypes = [i32, i64, i32]
+        L.qb_hist_lo_workspace_bytes.restype = C.c_int64
         L.qb_status_string.argtypes = [C.c_int]
         L.qb_status_string.restype = C.c_char_p
         L.qb_last_error.argtypes = []
@@ -262,6 +266,41 @@ def qb_lei_backward(g, load_mb, K, n_mb, eta, bounded=False, s=None, g_out=None,
         _ptr(dlogits, torch.float32, "dlogits", (N, E), opt=True), _stream(stream)))
 
 
+def qb_hist_lo_workspace_bytes(L, N, E):
+    n = lib().qb_hist_lo_workspace_bytes(L, N, E)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def qb_radix_hist_lo_ws(s, alpha, sel_hi, ws, stream=None):
+    """Pass 2 into per-workgroup partial histograms in ws (uint8 tensor of
+    at least qb_hist_lo_workspace_bytes bytes)."""
+    L, N, E, lead = _lne(s)
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device.type != "cuda":
+        raise ValueError("ws must be a contiguous uint8 GPU tensor")
+    _check(lib().qb_radix_hist_lo_ws(
+        _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
+        _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)), ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def qb_select_lo_ws(N, ws, sel_hi, rank_lo, q_out, b, bounds, hist_lo=None, key_out=None, err=None,
+                    stream=None):
+    if sel_hi.dim() == 1:
+        L, E, lead = 1, sel_hi.shape[0], ()
+    else:
+        L, E = sel_hi.shape
+        lead = (L,)
+    _check(lib().qb_select_lo_ws(
+        L, N, E, ws.data_ptr(), _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)),
+        _ptr(rank_lo, torch.int32, "rank_lo", lead + (E,)),
+        _ptr(hist_lo, torch.int32, "hist_lo", lead + (E, 256), opt=True),
+        _ptr(key_out, torch.uint16, "key_out", lead + (E,), opt=True),
+        _ptr(q_out, torch.float32, "q_out", lead + (E,)), _ptr(b, torch.float32, "b", lead + (E,)),
+        _ptr(bounds, torch.float32, "bounds", lead + (2,)),
+        _ptr(err, torch.int32, "err", (1,), opt=True), _stream(stream)))
+
+
 def qb_allreduce_sum_i32(buf, stream=None):
     """buf int32 [R, ...]: every rank's copy (leading index) becomes the sum
     of all copies, in place."""
@@ -317,6 +356,19 @@ def eqb_update(s, b, K, alpha, buf: EqbBuffers, load=None, stream=None):
     qb_select_update(QB_SELECT_LO, K, buf.hist_lo, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
                      key_out=buf.key, q_out=buf.q, b=b, bounds=buf.bounds, err=buf.err,
                      stream=stream)
+
+
+def eqb_update_ws(s, b, K, alpha, buf: EqbBuffers, ws, load=None, stream=None):
+    """eqb_update with pass 2 merged through the workspace `ws` (see
+    qb_radix_hist_lo_ws): same results; buf.hist_lo receives the summed
+    low-byte histogram.  buf.hist_hi must be zero on entry."""
+    L, N, E, lead = _lne(s)
+    qb_margins_topk(s, b, K, alpha, load=load, hist_hi=buf.hist_hi, stream=stream)
+    qb_select_update(QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                     err=buf.err, stream=stream)
+    qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws, stream=stream)
+    qb_select_lo_ws(N, ws, buf.sel_hi, buf.rank_lo, buf.q, b, buf.bounds, hist_lo=buf.hist_lo,
+                    key_out=buf.key, err=buf.err, stream=stream)
 
 
 def k3_update(s, b, K, alpha, bounds, hist_u, q_out, err=None, stream=None):

@@ -169,6 +169,30 @@ QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist,
                             qb_stream_t stream);
 
 /*
+ * Pass 2 and the low-byte select without global atomics, for one update per
+ * call (no accumulation across calls).  Same results as qb_radix_hist_lo +
+ * qb_select_update(QB_SELECT_LO), bit for bit: every workgroup of pass 2
+ * stores its counts as a dense partial histogram in a caller workspace
+ * (uint16 [L][E][G][256], G = workgroups per layer), and the select sums the
+ * G partials of each bin in workgroup order (integer sums) before the rank
+ * scan.  The EQB paragraph's low-byte histogram, with the merge moved from
+ * global atomics to the select.
+ *   qb_hist_lo_workspace_bytes: bytes the workspace needs for this shape
+ *     (L * E * G * 512; 32 MiB for one 1,048,576 x 256 layer), or a negative
+ *     status.  ws must be 16-byte aligned.
+ *   qb_radix_hist_lo_ws: as qb_radix_hist_lo, writing ws (overwritten).
+ *   qb_select_lo_ws: as qb_select_update(QB_SELECT_LO) from ws; N must be
+ *     the N given to qb_radix_hist_lo_ws; hist_lo (nullable) receives the
+ *     summed histogram (overwritten, not accumulated).
+ */
+QB_API int64_t qb_hist_lo_workspace_bytes(int L, int64_t N, int E);
+QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E, const int32_t* sel_hi,
+                               void* ws, int64_t ws_bytes, qb_stream_t stream);
+QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_t* sel_hi, const int32_t* rank_lo,
+                           int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* err,
+                           qb_stream_t stream);
+
+/*
  * K3 mode binning ("[Dev] Add global-batch quantile balancing", sections
  * "Quantile estimator" and "Implementation"): for the fp32 margin r,
  * bin = clamp(floor(fl32(fl32(r - lo) * fl32(n_bins / fl32(hi - lo)))), 0,

@@ -97,6 +97,19 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
     assert rc == qb.QB_EINVAL and "K=300" in _last(libqb)
     rc = libqb.qb_maxvio(fake, 1, 4, 256, 6, 1024, None, None, None, None)
     assert rc == qb.QB_EINVAL and "maxvio" in _last(libqb)
+    libqb.qb_hist_lo_workspace_bytes.restype = C.c_int64
+    assert libqb.qb_hist_lo_workspace_bytes(1, 1 << 20, 256) > 0
+    assert libqb.qb_hist_lo_workspace_bytes(1, 1 << 20, 48) == qb.QB_EINVAL
+    assert libqb.qb_hist_lo_workspace_bytes(0, 10, 256) == qb.QB_EINVAL
+    rc = libqb.qb_radix_hist_lo_ws(fake, fake, 1, 1024, 256, fake, None, C.c_int64(0), None)
+    assert rc == qb.QB_EINVAL and "ws are required" in _last(libqb)
+    rc = libqb.qb_radix_hist_lo_ws(fake, fake, 1, 1024, 256, fake, fake, C.c_int64(16), None)
+    assert rc == qb.QB_EINVAL and "ws_bytes=16" in _last(libqb)
+    rc = libqb.qb_radix_hist_lo_ws(fake, fake, 1, 1024, 256, fake, fake + 4, C.c_int64(1 << 30), None)
+    assert rc == qb.QB_EINVAL and "16-byte aligned" in _last(libqb)
+    rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 48, fake, fake, fake, None, None, fake, None, None, None,
+                               None)
+    assert rc == qb.QB_EUNSUPPORTED and "E=48" in _last(libqb)
     assert libqb.qb_fill_i32(None, 0, 0, None) == qb.QB_OK  # empty fill is a no-op
     assert libqb.qb_fill_i32(None, 5, 0, None) == qb.QB_EINVAL
     for st in (0, -1, -2, -3):

@@ -1,0 +1,72 @@
+"""GPU checks of the workspace path of pass 2 (per-workgroup partial
+histograms summed in the low-byte select instead of global atomics): the
+whole EQB update is bit-exact against the oracle and equal to the atomic
+path."""
+import numpy as np
+import pytest
+import torch
+
+from exact_quantile_selection_amd import qb, synth
+
+import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qb.lib()
+
+
+def run_ws(s_np, b_np, K):
+    lead = s_np.shape[:-2]
+    L = int(np.prod(lead)) if lead else 1
+    N, E = s_np.shape[-2:]
+    s, b = G.dev(s_np), G.dev(b_np)
+    alpha = torch.empty(lead + (N,), dtype=torch.float32, device=G.DEV)
+    load = torch.zeros(lead + (E,), dtype=torch.int32, device=G.DEV)
+    buf = qb.EqbBuffers(L, E, device=G.DEV, lead=bool(lead))
+    ws = torch.empty(qb.qb_hist_lo_workspace_bytes(L, N, E), dtype=torch.uint8, device=G.DEV)
+    ws.fill_(0xAB)  # stale bytes: the path overwrites, never accumulates
+    qb.eqb_update_ws(s, b, K, alpha, buf, ws, load=load)
+    torch.cuda.synchronize()
+    return dict(alpha=G.host(alpha), hist_hi=G.host(buf.hist_hi), sel_hi=G.host(buf.sel_hi),
+                rank_lo=G.host(buf.rank_lo), hist_lo=G.host(buf.hist_lo), key=G.host(buf.key),
+                q=G.host(buf.q), b_next=G.host(b), bounds=G.host(buf.bounds), err=int(buf.err.item()),
+                load=G.host(load))
+
+
+@pytest.mark.parametrize("N,E,K,quant", [(5000, 256, 6, None), (3333, 64, 4, 16.0), (1, 16, 2, None),
+                                         (777, 32, 7, 8.0), (65536, 128, 3, 64.0), (100, 256, 1, None)])
+def test_ws_update_vs_oracle(O, N, E, K, quant):
+    G.say(f"ws update N={N} E={E} K={K}")
+    s, b, _ = synth.random_case(71, N, E, K, quant=quant)
+    G.compare_eqb(run_ws(s, b, K), O.eqb_layer(s, b, K), tag="ws ")
+
+
+def test_ws_update_three_layers(O):
+    L, N, E, K = 3, 4096, 64, 4
+    G.say("ws update, 3 layers")
+    s = synth.stream_batch(5, N, E, L=L)
+    b = np.random.default_rng(4).uniform(-0.2, 0.2, (L, E)).astype(np.float32)
+    got = run_ws(s, b, K)
+    assert got["err"] == 0
+    for l in range(L):
+        ref = O.eqb_layer(s[l], b[l], K)
+        for k in G.EQB_KEYS + ("load",):
+            G.assert_same(f"layer {l} {k}", got[k][l], ref[k])
+
+
+@pytest.mark.timeout(900)
+def test_ws_update_skewed_full_size(O):
+    """The 1,048,576-token skewed layer: the workspace path equals the
+    atomic path and the oracle."""
+    s, b, K = synth.skew()
+    G.say("ws full size")
+    got = run_ws(s, b, K)
+    atomic = G.run_eqb(s, b, K)
+    for k in G.EQB_KEYS + ("load",):
+        G.assert_same(f"ws vs atomic {k}", got[k], atomic[k])
+    G.compare_eqb(got, O.eqb_layer(s, b, K), tag="ws ")
