@@ -216,8 +216,11 @@ QB_API int qb_fill_i32(int32_t* dst, int64_t count, int32_t value, qb_stream_t s
 
 /*
  * Router forward fused with pass 1, for one layer: logits = hidden . w^T on
- * MFMA (bf16 inputs, fp32 accumulation), s = sigmoid(logits) with the device
- * expf, written to s_out; then exactly qb_margins_topk on s_out (alpha,
+ * MFMA (bf16 inputs, fp32 accumulation), s = 1 / (1 + 2^(-x log2 e)) with
+ * a two-constant (Cody-Waite) split of x log2 e, the hardware exp2 and
+ * reciprocal (within a few ulp of the correctly rounded sigmoid; results
+ * below 2^-126 flush to 0), written to s_out; then exactly qb_margins_topk
+ * on s_out (alpha,
  * optional top-K loads, optional high-byte histogram).  The sigmoid scores
  * are those of "[Dev] Add global-batch quantile balancing", section
  * "Quantile estimator"; the router forward is the one its Validation section
