@@ -1,11 +1,12 @@
 """Benchmark of the exact quantile-balancing (EQB) bias update on one MI355X.
 
 A step is one full EQB layer update of the skewed 1,048,576-token workload
-(E=256, K=6): the in-place histogram reset, pass 1 (alpha + high-byte
-histogram), the high-byte select, pass 2 (low-byte histogram) and the
-low-byte select with the in-place bias update; the bias is restored first
-so every step does identical work.  Inputs are resident in HBM before timing starts.  The step
-is replayed from a HIP graph captured once.
+(E=256, K=6): pass 1 (alpha + high-byte histogram), the high-byte select,
+pass 2 (low-byte partial histograms) and the low-byte select with the
+in-place bias update and the in-place reset of the high-byte histogram; the
+bias is restored first so every step does identical work.  Inputs are
+resident in HBM before timing starts.  The timed steps run back to back from
+one HIP graph that holds all of them.
 
 Printed: one JSON line with the metric (tokens/s per layer), the roofline
 of the dominant kernel (algorithmic bytes / average duration from HIP events
@@ -63,25 +64,28 @@ class EqbStep:
                    if ws else None)
 
     def launches(self):
-        """(name, callable) of the step, in stream order."""
+        """(name, callable) of the step, in stream order.  The workspace
+        step clears the high-byte histogram in its last select (the reset
+        after the update), so it needs no separate clear; the atomic step
+        clears both histograms with a fill kernel first."""
         qb, buf = self.qb, self.buf
-        head = [
-            ("restore_bias", lambda: self.b.copy_(self.b0)),
-            ("reset_hist", lambda: buf.reset()),
+        body = [
             ("pass1_topk_hist_hi", lambda: qb.qb_margins_topk(self.s, self.b, self.K, self.alpha,
                                                               hist_hi=buf.hist_hi)),
             ("select_hi", lambda: qb.qb_select_update(qb.QB_SELECT_HI, self.K, buf.hist_hi,
                                                       sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
                                                       err=buf.err)),
         ]
+        restore = ("restore_bias", lambda: self.b.copy_(self.b0))
         if self.ws is not None:
-            return head + [
+            return [restore] + body + [
                 ("pass2_hist_lo", lambda: qb.qb_radix_hist_lo_ws(self.s, self.alpha, buf.sel_hi, self.ws)),
                 ("select_lo", lambda: qb.qb_select_lo_ws(self.N, self.ws, buf.sel_hi, buf.rank_lo, buf.q,
                                                          self.b, buf.bounds, hist_lo=buf.hist_lo,
-                                                         key_out=buf.key, err=buf.err)),
+                                                         key_out=buf.key, err=buf.err,
+                                                         hist_hi=buf.hist_hi)),
             ]
-        return head + [
+        return [restore, ("reset_hist", lambda: buf.reset())] + body + [
             ("pass2_hist_lo", lambda: qb.qb_radix_hist_lo(self.s, self.alpha, buf.sel_hi, buf.hist_lo)),
             ("select_lo", lambda: qb.qb_select_update(qb.QB_SELECT_LO, self.K, buf.hist_lo,
                                                       sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
@@ -95,7 +99,10 @@ class EqbStep:
 
 
 def time_graph(step, torch, steps, warmup):
-    """Capture the step in a HIP graph; time `steps` replays."""
+    """Run `warmup` steps eagerly, capture `steps` consecutive steps in one
+    HIP graph (as a training step's graph holds its layers' updates back to
+    back), replay it once untimed, then time one replay: exactly `steps`
+    steps between two device synchronizations.  Returns seconds per step."""
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for _ in range(max(1, warmup)):
@@ -103,13 +110,12 @@ def time_graph(step, torch, steps, warmup):
     stream.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        step.run()
-    for _ in range(warmup):
-        g.replay()
+        for _ in range(steps):
+            step.run()
+    g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        g.replay()
+    g.replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps, g
 
@@ -288,7 +294,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "skew: N=1048576 tokens (256 x 4096), E=256, K=6, one layer, EQB",
-                   "N": N, "E": E, "K": K, "L": 1, "launch": "hip_graph",
+                   "N": N, "E": E, "K": K, "L": 1, "launch": f"hip_graph ({args.steps} steps per graph)",
                    "step_algorithmic_bytes": N * bpt["step"],
                    "step_GBps": round(step_gbs, 1),
                    "step_frac_of_peak": round(step_gbs / PEAK_HBM_GBS, 4)},

@@ -284,8 +284,8 @@ QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_
 }
 
 QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_t* sel_hi, const int32_t* rank_lo,
-                           int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* err,
-                           qb_stream_t stream) {
+                           int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
+                           int32_t* hist_hi, int32_t* err, qb_stream_t stream) {
   const char* fn = "qb_select_lo_ws";
   if (L < 1 || N < 1) return fail(QB_EINVAL, "%s: L=%d, N=%lld, expected both >= 1", fn, L, (long long)N);
   if (!qbk::supported_E(E))
@@ -294,10 +294,11 @@ QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_
     return fail(QB_EINVAL,
                 "%s: ws, sel_hi, rank_lo (int32 [L=%d][E=%d]), q_out, b (float [L][E]) and bounds (float [L][2]) are required",
                 fn, L, E);
-  if (!aligned16(ws) || (hist_lo && !aligned4(hist_lo)))
-    return fail(QB_EINVAL, "%s: ws must be 16-byte aligned and hist_lo 4-byte aligned", fn);
+  if (!aligned16(ws) || (hist_lo && !aligned4(hist_lo)) || (hist_hi && !aligned4(hist_hi)))
+    return fail(QB_EINVAL, "%s: ws must be 16-byte aligned, hist_lo and hist_hi 4-byte aligned", fn);
   return hip_status(qbk::launch_select_lo_ws(L, E, qbk::radix_wg_per_layer(L, N, E), static_cast<const uint16_t*>(ws),
-                                             sel_hi, rank_lo, hist_lo, key_out, q_out, b, bounds, err, stream),
+                                             sel_hi, rank_lo, hist_lo, key_out, q_out, b, bounds, hist_hi, err,
+                                             stream),
                     fn);
 }
 

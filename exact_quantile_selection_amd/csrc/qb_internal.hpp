@@ -34,8 +34,8 @@ int radix_wg_per_layer(int L, int64_t N, int E);
 int launch_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E,
                             const int32_t* sel_hi, uint16_t* ws, hipStream_t st);
 int launch_select_lo_ws(int L, int E, int G, const uint16_t* ws, const int32_t* sel_hi, const int32_t* rank_lo,
-                        int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* err,
-                        hipStream_t st);
+                        int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
+                        int32_t* hist_hi, int32_t* err, hipStream_t st);
 int launch_lei_bwd(const float* g, const float* s, const int32_t* load_mb, int64_t N, int E, int K,
                    int64_t n_mb, float eta, int bounded, float* g_out, float* dlogits, hipStream_t st);
 int launch_allreduce_sum(int32_t* buf, int R, int64_t M, hipStream_t st);

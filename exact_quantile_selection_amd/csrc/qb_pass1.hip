@@ -41,10 +41,13 @@
 
 namespace qbk {
 
-// 16 waves per workgroup (<= 128 VGPRs each); the load-counting variant
-// keeps more state per lane and runs 8 waves (<= 256 VGPRs each).
+#ifndef QB_P1_WAVES
+#define QB_P1_WAVES 16
+#endif
+// QB_P1_WAVES waves per workgroup; the load-counting variant keeps more
+// state per lane and runs 8 waves (<= 256 VGPRs each).
 template <bool LOAD>
-constexpr int p1_waves() { return LOAD ? 8 : 16; }
+constexpr int p1_waves() { return LOAD ? 8 : QB_P1_WAVES; }
 
 template <int E>
 struct P1Shape {

@@ -29,7 +29,10 @@
 
 namespace qbk {
 
-constexpr int kRHWaves = 16;
+#ifndef QB_RH_WAVES
+#define QB_RH_WAVES 16
+#endif
+constexpr int kRHWaves = QB_RH_WAVES;
 constexpr int kRHThreads = kRHWaves * kWave;
 constexpr int kRHUnroll = 8;  // rows per lane per register set
 
@@ -75,17 +78,24 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     for (int c = 0; c < 4; ++c) {
       const int v = sel_hi[int64_t(layer) * E + 4 * quad + c];
       sel[c] = (v >= 0 && v < 256) ? uint32_t(v) : 0x100u;
+      // Materialise the value here: first used inside the row loop, the
+      // load would otherwise be waited for there with a full vmcnt(0) on
+      // every trip, draining the rows in flight.
+      asm volatile("" : "+v"(sel[c]));
     }
   }
   __syncthreads();
 
-  auto load = [&](int64_t base, float4 (&x)[kRHUnroll], float (&a)[kRHUnroll]) {
+  // Full trips (every row < N): addresses from the wave-uniform row base
+  // with 32-bit lane offsets, no clamps and no per-row tests, so the loop
+  // body is straight-line and each set's loads are waited for one by one.
+  auto load_full = [&](int64_t base, float4 (&x)[kRHUnroll], float (&a)[kRHUnroll]) {
+    const float* sw = s + base * E;
+    const float* aw = alpha + base;
 #pragma unroll
     for (int u = 0; u < kRHUnroll; ++u) {
-      int64_t row = base + u * S::RPI + rsub;
-      row = row < N ? row : N - 1;
-      x[u] = ld4(s + row * E + 4 * quad);
-      a[u] = alpha[row];
+      x[u] = ld4(sw + uint32_t((u * S::RPI + rsub) * E + 4 * quad));
+      a[u] = aw[u * S::RPI + rsub];
     }
   };
   auto count1 = [&](const float4& x, float a) {
@@ -103,43 +113,88 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
       if ((k23 >> 24) == sel[3]) atomicAdd(rowp + 256 + ((l23 >> 16) & 0xFFu), 0x10000u);
     }
   };
-  auto count = [&](int64_t base, const float4 (&x)[kRHUnroll], const float (&a)[kRHUnroll]) {
-    if (base + S::RPW <= N) {
-#pragma unroll
-      for (int u = 0; u < kRHUnroll; ++u) count1(x[u], a[u]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < kRHUnroll; ++u)
-        if (base + u * S::RPI + rsub < N) count1(x[u], a[u]);
-    }
-  };
   // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
   // Two register sets: the next trip's rows are in flight while this trip's
-  // keys are counted.
+  // keys are counted.  The next set is always loaded -- after its last full
+  // trip a wave re-reads that trip's (cached) rows -- so the loop has one
+  // path and the compiler waits for each load alone instead of for both
+  // sets.  Only a wave's last trip can be partial; it runs after the loop.
   const int64_t stride = int64_t(wg_per_layer) * S::STEP;
   int64_t base = int64_t(g) * S::STEP + int64_t(wave) * S::RPW;
   float4 xa[kRHUnroll], xb[kRHUnroll];
   float aa[kRHUnroll], ab[kRHUnroll];
-  if (base < N) load(base, xa, aa);
-  for (; base < N; base += 2 * stride) {
-    const int64_t nb = base + stride;
-    if (nb < N) load(nb, xb, ab);
-    count(base, xa, aa);
-    if (nb >= N) break;
-    if (nb + stride < N) load(nb + stride, xa, aa);
-    count(nb, xb, ab);
+  if (base + S::RPW <= N) {
+    load_full(base, xa, aa);
+    for (;;) {
+      const int64_t nb = base + stride;
+      const bool nfull = nb + S::RPW <= N;
+      load_full(nfull ? nb : base, xb, ab);
+#pragma unroll
+      for (int u = 0; u < kRHUnroll; ++u) count1(xa[u], aa[u]);
+      base = nb;
+      if (!nfull) break;
+      const int64_t nb2 = base + stride;
+      const bool nfull2 = nb2 + S::RPW <= N;
+      load_full(nfull2 ? nb2 : base, xa, aa);
+#pragma unroll
+      for (int u = 0; u < kRHUnroll; ++u) count1(xb[u], ab[u]);
+      base = nb2;
+      if (!nfull2) break;
+    }
+  }
+  if (base < N) {
+    // the partial trip: rows clamped to N - 1 for the loads, not counted
+#pragma unroll
+    for (int u = 0; u < kRHUnroll; ++u) {
+      int64_t row = base + u * S::RPI + rsub;
+      row = row < N ? row : N - 1;
+      xa[u] = ld4(s + row * E + 4 * quad);
+      aa[u] = alpha[row];
+    }
+#pragma unroll
+    for (int u = 0; u < kRHUnroll; ++u)
+      if (base + u * S::RPI + rsub < N) count1(xa[u], aa[u]);
   }
   __syncthreads();
   if constexpr (WS) {
-    constexpr int HDW = (E / 2) * 256;
+    // Item i covers bins 8k .. 8k+7 (k = i & 31) of dword row pair = i >> 5
+    // (experts 2 pair and 2 pair + 1).  Its eight counters are one aligned
+    // 8-dword block of LDS, permuted by the row's bank swizzle
+    // (quad = pair >> 1: c[m] holds bin 8k + (m ^ (quad & 7))), and leave
+    // as one 16-byte store per expert.  The 64 items of a wave are the two
+    // rows of one quad, so the permutation is the same across the wave.
     const int G = wg_per_layer;
     uint16_t* w = ws + int64_t(layer) * E * G * 256;
-    for (int d = tid; d < HDW; d += kRHThreads) {
-      const uint32_t v = lds_hist[d];
-      const int pair = d >> 8;
-      const int h = (d & 255) ^ ((pair >> 1) & 63);
-      w[(int64_t(2 * pair) * G + g) * 256 + h] = uint16_t(v & 0xFFFFu);
-      w[(int64_t(2 * pair + 1) * G + g) * 256 + h] = uint16_t(v >> 16);
+    for (int i = tid; i < (E / 2) * 32; i += kRHThreads) {
+      const int pair = i >> 5, k = i & 31;
+      const int sw = (pair >> 1) & 63;
+      const uint4* src = reinterpret_cast<const uint4*>(lds_hist + pair * 256 + ((8 * k) ^ (sw & 0xF8)));
+      const uint4 v0 = src[0], v1 = src[1];
+      uint32_t c[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      // c[m] <- c[m ^ (sw & 7)], one XOR bit at a time
+#pragma unroll
+      for (int bit = 4; bit >= 1; bit >>= 1) {
+        if (sw & bit) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            if ((m & bit) == 0) {
+              const uint32_t t = c[m];
+              c[m] = c[m | bit];
+              c[m | bit] = t;
+            }
+        }
+      }
+      uint4 lo, hi;  // expert 2 pair: low halves; expert 2 pair + 1: high halves
+      lo.x = (c[0] & 0xFFFFu) | (c[1] << 16);
+      lo.y = (c[2] & 0xFFFFu) | (c[3] << 16);
+      lo.z = (c[4] & 0xFFFFu) | (c[5] << 16);
+      lo.w = (c[6] & 0xFFFFu) | (c[7] << 16);
+      hi.x = (c[0] >> 16) | (c[1] & 0xFFFF0000u);
+      hi.y = (c[2] >> 16) | (c[3] & 0xFFFF0000u);
+      hi.z = (c[4] >> 16) | (c[5] & 0xFFFF0000u);
+      hi.w = (c[6] >> 16) | (c[7] & 0xFFFF0000u);
+      *reinterpret_cast<uint4*>(w + (int64_t(2 * pair) * G + g) * 256 + 8 * k) = lo;
+      *reinterpret_cast<uint4*>(w + (int64_t(2 * pair + 1) * G + g) * 256 + 8 * k) = hi;
     }
   } else {
     hist16_flush<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads, g);

@@ -228,6 +228,85 @@ __global__ __launch_bounds__(kFullThreads) void k_select_full(int E, int K, cons
   if (key_out) key_out[le + j] = uint16_t(key);
 }
 
+// b_next = q - mean(q) (float64 sum in expert order on one thread, one
+// rounding to fp32), written over b; bounds = [min - 1, max + 1] (min and
+// max as a parallel reduction: any order gives the same values up to the
+// sign of a zero, which the -1 / +1 removes).  A layer with a NaN quantile
+// (failed rank search) keeps its b and bounds.  Run by the first
+// kFinThreads threads of a workgroup for one layer (q, b: that layer's E
+// entries; bounds: its pair); every thread of the workgroup calls it.
+__device__ void finalize_layer(int E, const float* q, float* b, float* bounds, int32_t* err, int tid) {
+  __shared__ __align__(16) float sq[kFinThreads];
+  __shared__ double s_mean;
+  __shared__ int s_bad;
+  __shared__ float s_min[kFinThreads / kWave], s_max[kFinThreads / kWave];
+  const int lane = tid & (kWave - 1);
+  const bool mine = tid < kFinThreads;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (tid < E) {
+    const float v = q[tid];
+    sq[tid] = v;
+    if (v != v) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0 && err) atomicOr(err, QB_ERR_RANK);
+    return;
+  }
+  if (tid == 0) {
+    // E is a multiple of 4; vector LDS reads keep the in-order float64 chain
+    // from waiting on one LDS round trip per term.
+    double sum = 0.0;
+    const float4* q4 = reinterpret_cast<const float4*>(sq);
+#pragma unroll 8
+    for (int k = 0; k < E / 4; ++k) {
+      const float4 v = q4[k];
+      sum += double(v.x);
+      sum += double(v.y);
+      sum += double(v.z);
+      sum += double(v.w);
+    }
+    s_mean = sum / double(E);
+  }
+  __syncthreads();
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  if (tid < E) {
+    const float bn = float(double(sq[tid]) - s_mean);
+    b[tid] = bn;
+    mn = bn;
+    mx = bn;
+  }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, d));
+    mx = fmaxf(mx, __shfl_xor(mx, d));
+  }
+  if (mine && lane == 0) {
+    s_min[tid / kWave] = mn;
+    s_max[tid / kWave] = mx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kFinThreads / kWave; ++w) {
+      mn = fminf(mn, s_min[w]);
+      mx = fmaxf(mx, s_max[w]);
+    }
+    bounds[0] = mn - 1.0f;
+    bounds[1] = mx + 1.0f;
+  }
+}
+
+// One workgroup per layer.
+__global__ __launch_bounds__(kFinThreads) void k_finalize(int E, const float* __restrict__ q,
+                                                          float* __restrict__ b,
+                                                          float* __restrict__ bounds,
+                                                          int32_t* __restrict__ err) {
+  const int layer = blockIdx.x;
+  const int64_t le = int64_t(layer) * E;
+  finalize_layer(E, q + le, b + le, bounds + 2 * layer, err, threadIdx.x);
+}
+
 // Low-byte select from per-workgroup partial histograms (the workspace of
 // qb_radix_hist_lo_ws): one workgroup per (expert, layer).  Expert j's G
 // partial rows are contiguous (G x 512 bytes); 32 lanes read one row with
@@ -244,6 +323,7 @@ __global__ __launch_bounds__(kLoWsThreads) void k_select_lo_ws(int E, int G, con
                                                                int32_t* __restrict__ hist_lo,
                                                                uint16_t* __restrict__ key_out,
                                                                float* __restrict__ q_out,
+                                                               int32_t* __restrict__ hist_hi,
                                                                int32_t* __restrict__ err) {
   __shared__ __align__(16) int32_t s_part[kLoWsRows][256];
   __shared__ int64_t s_wave[256 / kWave];
@@ -302,6 +382,9 @@ __global__ __launch_bounds__(kLoWsThreads) void k_select_lo_ws(int E, int G, con
     for (int w = 0; w < wave; ++w) incl += s_wave[w];
     if (ok && c > 0 && incl >= rank && incl - c < rank) s_bin = h;  // exactly one bin
   }
+  // The high-byte histogram of this update has been read (select HI ran
+  // before pass 2): clear expert j's row in place for the next update.
+  if (hist_hi && h < 256) hist_hi[(le + j) * 256 + h] = 0;
   __syncthreads();
   if (h != 0) return;
   const int bin = s_bin;
@@ -313,78 +396,6 @@ __global__ __launch_bounds__(kLoWsThreads) void k_select_lo_ws(int E, int G, con
   const uint32_t key = (uint32_t(hi_byte) << 8) | uint32_t(bin);
   q_out[le + j] = __builtin_bit_cast(float, unkey16(key) << 16);
   if (key_out) key_out[le + j] = uint16_t(key);
-}
-
-// b_next = q - mean(q) (float64 sum in expert order on one thread, one
-// rounding to fp32), written over b; bounds = [min - 1, max + 1] (min and
-// max as a parallel reduction: any order gives the same values up to the
-// sign of a zero, which the -1 / +1 removes).  A layer with a NaN quantile
-// (failed rank search) keeps its b and bounds.  One workgroup per layer.
-__global__ __launch_bounds__(kFinThreads) void k_finalize(int E, const float* __restrict__ q,
-                                                          float* __restrict__ b,
-                                                          float* __restrict__ bounds,
-                                                          int32_t* __restrict__ err) {
-  __shared__ __align__(16) float sq[kFinThreads];
-  __shared__ double s_mean;
-  __shared__ int s_bad;
-  __shared__ float s_min[kFinThreads / kWave], s_max[kFinThreads / kWave];
-  const int layer = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int64_t le = int64_t(layer) * E;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  if (tid < E) {
-    const float v = q[le + tid];
-    sq[tid] = v;
-    if (v != v) atomicOr(&s_bad, 1);
-  }
-  __syncthreads();
-  if (s_bad) {
-    if (tid == 0 && err) atomicOr(err, QB_ERR_RANK);
-    return;
-  }
-  if (tid == 0) {
-    // E is a multiple of 4; vector LDS reads keep the in-order float64 chain
-    // from waiting on one LDS round trip per term.
-    double sum = 0.0;
-    const float4* q4 = reinterpret_cast<const float4*>(sq);
-#pragma unroll 8
-    for (int k = 0; k < E / 4; ++k) {
-      const float4 v = q4[k];
-      sum += double(v.x);
-      sum += double(v.y);
-      sum += double(v.z);
-      sum += double(v.w);
-    }
-    s_mean = sum / double(E);
-  }
-  __syncthreads();
-  float mn = __builtin_inff(), mx = -__builtin_inff();
-  if (tid < E) {
-    const float bn = float(double(sq[tid]) - s_mean);
-    b[le + tid] = bn;
-    mn = bn;
-    mx = bn;
-  }
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, d));
-    mx = fmaxf(mx, __shfl_xor(mx, d));
-  }
-  if (lane == 0) {
-    s_min[tid / kWave] = mn;
-    s_max[tid / kWave] = mx;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < kFinThreads / kWave; ++w) {
-      mn = fminf(mn, s_min[w]);
-      mx = fmaxf(mx, s_max[w]);
-    }
-    bounds[2 * layer] = mn - 1.0f;
-    bounds[2 * layer + 1] = mx + 1.0f;
-  }
 }
 
 int launch_select(int phase, int L, int E, int K, const int32_t* hist, int n_bins,
@@ -416,10 +427,10 @@ int launch_select(int phase, int L, int E, int K, const int32_t* hist, int n_bin
 }
 
 int launch_select_lo_ws(int L, int E, int G, const uint16_t* ws, const int32_t* sel_hi, const int32_t* rank_lo,
-                        int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* err,
-                        hipStream_t st) {
+                        int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
+                        int32_t* hist_hi, int32_t* err, hipStream_t st) {
   hipLaunchKernelGGL(k_select_lo_ws, dim3(unsigned(E), unsigned(L)), dim3(kLoWsThreads), 0, st, E, G, ws, sel_hi,
-                     rank_lo, hist_lo, key_out, q_out, err);
+                     rank_lo, hist_lo, key_out, q_out, hist_hi, err);
   if (int rc = int(hipGetLastError())) return rc;
   hipLaunchKernelGGL(k_finalize, dim3(unsigned(L)), dim3(kFinThreads), 0, st, E, q_out, b, bounds, err);
   return int(hipGetLastError());

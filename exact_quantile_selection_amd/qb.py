@@ -63,7 +63,7 @@ def lib() -> C.CDLL:
             "qb_margins_full_hist": [vp, vp, i32, i64, i32, i32, vp, vp, vp],
             "qb_lei_backward": [vp, vp, vp, i64, i32, i32, i64, f32, i32, vp, vp, vp],
             "qb_radix_hist_lo_ws": [vp, vp, i32, i64, i32, vp, vp, i64, vp],
-            "qb_select_lo_ws": [i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "qb_select_lo_ws": [i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "qb_rank_average": [vp, i32, i32, vp, vp, vp],
         }
         for name, args in sig.items():
@@ -285,7 +285,9 @@ def qb_radix_hist_lo_ws(s, alpha, sel_hi, ws, stream=None):
 
 
 def qb_select_lo_ws(N, ws, sel_hi, rank_lo, q_out, b, bounds, hist_lo=None, key_out=None, err=None,
-                    stream=None):
+                    hist_hi=None, stream=None):
+    """Low-byte select from the workspace of qb_radix_hist_lo_ws, with the
+    in-place bias / bounds update; hist_hi (optional) is zeroed in place."""
     if sel_hi.dim() == 1:
         L, E, lead = 1, sel_hi.shape[0], ()
     else:
@@ -298,6 +300,7 @@ def qb_select_lo_ws(N, ws, sel_hi, rank_lo, q_out, b, bounds, hist_lo=None, key_
         _ptr(key_out, torch.uint16, "key_out", lead + (E,), opt=True),
         _ptr(q_out, torch.float32, "q_out", lead + (E,)), _ptr(b, torch.float32, "b", lead + (E,)),
         _ptr(bounds, torch.float32, "bounds", lead + (2,)),
+        _ptr(hist_hi, torch.int32, "hist_hi", lead + (E, 256), opt=True),
         _ptr(err, torch.int32, "err", (1,), opt=True), _stream(stream)))
 
 
@@ -358,17 +361,19 @@ def eqb_update(s, b, K, alpha, buf: EqbBuffers, load=None, stream=None):
                      stream=stream)
 
 
-def eqb_update_ws(s, b, K, alpha, buf: EqbBuffers, ws, load=None, stream=None):
+def eqb_update_ws(s, b, K, alpha, buf: EqbBuffers, ws, load=None, reset_hist_hi=False, stream=None):
     """eqb_update with pass 2 merged through the workspace `ws` (see
     qb_radix_hist_lo_ws): same results; buf.hist_lo receives the summed
-    low-byte histogram.  buf.hist_hi must be zero on entry."""
+    low-byte histogram.  buf.hist_hi must be zero on entry; with
+    reset_hist_hi it is zero again on return (cleared by the select)."""
     L, N, E, lead = _lne(s)
     qb_margins_topk(s, b, K, alpha, load=load, hist_hi=buf.hist_hi, stream=stream)
     qb_select_update(QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
                      err=buf.err, stream=stream)
     qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws, stream=stream)
     qb_select_lo_ws(N, ws, buf.sel_hi, buf.rank_lo, buf.q, b, buf.bounds, hist_lo=buf.hist_lo,
-                    key_out=buf.key, err=buf.err, stream=stream)
+                    key_out=buf.key, err=buf.err, hist_hi=buf.hist_hi if reset_hist_hi else None,
+                    stream=stream)
 
 
 def k3_update(s, b, K, alpha, bounds, hist_u, q_out, err=None, stream=None):

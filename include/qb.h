@@ -179,18 +179,24 @@ QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist,
  * global atomics to the select.
  *   qb_hist_lo_workspace_bytes: bytes the workspace needs for this shape
  *     (L * E * G * 512; 32 MiB for one 1,048,576 x 256 layer), or a negative
- *     status.  ws must be 16-byte aligned.
+ *     status.  ws must be 16-byte aligned; its contents on entry do not
+ *     matter.
  *   qb_radix_hist_lo_ws: as qb_radix_hist_lo, writing ws (overwritten).
- *   qb_select_lo_ws: as qb_select_update(QB_SELECT_LO) from ws; N must be
- *     the N given to qb_radix_hist_lo_ws; hist_lo (nullable) receives the
- *     summed histogram (overwritten, not accumulated).
+ *   qb_select_lo_ws: as qb_select_update(QB_SELECT_LO) from ws; ws must be
+ *     the workspace the preceding qb_radix_hist_lo_ws call wrote, with the
+ *     same L, N and E.  hist_lo (nullable) receives the summed histogram
+ *     (overwritten, not accumulated).  hist_hi (nullable, int32
+ *     [L][E][256]): the high-byte histogram this update was selected from;
+ *     it is zeroed in place (addresses unchanged) -- the reset that follows
+ *     the bias update in the "Implementation" section -- so the next pass 1
+ *     can accumulate into it without a separate clear.
  */
 QB_API int64_t qb_hist_lo_workspace_bytes(int L, int64_t N, int E);
 QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E, const int32_t* sel_hi,
                                void* ws, int64_t ws_bytes, qb_stream_t stream);
 QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_t* sel_hi, const int32_t* rank_lo,
-                           int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* err,
-                           qb_stream_t stream);
+                           int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
+                           int32_t* hist_hi, int32_t* err, qb_stream_t stream);
 
 /*
  * K3 mode binning ("[Dev] Add global-batch quantile balancing", sections

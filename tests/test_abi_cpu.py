@@ -108,7 +108,7 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
     rc = libqb.qb_radix_hist_lo_ws(fake, fake, 1, 1024, 256, fake, fake + 4, C.c_int64(1 << 30), None)
     assert rc == qb.QB_EINVAL and "16-byte aligned" in _last(libqb)
     rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 48, fake, fake, fake, None, None, fake, None, None, None,
-                               None)
+                               None, None)
     assert rc == qb.QB_EUNSUPPORTED and "E=48" in _last(libqb)
     assert libqb.qb_fill_i32(None, 0, 0, None) == qb.QB_OK  # empty fill is a no-op
     assert libqb.qb_fill_i32(None, 5, 0, None) == qb.QB_EINVAL

@@ -20,7 +20,7 @@ def _gpu():
     qb.lib()
 
 
-def run_ws(s_np, b_np, K):
+def run_ws(s_np, b_np, K, reset=False):
     lead = s_np.shape[:-2]
     L = int(np.prod(lead)) if lead else 1
     N, E = s_np.shape[-2:]
@@ -30,7 +30,7 @@ def run_ws(s_np, b_np, K):
     buf = qb.EqbBuffers(L, E, device=G.DEV, lead=bool(lead))
     ws = torch.empty(qb.qb_hist_lo_workspace_bytes(L, N, E), dtype=torch.uint8, device=G.DEV)
     ws.fill_(0xAB)  # stale bytes: the path overwrites, never accumulates
-    qb.eqb_update_ws(s, b, K, alpha, buf, ws, load=load)
+    qb.eqb_update_ws(s, b, K, alpha, buf, ws, load=load, reset_hist_hi=reset)
     torch.cuda.synchronize()
     return dict(alpha=G.host(alpha), hist_hi=G.host(buf.hist_hi), sel_hi=G.host(buf.sel_hi),
                 rank_lo=G.host(buf.rank_lo), hist_lo=G.host(buf.hist_lo), key=G.host(buf.key),
@@ -70,3 +70,41 @@ def test_ws_update_skewed_full_size(O):
     for k in G.EQB_KEYS + ("load",):
         G.assert_same(f"ws vs atomic {k}", got[k], atomic[k])
     G.compare_eqb(got, O.eqb_layer(s, b, K), tag="ws ")
+
+
+def test_ws_select_resets_hist_hi_and_repeats(O):
+    """With the reset, the select leaves the high-byte histogram zero (same
+    buffer), so a second update from the same bias needs no clear and gives
+    the same results; a repeated select over one workspace gives the same
+    b_next again."""
+    L, N, E, K = 2, 3000, 64, 5
+    G.say("ws reset + repeat")
+    s_np = synth.stream_batch(9, N, E, L=L)
+    b_np = np.random.default_rng(2).uniform(-0.2, 0.2, (L, E)).astype(np.float32)
+    s, b0 = G.dev(s_np), G.dev(b_np)
+    alpha = torch.empty((L, N), dtype=torch.float32, device=G.DEV)
+    buf = qb.EqbBuffers(L, E, device=G.DEV)
+    ws = torch.empty(qb.qb_hist_lo_workspace_bytes(L, N, E), dtype=torch.uint8, device=G.DEV)
+    ws.fill_(0xCD)
+    ptr = buf.hist_hi.data_ptr()
+    outs = []
+    for _ in range(2):
+        b = b0.clone()
+        qb.eqb_update_ws(s, b, K, alpha, buf, ws, reset_hist_hi=True)
+        torch.cuda.synchronize()
+        assert buf.hist_hi.data_ptr() == ptr
+        assert int(buf.hist_hi.abs().sum().item()) == 0, "hist_hi not cleared"
+        assert int(buf.err.item()) == 0
+        outs.append((G.host(b), G.host(buf.bounds), G.host(buf.q), G.host(buf.hist_lo)))
+    for k, (x, y) in enumerate(zip(outs[0], outs[1])):
+        G.assert_same(f"update 1 vs 2 [{k}]", x, y)
+    for l in range(L):
+        ref = O.eqb_layer(s_np[l], b_np[l], K)
+        G.assert_same(f"layer {l} b_next", outs[0][0][l], ref["b_next"])
+        G.assert_same(f"layer {l} bounds", outs[0][1][l], ref["bounds"])
+        G.assert_same(f"layer {l} hist_lo", outs[0][3][l], ref["hist_lo"])
+    # select again over the same workspace: same bias update from the same q
+    b = b0.clone()
+    qb.qb_select_lo_ws(N, ws, buf.sel_hi, buf.rank_lo, buf.q, b, buf.bounds, err=buf.err)
+    torch.cuda.synchronize()
+    G.assert_same("repeated select b_next", G.host(b), outs[0][0])
