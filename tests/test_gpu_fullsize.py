@@ -98,3 +98,44 @@ def test_step_48_layers(O):
                    hist_lo=hl[l], key=key[l], q=G.host(buf.q[l]), b_next=bn[l],
                    bounds=G.host(buf.bounds[l]), err=0)
         G.compare_eqb(got, ref, with_load=False, tag=f"step layer {l} ")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("ws", [False, True])
+def test_tiled_layer_beyond_int32_elements(O, ws):
+    """A layer of 9,437,184 tokens x 256 experts (2.4e9 scores, 9.7 GB:
+    element offsets past 2^31) built by repeating a 4096-row block T = 2304
+    times.  Every expert column is the block's column repeated T times, so
+    its order statistic of rank m = T * m_block (m_block = K * 4096 / E = 96)
+    is the block's order statistic of rank m_block: the oracle run on the
+    block gives the exact expected key, q, b_next and bounds, and the
+    histograms and loads are T times the block's."""
+    P, E, K, T = 4096, 256, 6, 2304
+    N = P * T
+    assert N * E > 2 ** 31 and (K * P) % E == 0
+    blk, b_np, _ = synth.random_case(17, P, E, K, quant=64.0)
+    ref = O.eqb_layer(blk, b_np, K)
+    G.say(f"tiled layer N={N} E={E} ({'workspace' if ws else 'atomic'} pass 2)")
+    s = G.dev(blk).repeat(T, 1)
+    b = G.dev(b_np)
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    load = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+    buf = qb.EqbBuffers(1, E, device=G.DEV, lead=False)
+    if ws:
+        wsb = torch.empty(qb.qb_hist_lo_workspace_bytes(1, N, E), dtype=torch.uint8, device=G.DEV)
+        qb.eqb_update_ws(s, b, K, alpha, buf, wsb, load=load)
+    else:
+        qb.eqb_update(s, b, K, alpha, buf, load=load)
+    torch.cuda.synchronize()
+    assert int(buf.err.item()) == 0
+    del s
+    a = G.host(alpha).reshape(T, P)
+    assert (a == ref["alpha"][None, :]).all(), "alpha differs from the block's in some repeat"
+    G.assert_same("load", G.host(load), T * ref["load"])
+    G.assert_same("hist_hi", G.host(buf.hist_hi), T * ref["hist_hi"])
+    G.assert_same("sel_hi", G.host(buf.sel_hi), ref["sel_hi"])
+    G.assert_same("rank_lo", G.host(buf.rank_lo), T * ref["rank_lo"])
+    G.assert_same("hist_lo", G.host(buf.hist_lo), T * ref["hist_lo"])
+    for k in ("key", "q", "b_next", "bounds"):
+        G.assert_same(k, G.host({"key": buf.key, "q": buf.q, "b_next": b, "bounds": buf.bounds}[k]), ref[k])
+    torch.cuda.empty_cache()
