@@ -82,6 +82,9 @@ RowSplit split_rows(int L, int64_t N, int step, int64_t max_rows) {
 
 namespace {
 
+// Largest K of the top-(K+1) passes (lists of up to 16 per lane).
+constexpr int kMaxK = 15;
+
 thread_local std::string g_last_error;
 
 int fail(int status, const char* fmt, ...) {
@@ -132,7 +135,7 @@ QB_API int qb_margins_topk(const float* s, const float* b, int L, int64_t N, int
   if (!b) return fail(QB_EINVAL, "%s: b is NULL (expected float [L=%d][E=%d])", fn, L, E);
   if (!alpha) return fail(QB_EINVAL, "%s: alpha is NULL (expected float [L=%d][N=%lld])", fn, L, (long long)N);
   if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
-  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (K > kMaxK) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= %d", fn, K, kMaxK);
   if (!aligned4(b) || !aligned4(alpha) || (load && !aligned4(load)))
     return fail(QB_EINVAL, "%s: b, alpha and load must be 4-byte aligned", fn);
   if (hist_hi && !aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
@@ -148,7 +151,7 @@ QB_API int qb_margins_topk_mb(const float* s, const float* b, int L, int64_t N, 
     return fail(QB_EINVAL, "%s: b (float [L=%d][E=%d]), alpha (float [L][N]), load (int32 [L][E]) and load_mb (int32 [L][N/n_mb][E]) are required",
                 fn, L, E);
   if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
-  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (K > kMaxK) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= %d", fn, K, kMaxK);
   if (n_mb < 1 || N % n_mb != 0)
     return fail(QB_EINVAL, "%s: n_mb=%lld must be >= 1 and divide N=%lld", fn, (long long)n_mb, (long long)N);
   if (!aligned4(b) || !aligned4(alpha) || !aligned4(load) || !aligned4(load_mb))
@@ -164,7 +167,7 @@ QB_API int qb_microbatch_loads(const float* s, const float* b, int L, int64_t N,
   if (int rc = check_pass(fn, s, L, N, E)) return rc;
   if (!b) return fail(QB_EINVAL, "%s: b is NULL (expected float [L=%d][E=%d])", fn, L, E);
   if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
-  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (K > kMaxK) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= %d", fn, K, kMaxK);
   if (n_mb < 1 || N % n_mb != 0)
     return fail(QB_EINVAL, "%s: n_mb=%lld must be >= 1 and divide N=%lld", fn, (long long)n_mb,
                 (long long)N);
@@ -226,7 +229,7 @@ QB_API int qb_margins_full_hist(const float* s, const float* b, int L, int64_t N
     return fail(QB_EINVAL, "%s: b (float [L=%d][E=%d]), alpha (float [L][N]) and hist_full (int32 [L][E][65536]) are required",
                 fn, L, E);
   if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
-  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (K > kMaxK) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= %d", fn, K, kMaxK);
   if (!aligned4(b) || !aligned4(alpha) || !aligned16(hist_full))
     return fail(QB_EINVAL, "%s: b and alpha must be 4-byte and hist_full 16-byte aligned", fn);
   int rc;
@@ -427,7 +430,7 @@ QB_API int qb_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N,
   if (E != 32 && E != 64 && E != 128 && E != 256)
     return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {32, 64, 128, 256}", fn, E);
   if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
-  if (K > 7) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= 7", fn, K);
+  if (K > kMaxK) return fail(QB_EUNSUPPORTED, "%s: K=%d, compiled for K <= %d", fn, K, kMaxK);
   if (!aligned16(hidden) || !aligned16(w) || !aligned16(s_out))
     return fail(QB_EINVAL, "%s: hidden, w and s_out must be 16-byte aligned", fn);
   if ((logits_out && !aligned4(logits_out)) || !aligned4(b) || !aligned4(alpha) || (load && !aligned4(load)))

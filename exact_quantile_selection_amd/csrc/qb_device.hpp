@@ -57,8 +57,8 @@ __device__ __forceinline__ void top_insert(float (&t)[P], float v) {
 
 // Compare-exchange for a descending network; positions below PAD hold +inf
 // and never move, so exchanges that touch them are skipped at compile time.
-template <int PAD, int A, int B>
-__device__ __forceinline__ void ce_desc(float (&c)[8]) {
+template <int PAD, int A, int B, int W>
+__device__ __forceinline__ void ce_desc(float (&c)[W]) {
   if constexpr (A >= PAD) {
     const float hi = fmaxf(c[A], c[B]);
     const float lo = fminf(c[A], c[B]);
@@ -67,25 +67,45 @@ __device__ __forceinline__ void ce_desc(float (&c)[8]) {
   }
 }
 
+// One half-cleaner stage of a bitonic merge of width W at distance D:
+// compare-exchange (i, i + D) for every i with bit D clear.
+template <int PAD, int D, int W, int I = 0>
+__device__ __forceinline__ void bitonic_stage(float (&c)[W]) {
+  if constexpr (I < W) {
+    if constexpr ((I & D) == 0) ce_desc<PAD, I, I + D, W>(c);
+    bitonic_stage<PAD, D, W, I + 1>(c);
+  }
+}
+
+// Bitonic merge of width W (a power of two): stages at distances W/2, ...,
+// 1 sort a bitonic sequence into descending order.
+template <int PAD, int W, int D = W / 2>
+__device__ __forceinline__ void bitonic_merge(float (&c)[W]) {
+  if constexpr (D >= 1) {
+    bitonic_stage<PAD, D, W>(c);
+    bitonic_merge<PAD, W, D / 2>(c);
+  }
+}
+
 // Merge this lane's descending list with the partner lane's (DPP control
 // CTRL) into the descending list of the P largest of their union.
-// max(A_k, B_{P-1-k}) is the top-P multiset in bitonic order; a bitonic
-// sorting network of width 8 (front-padded with +inf) restores the order.
+// max(A_k, B_{P-1-k}) is the top-P multiset in bitonic order (decreasing,
+// then increasing); a bitonic merge of width 8 or 16 (front-padded with
+// +inf) restores the order.
 template <int P, int CTRL>
 __device__ __forceinline__ void top_merge(float (&t)[P]) {
-  static_assert(P >= 1 && P <= 8, "list length");
-  constexpr int PAD = 8 - P;
+  static_assert(P >= 1 && P <= 16, "list length");
+  constexpr int W = P <= 8 ? 8 : 16;
+  constexpr int PAD = W - P;
   float pt[P];
 #pragma unroll
   for (int k = 0; k < P; ++k) pt[k] = quad_mov<CTRL>(t[k]);
-  float c[8];
+  float c[W];
 #pragma unroll
   for (int k = 0; k < PAD; ++k) c[k] = __builtin_inff();
 #pragma unroll
   for (int k = 0; k < P; ++k) c[PAD + k] = fmaxf(t[k], pt[P - 1 - k]);
-  ce_desc<PAD, 0, 4>(c); ce_desc<PAD, 1, 5>(c); ce_desc<PAD, 2, 6>(c); ce_desc<PAD, 3, 7>(c);
-  ce_desc<PAD, 0, 2>(c); ce_desc<PAD, 1, 3>(c); ce_desc<PAD, 4, 6>(c); ce_desc<PAD, 5, 7>(c);
-  ce_desc<PAD, 0, 1>(c); ce_desc<PAD, 2, 3>(c); ce_desc<PAD, 4, 5>(c); ce_desc<PAD, 6, 7>(c);
+  bitonic_merge<PAD, W>(c);
 #pragma unroll
   for (int k = 0; k < P; ++k) t[k] = c[PAD + k];
 }

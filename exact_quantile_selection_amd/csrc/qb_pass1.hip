@@ -44,10 +44,11 @@ namespace qbk {
 #ifndef QB_P1_WAVES
 #define QB_P1_WAVES 16
 #endif
-// QB_P1_WAVES waves per workgroup; the load-counting variant keeps more
-// state per lane and runs 8 waves (<= 256 VGPRs each).
-template <bool LOAD>
-constexpr int p1_waves() { return LOAD ? 8 : QB_P1_WAVES; }
+// QB_P1_WAVES waves per workgroup (<= 128 VGPRs each); the load-counting
+// variant and lists longer than 8 keep more state per lane and run 8 waves
+// (<= 256 VGPRs each).
+template <bool LOAD, int P>
+constexpr int p1_waves() { return (LOAD || P > 8) ? 8 : QB_P1_WAVES; }
 
 template <int E>
 struct P1Shape {
@@ -238,12 +239,12 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
 }
 
 template <int E, int P, int HM, bool LOAD>
-__global__ __launch_bounds__(p1_waves<LOAD>() * kWave) void k_margins_topk(
+__global__ __launch_bounds__((p1_waves<LOAD, P>() * kWave)) void k_margins_topk(
     const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int bdiv, int K,
     float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi,
     int32_t* __restrict__ load_mb, int64_t n_mb) {
   using S = P1Shape<E>;
-  constexpr int kWaves = p1_waves<LOAD>();
+  constexpr int kWaves = p1_waves<LOAD, P>();
   constexpr int kThreads = kWaves * kWave;
   __shared__ uint32_t lds_hist[HM == 1 ? S::HDW : 4];
   __shared__ float lds_b[E];
@@ -292,8 +293,8 @@ template <int E, int P, int HM, bool LOAD>
 static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb = nullptr,
                        int64_t n_mb = 1) {
-  constexpr int kThreads = p1_waves<LOAD>() * kWave;
-  const RowSplit sp = split_rows(L, N, p1_waves<LOAD>() * P1Shape<E>::RPW, QB_P1_MAXROWS);
+  constexpr int kThreads = p1_waves<LOAD, P>() * kWave;
+  const RowSplit sp = split_rows(L, N, p1_waves<LOAD, P>() * P1Shape<E>::RPW, QB_P1_MAXROWS);
   hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD>), dim3(unsigned(sp.blocks)), dim3(kThreads),
                      0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi, load_mb, n_mb);
   return int(hipGetLastError());
@@ -309,32 +310,25 @@ static int launch_p1(const float* s, const float* b, int L, int bdiv, int64_t N,
   return launch_p1_v<E, P, 0, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
 }
 
-template <int E>
+// List length P = K + 1, 2 .. kMaxList (K <= 15), dispatched at run time.
+constexpr int kMaxList = 16;
+
+template <int E, int P = 2>
 static int launch_p1_k(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb, int64_t n_mb) {
-  switch (K + 1) {
-    case 2: return launch_p1<E, 2>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
-    case 3: return launch_p1<E, 3>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
-    case 4: return launch_p1<E, 4>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
-    case 5: return launch_p1<E, 5>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
-    case 6: return launch_p1<E, 6>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
-    case 7: return launch_p1<E, 7>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
-    case 8: return launch_p1<E, 8>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+  if constexpr (P <= kMaxList) {
+    if (K + 1 == P) return launch_p1<E, P>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    return launch_p1_k<E, P + 1>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
   }
   return int(hipErrorInvalidValue);
 }
 
-template <int E>
+template <int E, int P = 2>
 static int launch_full_k(const float* s, const float* b, int L, int64_t N, int K, float* alpha,
                          int32_t* hist_full, hipStream_t st) {
-  switch (K + 1) {
-    case 2: return launch_p1_v<E, 2, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
-    case 3: return launch_p1_v<E, 3, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
-    case 4: return launch_p1_v<E, 4, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
-    case 5: return launch_p1_v<E, 5, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
-    case 6: return launch_p1_v<E, 6, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
-    case 7: return launch_p1_v<E, 7, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
-    case 8: return launch_p1_v<E, 8, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+  if constexpr (P <= kMaxList) {
+    if (K + 1 == P) return launch_p1_v<E, P, 2, false>(s, b, L, 1, N, K, alpha, nullptr, hist_full, st);
+    return launch_full_k<E, P + 1>(s, b, L, N, K, alpha, hist_full, st);
   }
   return int(hipErrorInvalidValue);
 }

@@ -24,7 +24,7 @@ QB_SELECT_HI, QB_SELECT_LO, QB_SELECT_UNIFORM, QB_SELECT_FULL = 0, 1, 2, 3
 QB_ERR_ROW_TOTALS, QB_ERR_EMPTY, QB_ERR_RANK = 1, 2, 4
 
 SUPPORTED_E = (16, 32, 64, 128, 256)
-MAX_K = 7
+MAX_K = 15
 
 _lib = None
 

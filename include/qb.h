@@ -44,7 +44,7 @@
  *     addresses never change.
  *   - Scores are sigmoid outputs: finite, >= +0.  Bias values are finite.
  *     NaN/Inf inputs give unspecified (but memory-safe) results.
- *   - Supported shapes: E in {16, 32, 64, 128, 256}; 1 <= K <= 7 and K < E;
+ *   - Supported shapes: E in {16, 32, 64, 128, 256}; 1 <= K <= 15 and K < E;
  *     1 <= N < 2^31; L >= 1; n_bins in [1, 2048].
  *   - Return value: QB_OK, or a negative status; on error nothing is launched.
  *     qb_status_string() names a status; qb_last_error() gives the detailed
@@ -236,7 +236,7 @@ QB_API int qb_fill_i32(int32_t* dst, int64_t count, int32_t value, qb_stream_t s
  *   b       float [E]; s_out float [N][E] (16-byte aligned);
  *   logits_out nullable float [N][E]; alpha float [N]; load nullable int32 [E];
  *   hist_hi nullable int32 [E][256] (8-byte aligned).
- *   E in {32, 64, 128, 256}; 1 <= K <= 7.
+ *   E in {32, 64, 128, 256}; 1 <= K <= 15.
  */
 QB_API int qb_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E,
                            int K, const float* b, float* s_out, float* logits_out, float* alpha,

@@ -58,8 +58,8 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
     assert rc == qb.QB_EINVAL and "s is NULL" in _last(libqb)
     rc = libqb.qb_margins_topk(fake, fake, 1, 1024, 48, 6, fake, None, None, None)
     assert rc == qb.QB_EUNSUPPORTED and "E=48" in _last(libqb)
-    rc = libqb.qb_margins_topk(fake, fake, 1, 1024, 256, 8, fake, None, None, None)
-    assert rc == qb.QB_EUNSUPPORTED and "K=8" in _last(libqb)
+    rc = libqb.qb_margins_topk(fake, fake, 1, 1024, 256, 16, fake, None, None, None)
+    assert rc == qb.QB_EUNSUPPORTED and "K=16" in _last(libqb) and "K <= 15" in _last(libqb)
     rc = libqb.qb_margins_topk(fake, fake, 1, 1024, 16, 16, fake, None, None, None)
     assert rc == qb.QB_EINVAL and "K=16" in _last(libqb)
     rc = libqb.qb_margins_topk(fake + 4, fake, 1, 1024, 256, 6, fake, None, None, None)

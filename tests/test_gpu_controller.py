@@ -39,7 +39,7 @@ def test_maxvio_vs_oracle(O, L, C, E, K, n):
 
 @pytest.mark.parametrize("N,E,K,n_mb,quant", [(4096, 256, 6, 512, None), (6000, 64, 4, 1000, 8.0),
                                              (2048, 16, 2, 64, None), (3072, 128, 7, 3072, 16.0),
-                                             (1024, 32, 3, 1, None)])
+                                             (1024, 32, 3, 1, None), (4096, 256, 8, 1024, 64.0)])
 def test_microbatch_loads_vs_oracle(O, N, E, K, n_mb, quant):
     G.say(f"microbatch loads N={N} E={E} K={K} n_mb={n_mb}")
     s, b, _ = synth.random_case(21, N, E, K, quant=quant)
@@ -138,7 +138,8 @@ def test_closed_loop_full_size(O):
 
 
 @pytest.mark.parametrize("N,E,K,n_mb,quant", [(8192, 256, 6, 1024, None), (6000, 64, 4, 1000, 8.0),
-                                             (2048, 16, 2, 2048, None), (4096, 128, 7, 128, 16.0)])
+                                             (2048, 16, 2, 2048, None), (4096, 128, 7, 128, 16.0),
+                                             (3000, 16, 13, 1000, None)])
 def test_fused_pass1_microbatch_loads(O, N, E, K, n_mb, quant):
     """qb_margins_topk_mb: alpha, global loads, per-microbatch loads and the
     high-byte histogram from one read of the scores."""

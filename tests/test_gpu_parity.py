@@ -39,6 +39,9 @@ SWEEP = [
     (3, 128, 2, None), (999, 128, 6, 32.0), (4100, 128, 7, None),
     (1, 256, 6, None), (17, 256, 6, 64.0), (4097, 256, 6, None), (6000, 256, 1, 4.0),
     (2500, 256, 7, 64.0), (1500, 256, 3, None),
+    # top-(K+1) lists longer than 8 (K = 8 for top-8 routers, up to K = 15)
+    (3000, 16, 15, None), (5, 32, 9, None), (2049, 64, 8, 16.0), (777, 128, 11, None),
+    (4097, 256, 8, None), (1000, 256, 15, 64.0), (1, 256, 12, None),
 ]
 
 

@@ -66,7 +66,7 @@ def run_router(hidden_np, w_np, b_np, K, with_logits=True):
 
 
 @pytest.mark.parametrize("N,H,E,K", [(1000, 256, 256, 6), (333, 128, 64, 4), (129, 64, 32, 2),
-                                     (4096, 512, 128, 7)])
+                                     (4096, 512, 128, 7), (700, 128, 256, 8)])
 def test_router_small(O, N, H, E, K):
     hidden_np, w_np, b_np, _, _, _ = synth.router(seed=3, N=N, H=H, E=E)
     G.say(f"router N={N} H={H} E={E} K={K}")
