@@ -374,6 +374,7 @@ def suite(torch, qb, synth, dev, args):
     res["controller"] = controller_suite(torch, qb, synth, dev, args)
     res["sharding"] = sharding_suite(torch, qb, synth, dev, args)
     res["one_pass_full_hist"] = full_hist_suite(torch, qb, synth, dev, args)
+    res["k3_skew"] = k3_skew_suite(torch, qb, synth, dev, args)
     res["lei_backward"] = lei_backward_suite(torch, qb, synth, dev, args)
     return res
 
@@ -443,6 +444,50 @@ def full_hist_suite(torch, qb, synth, dev, args):
                same_b_next=same,
                note="one pass reads s once but makes one device atomic per score into a 64 MiB histogram")
     del s, hist
+    torch.cuda.empty_cache()
+    return out
+
+
+def k3_skew_suite(torch, qb, synth, dev, args):
+    """The K3 mode on the skewed 1M-token layer (1000 uniform bins over the
+    bias range): the alpha pass, the binning pass over the same 1 GiB of
+    scores, the interpolating select and the bias update, from one graph;
+    the binning pass alone from HIP events around back-to-back launches."""
+    s_np, b_np, K = synth.skew()
+    N, E = s_np.shape
+    s = torch.from_numpy(s_np).to(dev)
+    b0 = torch.from_numpy(b_np).to(dev)
+    bounds0 = torch.zeros(2, dtype=torch.float32, device=dev)
+    qb.qb_bias_bounds(b0, bounds0)
+    b, bounds = b0.clone(), bounds0.clone()
+    alpha = torch.empty(N, dtype=torch.float32, device=dev)
+    hist_u = torch.zeros((E, 1000), dtype=torch.int32, device=dev)
+    q = torch.zeros(E, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    class K3Step:
+        def run(self_, i=0):
+            b.copy_(b0)
+            bounds.copy_(bounds0)
+            qb.qb_fill_i32(hist_u, 0)
+            qb.k3_update(s, b, K, alpha, bounds, hist_u, q, err=err)
+
+    sec, _ = time_graph(K3Step(), torch, max(5, args.steps // 2), 2)
+    assert int(err.item()) == 0
+    f = lambda: qb.qb_uniform_hist(s, alpha, bounds, hist_u)
+    f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    bin_us = e0.elapsed_time(e1) * 1e3 / 10
+    out = dict(N=N, E=E, K=K, n_bins=1000, us_per_step=round(sec * 1e6, 2), tokens_per_s=N / sec,
+               step_GBps=round(N * (8 * E + 8) / sec / 1e9, 1), binning_pass_us=round(bin_us, 2),
+               binning_pass_GBps=round(N * (4 * E + 4) / bin_us / 1e3, 1))
+    del s, hist_u
     torch.cuda.empty_cache()
     return out
 

@@ -9,10 +9,16 @@
 // Mixture-of-Experts" (summary page), LEI paragraph: add eta * rho_e to the
 // score gradient of expert e for every token of the batch.
 //
-// Layout of the K3 pass: E x 1000 int32 counters do not fit in LDS, so each
-// workgroup owns a slice of 16 experts (16 * n_bins int32 in LDS, 64 KB at
-// 1000 bins, two workgroups per CU) and a chunk of rows; 4 lanes read the
-// slice's 64 contiguous bytes of a row, 16 rows per load instruction.
+// Layout of the K3 pass: E x n_bins counters do not fit in LDS, so each
+// workgroup owns a slice of S experts (S = 64 for up to 1024 bins, 32 or 16
+// for more bins or fewer experts) and a block of rows, and counts in packed
+// 16-bit pairs (two experts per dword; <= 65535 rows per workgroup), about
+// 128 KiB of LDS at 64 experts x 1000 bins.  S/4 lanes read the slice's
+// S * 4 contiguous bytes of a row (256 B at S = 64), 64/(S/4) rows per load
+// instruction; the row stride of the counter table is one more than a
+// multiple of 64 dwords, so the lanes of different experts that hit the
+// same bin land in different banks.  The counts are flushed once per
+// workgroup into the int32 [E][n_bins] histogram with agent-scope atomics.
 #include <algorithm>
 
 #include "qb_device.hpp"
@@ -20,27 +26,45 @@
 
 namespace qbk {
 
-constexpr int kUHThreads = 512;
-constexpr int kUHWaves = kUHThreads / kWave;
-constexpr int kUHSlice = 16;                 // experts per workgroup
-constexpr int kUHRPI = kWave / (kUHSlice / 4);  // rows per load instruction
-constexpr int kUHUnroll = 4;
-constexpr int kUHStep = kUHWaves * kUHRPI * kUHUnroll;
+constexpr int kUHWaves = 16;
+constexpr int kUHThreads = kUHWaves * kWave;
+#ifndef QB_UH_UNROLL
+#define QB_UH_UNROLL 8
+#endif
+constexpr int kUHUnroll = QB_UH_UNROLL;  // rows per lane per trip
+// workgroups per CU when the counter table takes at most 40 KiB
+#ifndef QB_UH_SMALL_PER_CU
+#define QB_UH_SMALL_PER_CU 4
+#endif
 
+template <int S>
+struct UHShape {
+  static constexpr int QPS = S / 4;                // lanes per row (one float4 each)
+  static constexpr int RPI = kWave / QPS;          // rows per load instruction
+  static constexpr int RPW = RPI * kUHUnroll;      // rows per wave trip
+  static constexpr int STEP = kUHWaves * RPW;      // rows per workgroup trip
+};
+
+// Row stride (dwords) of the packed counter table for n_bins bins.
+inline int uh_stride(int n_bins) { return (n_bins + 63) / 64 * 64 + 1; }
+
+template <int S>
 __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
     const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int E,
-    const float* __restrict__ bounds, int n_bins, int wg_per_layer, int32_t* __restrict__ hist_u) {
-  extern __shared__ int32_t lds_u[];  // [kUHSlice][n_bins]
-  const int n_slices = E / kUHSlice;
-  const int per_layer = n_slices * wg_per_layer;
+    const float* __restrict__ bounds, int n_bins, int stride, int wg_per_slice, int32_t* __restrict__ hist_u) {
+  using U = UHShape<S>;
+  extern __shared__ uint32_t lds_u[];  // [S / 2][stride] packed pairs
+  const int n_slices = E / S;
+  const int per_layer = n_slices * wg_per_slice;
   const int layer = blockIdx.x / per_layer;
   const int rem = blockIdx.x - layer * per_layer;
   const int slice = rem % n_slices;
   const int g = rem / n_slices;
-  s += int64_t(layer) * N * E + slice * kUHSlice;
+  s += int64_t(layer) * N * E + slice * S;
   alpha += int64_t(layer) * N;
   const int tid = threadIdx.x;
-  for (int d = tid; d < kUHSlice * n_bins; d += kUHThreads) lds_u[d] = 0;
+  const int words = (S / 2) * stride;
+  for (int d = tid; d < words; d += kUHThreads) lds_u[d] = 0u;
   const float lo = bounds[2 * layer];
   const float hi = bounds[2 * layer + 1];
   const float width = hi - lo;
@@ -49,60 +73,104 @@ __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
   __syncthreads();
 
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int q4 = lane & 3;
-  const int rsub = lane >> 2;
-  int32_t* cnt = lds_u + 4 * q4 * n_bins;
-  // Block-cyclic trips of kUHStep rows: this workgroup takes g, g + G, ...
-  for (int64_t base = int64_t(g) * kUHStep + int64_t(wave) * kUHRPI * kUHUnroll; base < N;
-       base += int64_t(wg_per_layer) * kUHStep) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int q = lane % U::QPS;
+  const int rsub = lane / U::QPS;
+  uint32_t* rowp = lds_u + 2 * q * stride;  // experts 4q, 4q+1; 4q+2, 4q+3 one stride on
+  // Block-cyclic trips of STEP rows: this workgroup takes g, g + G, ...
+  for (int64_t base = int64_t(g) * U::STEP + int64_t(wave) * U::RPW; base < N;
+       base += int64_t(wg_per_slice) * U::STEP) {
     float4 x[kUHUnroll];
     float a[kUHUnroll];
 #pragma unroll
     for (int u = 0; u < kUHUnroll; ++u) {
-      int64_t row = base + u * kUHRPI + rsub;
+      int64_t row = base + u * U::RPI + rsub;
       row = row < N ? row : N - 1;
-      x[u] = ld4(s + row * E + 4 * q4);
+      x[u] = ld4(s + row * E + 4 * q);
       a[u] = alpha[row];
     }
 #pragma unroll
     for (int u = 0; u < kUHUnroll; ++u) {
-      if (base + u * kUHRPI + rsub < N) {
+      if (base + u * U::RPI + rsub < N) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float r = a[u] - comp(x[u], c);
           const float t = (r - lo) * inv_w;
           const int idx = !(t >= 0.0f) ? 0 : (t >= fbins ? n_bins - 1 : int(t));
-          atomicAdd(cnt + c * n_bins + idx, 1);
+          atomicAdd(rowp + (c >> 1) * stride + idx, (c & 1) ? 0x10000u : 1u);
         }
       }
     }
   }
   __syncthreads();
-  int32_t* out = hist_u + (int64_t(layer) * E + slice * kUHSlice) * n_bins;
-  for (int d = tid; d < kUHSlice * n_bins; d += kUHThreads)
-    if (lds_u[d]) atomicAdd(out + d, lds_u[d]);
+  // Flush: the G workgroups of a slice add into the same counters, so each
+  // starts its walk at a different block of the table (by its index g).
+  int32_t* out = hist_u + (int64_t(layer) * E + slice * S) * n_bins;
+  const int nblk = (words + kUHThreads - 1) / kUHThreads;
+  const int b0 = g % nblk;
+  for (int k = 0; k < nblk; ++k) {
+    int blk = b0 + k;
+    blk = blk >= nblk ? blk - nblk : blk;
+    const int d = blk * kUHThreads + tid;
+    if (d >= words) continue;
+    const uint32_t v = lds_u[d];
+    if (v) {
+      const int pair = d / stride;
+      const int bin = d - pair * stride;  // < n_bins: only those are ever incremented
+      int32_t* o = out + int64_t(2 * pair) * n_bins + bin;
+      if (v & 0xFFFFu) atomicAdd(o, int(v & 0xFFFFu));
+      if (v >> 16) atomicAdd(o + n_bins, int(v >> 16));
+    }
+  }
 }
+
+template <int S>
+static int64_t uh_groups(int L, int64_t N, int E, int per_cu) {
+  using U = UHShape<S>;
+  const int n_slices = E / S;
+  const int64_t trips = (N + U::STEP - 1) / U::STEP;
+  const int64_t max_trips = std::max<int64_t>(1, 65535 / U::STEP);  // 16-bit counters
+  int64_t G = (int64_t(device_cu_count()) * per_cu + int64_t(L) * n_slices - 1) / (int64_t(L) * n_slices);
+  G = std::max(G, (trips + max_trips - 1) / max_trips);
+  return std::max<int64_t>(1, std::min(G, trips));
+}
+
+template <int S>
+static int launch_uh(const float* s, const float* alpha, int L, int64_t N, int E, const float* bounds,
+                     int n_bins, int32_t* hist_u, hipStream_t st) {
+  const int stride = uh_stride(n_bins);
+  const size_t lds = size_t(S / 2) * size_t(stride) * sizeof(uint32_t);
+  // workgroups per CU that the table leaves room for (up to 4)
+  const int per_cu = lds > 80 * 1024 ? 1 : (lds > 40 * 1024 ? 2 : QB_UH_SMALL_PER_CU);
+  const int n_slices = E / S;
+  const int64_t G = uh_groups<S>(L, N, E, per_cu);
+  const int64_t blocks = int64_t(L) * n_slices * G;
+  static bool attr_set = false;
+  if (!attr_set && lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uniform_hist<S>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return int(e);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_uniform_hist<S>), dim3(unsigned(blocks)), dim3(kUHThreads), lds, st, s, alpha, N, E,
+                     bounds, n_bins, stride, int(G), hist_u);
+  return int(hipGetLastError());
+}
+
+// Wider slices read longer row segments but give each workgroup a larger
+// table to clear and flush; they are used when every workgroup still gets
+// at least kUHMinRows rows.
+#ifndef QB_UH_MIN_ROWS
+#define QB_UH_MIN_ROWS 8192
+#endif
 
 int launch_uniform_hist(const float* s, const float* alpha, int L, int64_t N, int E,
                         const float* bounds, int n_bins, int32_t* hist_u, hipStream_t st) {
-  // Row-trip workgroups per (layer, slice) so that all layers' slices make
-  // about two workgroups per CU.
-  const int n_slices = E / kUHSlice;
-  const int64_t trips = (N + kUHStep - 1) / kUHStep;
-  const int64_t per = std::max<int64_t>(
-      1, (2 * int64_t(device_cu_count()) + int64_t(L) * n_slices - 1) / (int64_t(L) * n_slices));
-  const int G = int(std::min<int64_t>(per, trips));
-  const int64_t blocks = int64_t(L) * n_slices * G;
-  const size_t lds = size_t(kUHSlice) * size_t(n_bins) * sizeof(int32_t);
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uniform_hist),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return int(e);
-  }
-  hipLaunchKernelGGL(k_uniform_hist, dim3(unsigned(blocks)), dim3(kUHThreads), lds, st, s, alpha, N,
-                     E, bounds, n_bins, G, hist_u);
-  return int(hipGetLastError());
+  if (E >= 64 && n_bins <= 1024 && N / uh_groups<64>(L, N, E, 1) >= QB_UH_MIN_ROWS)
+    return launch_uh<64>(s, alpha, L, N, E, bounds, n_bins, hist_u, st);
+  if (E >= 32 && N / uh_groups<32>(L, N, E, 1) >= QB_UH_MIN_ROWS)
+    return launch_uh<32>(s, alpha, L, N, E, bounds, n_bins, hist_u, st);
+  return launch_uh<16>(s, alpha, L, N, E, bounds, n_bins, hist_u, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -156,6 +224,16 @@ int launch_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta
 //   add_e  = fl32(eta * rho_e)
 //   g'     = fl32(g + add_e);  dlogit = fl32(g' * fl32(s * fl32(1 - s)))
 // grid (G, C): blockIdx.y is the microbatch.
+// Float4 groups per thread and trip, and workgroups per CU of the grid (up
+// to the work available): many small workgroups keep enough reads in flight
+// (at 262,144 x 256: 189 us with 64 per CU against 236 us with 8).
+#ifndef QB_LEI_U
+#define QB_LEI_U 4
+#endif
+#ifndef QB_LEI_WG_PER_CU
+#define QB_LEI_WG_PER_CU 64
+#endif
+
 __global__ __launch_bounds__(kLeiThreads) void k_lei_bwd(const float* __restrict__ g,
                                                          const float* __restrict__ s,
                                                          const int32_t* __restrict__ load_mb, int64_t n_mb,
@@ -195,7 +273,7 @@ __global__ __launch_bounds__(kLeiThreads) void k_lei_bwd(const float* __restrict
   float4* d4 = dlogits ? reinterpret_cast<float4*>(dlogits) + base4 : nullptr;
   // four strided elements per thread and trip: all loads issued before any
   // store, so each thread keeps 8 (or 4) 16-byte reads in flight
-  constexpr int U = 4;
+  constexpr int U = QB_LEI_U;
   for (int64_t i = i0; i < n4; i += U * stride) {
     float4 v[U], p[U];
 #pragma unroll
@@ -232,7 +310,7 @@ int launch_lei_bwd(const float* g, const float* s, const int32_t* load_mb, int64
   const int64_t C = N / n_mb;
   const int64_t n4 = n_mb * E / 4;
   const int64_t want = std::max<int64_t>(1, (n4 + kLeiThreads - 1) / kLeiThreads);
-  const int64_t cap = std::max<int64_t>(1, int64_t(device_cu_count()) * 8 / C);
+  const int64_t cap = std::max<int64_t>(1, int64_t(device_cu_count()) * QB_LEI_WG_PER_CU / C);
   const unsigned gx = unsigned(std::min(want, cap));
   hipLaunchKernelGGL(k_lei_bwd, dim3(gx, unsigned(C)), dim3(kLeiThreads), 0, st, g, s, load_mb, n_mb, E, K, eta,
                      bounded, g_out, dlogits);

@@ -139,3 +139,37 @@ def test_tiled_layer_beyond_int32_elements(O, ws):
     for k in ("key", "q", "b_next", "bounds"):
         G.assert_same(k, G.host({"key": buf.key, "q": buf.q, "b_next": b, "bounds": buf.bounds}[k]), ref[k])
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("E,T,n_bins", [(64, 4096, 40), (256, 64, 2048), (256, 256, 1000)])
+def test_k3_tiled_layer(O, E, T, n_bins):
+    """K3 binning of a 4096-row block with heavy ties repeated T times, at
+    sizes that take the wide expert slices of the binning pass: 16,777,216
+    tokens x 64 experts (64-expert slices, about 65,000 rows per workgroup,
+    so the packed 16-bit LDS counters run close to their limit), 262,144 x
+    256 with 2048 bins (32-expert slices) and 1,048,576 x 256 with 1000
+    bins (64-expert slices).  The histogram is T times the block's, and the
+    interpolated quantile (rank m = T * m_block; every count scales by the
+    same factor) and b_next are the block's exactly."""
+    P, K = 4096, 6
+    blk, b_np, _ = synth.random_case(23, P, E, K, quant=2.0)
+    bounds = O.bounds_of(b_np)
+    ref = O.k3_layer(blk, b_np, K, bounds, n_bins)
+    N = P * T
+    G.say(f"k3 tiled N={N} E={E} bins={n_bins}")
+    s = G.dev(blk).repeat(T, 1)
+    b = G.dev(b_np)
+    bnd = G.dev(bounds.astype(np.float32))
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    hist_u = torch.zeros((E, n_bins), dtype=torch.int32, device=G.DEV)
+    q = torch.zeros(E, dtype=torch.float32, device=G.DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+    qb.k3_update(s, b, K, alpha, bnd, hist_u, q_out=q, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    del s
+    G.assert_same("hist_u", G.host(hist_u), T * ref["hist_u"])
+    for k, t in (("q", q), ("b_next", b), ("bounds", bnd)):
+        G.assert_same(k, G.host(t), ref[k])
+    torch.cuda.empty_cache()

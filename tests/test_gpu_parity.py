@@ -104,7 +104,10 @@ def test_standalone_hist_hi_and_keys(O):
 
 @pytest.mark.parametrize("N,E,K,n_bins,quant", [
     (4000, 16, 2, 1000, None), (3000, 64, 6, 50, 64.0), (5000, 256, 6, 1000, None),
-    (1, 32, 3, 1000, None), (2049, 128, 7, 2048, None), (777, 256, 1, 7, 8.0)])
+    (1, 32, 3, 1000, None), (2049, 128, 7, 2048, None), (777, 256, 1, 7, 8.0),
+    # 64-, 32- and 16-expert slices of the packed counter table at their bin limits
+    (3000, 64, 5, 1024, 16.0), (3000, 32, 4, 1500, None), (2000, 256, 6, 2048, None),
+    (500, 16, 3, 2048, 4.0), (70000, 128, 6, 10, 1.0)])
 def test_k3_sweep(O, N, E, K, n_bins, quant):
     s, b, _ = synth.random_case(50, N, E, K, quant=quant)
     bounds = O.bounds_of(b)
