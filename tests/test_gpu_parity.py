@@ -271,3 +271,58 @@ def test_graph_capture_replays(O):
                    q=G.host(buf.q), b_next=G.host(b), bounds=G.host(buf.bounds),
                    err=int(buf.err.item()))
         G.compare_eqb(got, ref, with_load=False, tag=f"replay {rep} ")
+
+
+def test_graph_capture_workspace_step_and_k3(O):
+    """The benchmark's step -- bias restore, pass 1, select HI, the
+    workspace pass 2 and the select that also clears the high-byte
+    histogram (no fill launch) -- and a K3 update, each captured once and
+    replayed several times with eager work in between; every replay
+    matches the oracle."""
+    N, E, K = 30000, 256, 6
+    s_np, b_np, _ = synth.random_case(91, N, E, K, quant=64.0)
+    ref = O.eqb_layer(s_np, b_np, K)
+    bounds_np = O.bounds_of(b_np)
+    ref3 = O.k3_layer(s_np, b_np, K, bounds_np, 1000)
+    s, b0 = G.dev(s_np), G.dev(b_np)
+    bounds0 = G.dev(bounds_np.astype(np.float32))
+    b, b3, bnd3 = b0.clone(), b0.clone(), bounds0.clone()
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    alpha3 = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    buf = qb.EqbBuffers(1, E, device=G.DEV, lead=False)
+    ws = torch.empty(qb.qb_hist_lo_workspace_bytes(1, N, E), dtype=torch.uint8, device=G.DEV)
+    hist_u = torch.zeros((E, 1000), dtype=torch.int32, device=G.DEV)
+    q3 = torch.zeros(E, dtype=torch.float32, device=G.DEV)
+    err3 = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+
+    def step():
+        b.copy_(b0)
+        qb.eqb_update_ws(s, b, K, alpha, buf, ws, reset_hist_hi=True)
+        b3.copy_(b0)
+        bnd3.copy_(bounds0)
+        qb.qb_fill_i32(hist_u, 0)
+        qb.k3_update(s, b3, K, alpha3, bnd3, hist_u, q3, err=err3)
+
+    G.say("graph capture, workspace step + K3")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        step()  # warm-up outside capture
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    for rep in range(4):
+        junk = torch.randn(1 << 20, device=G.DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        assert int(buf.err.item()) == 0 and int(err3.item()) == 0
+        assert int(buf.hist_hi.abs().sum().item()) == 0, "hist_hi not cleared by the select"
+        for k, t in (("alpha", alpha), ("hist_lo", buf.hist_lo), ("sel_hi", buf.sel_hi),
+                     ("rank_lo", buf.rank_lo), ("key", buf.key), ("q", buf.q), ("b_next", b),
+                     ("bounds", buf.bounds)):
+            G.assert_same(f"replay {rep} {k}", G.host(t), ref[k])
+        for k, t in (("hist_u", hist_u), ("q", q3), ("b_next", b3), ("bounds", bnd3)):
+            G.assert_same(f"replay {rep} k3 {k}", G.host(t), ref3[k])
