@@ -82,13 +82,16 @@ __device__ __forceinline__ uint64_t rotl_v(uint64_t m, int n) {
 // element (u, c) has expert j = 4*(LPR*u + ql) + c and mask bit 4u + c, so
 // bit order is j order within a lane.  The masks are first built in load
 // order (bit 4t + c, constant positions) and then rotated by the lane's
-// column rotation; the counters take one LDS atomic per member.
+// column rotation; the counters take one LDS atomic per member.  Only the
+// "greater than alpha" mask is built for every row: fewer than K elements
+// exceed alpha only when alpha's value is tied, and then the whole wave
+// builds the "equal to alpha" masks and ranks the tied elements.
 template <int E, int P>
 __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], const float* lds_b,
                                             int rho, int ql, float a, int K, bool valid,
-                                            int32_t* lds_load, int32_t* mb_row) {
+                                            int32_t* lds_load) {
   using S = P1Shape<E>;
-  uint64_t gt_t = 0, eq_t = 0;
+  uint64_t gt_t = 0;
 #pragma unroll
   for (int t = 0; t < S::F4; ++t) {
     const int quad = S::LPR * ((t + rho) & (S::F4 - 1)) + ql;
@@ -97,49 +100,60 @@ __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], c
     for (int c = 0; c < 4; ++c) {
       const float v = comp(x[t], c) + comp(bb, c);
       gt_t |= v > a ? 1ull << (4 * t + c) : 0ull;
-      eq_t |= v == a ? 1ull << (4 * t + c) : 0ull;
     }
   }
   const int rot = 4 * (rho & (S::F4 - 1));
   uint64_t mem = rotl_v<S::V>(gt_t, rot);
-  const uint64_t eq = rotl_v<S::V>(eq_t, rot);
   int G = __popcll(gt_t);
   if constexpr (S::LPR >= 2) G += quad_mov_i<kQuadXor1>(G);
   if constexpr (S::LPR == 4) G += quad_mov_i<kQuadXor2>(G);
   const int need = K - G;  // equal-to-alpha elements that still belong to the top K
-  // equal-to-alpha masks of the row's lanes (exchanged with every lane active)
-  uint64_t M[S::LPR];
+  if (__ballot(valid && need > 0) != 0) {  // wave-uniform: every lane takes part
+    uint64_t eq_t = 0;
 #pragma unroll
-  for (int q2 = 0; q2 < S::LPR; ++q2) {
-    const int src = rho * S::LPR + q2;
-    const uint32_t lo = __shfl(uint32_t(eq), src);
-    const uint32_t hi = __shfl(uint32_t(eq >> 32), src);
-    M[q2] = (uint64_t(hi) << 32) | lo;
-  }
-  if (!valid) return;
-  if (need > 0) {
-    // an element equal to alpha is a member when fewer than `need` equal
-    // elements of the row precede it in expert order
-    uint64_t e = eq;
-    while (e) {
-      const int bit = __builtin_ctzll(e);
-      e &= e - 1;
-      const int u = bit >> 2, c = bit & 3;
-      int r = 0;
+    for (int t = 0; t < S::F4; ++t) {
+      const int quad = S::LPR * ((t + rho) & (S::F4 - 1)) + ql;
+      const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
 #pragma unroll
-      for (int q2 = 0; q2 < S::LPR; ++q2) {
-        const int nb = q2 < ql ? 4 * (u + 1) : (q2 > ql ? 4 * u : 4 * u + c);
-        r += __popcll(M[q2] & low_bits(nb));
+      for (int c = 0; c < 4; ++c) {
+        const float v = comp(x[t], c) + comp(bb, c);
+        eq_t |= v == a ? 1ull << (4 * t + c) : 0ull;
       }
-      if (r < need) mem |= 1ull << bit;
+    }
+    const uint64_t eq = rotl_v<S::V>(eq_t, rot);
+    // equal-to-alpha masks of the row's lanes
+    uint64_t M[S::LPR];
+#pragma unroll
+    for (int q2 = 0; q2 < S::LPR; ++q2) {
+      const int src = rho * S::LPR + q2;
+      const uint32_t lo = __shfl(uint32_t(eq), src);
+      const uint32_t hi = __shfl(uint32_t(eq >> 32), src);
+      M[q2] = (uint64_t(hi) << 32) | lo;
+    }
+    if (valid && need > 0) {
+      // an element equal to alpha is a member when fewer than `need` equal
+      // elements of the row precede it in expert order
+      uint64_t e = eq;
+      while (e) {
+        const int bit = __builtin_ctzll(e);
+        e &= e - 1;
+        const int u = bit >> 2, c = bit & 3;
+        int r = 0;
+#pragma unroll
+        for (int q2 = 0; q2 < S::LPR; ++q2) {
+          const int nb = q2 < ql ? 4 * (u + 1) : (q2 > ql ? 4 * u : 4 * u + c);
+          r += __popcll(M[q2] & low_bits(nb));
+        }
+        if (r < need) mem |= 1ull << bit;
+      }
     }
   }
+  if (!valid) return;
   while (mem) {
     const int bit = __builtin_ctzll(mem);
     mem &= mem - 1;
     const int e = 4 * (S::LPR * (bit >> 2) + ql) + (bit & 3);
     atomicAdd(&lds_load[e], 1);
-    if (mb_row) atomicAdd(mb_row + e, 1);  // this token's microbatch
   }
 }
 
@@ -177,7 +191,7 @@ template <int E, int P, int HM, bool LOAD>
 __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64_t base, int64_t N,
                                         int rho, int ql, int lane, int K, const float* lds_b,
                                         uint32_t* lds_hist, int32_t* lds_load, float* alpha,
-                                        int32_t* ghist, int32_t* load_mb, int64_t n_mb) {
+                                        int32_t* ghist) {
   using S = P1Shape<E>;
   const int64_t row = base + rho;
   const bool valid = row < N;
@@ -205,10 +219,7 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
     a = top_merge_last<P, kQuadXor2>(top);
   }
   if (valid && ql == 0) alpha[row] = a;
-  if constexpr (LOAD) {
-    int32_t* mb_row = load_mb && valid ? load_mb + (row / n_mb) * E : nullptr;
-    count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load, mb_row);
-  }
+  if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load);
   if constexpr (HM == 2) {
     // full 16-bit key histogram, [E][65536] int32 in global memory
     if (valid) {
@@ -238,12 +249,18 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
   }
 }
 
-template <int E, int P, int HM, bool LOAD>
+// MB (with LOAD): per-microbatch loads as well.  Each workgroup then takes
+// one contiguous block of rows and walks it microbatch by microbatch,
+// counting the members of the current microbatch in LDS and adding them to
+// load_mb and load at each microbatch boundary (one atomic per non-zero
+// counter instead of one device atomic per member).
+template <int E, int P, int HM, bool LOAD, bool MB>
 __global__ __launch_bounds__((p1_waves<LOAD, P>() * kWave)) void k_margins_topk(
     const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int bdiv, int K,
     float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi,
     int32_t* __restrict__ load_mb, int64_t n_mb) {
   using S = P1Shape<E>;
+  static_assert(!MB || LOAD, "microbatch loads need load counting");
   constexpr int kWaves = p1_waves<LOAD, P>();
   constexpr int kThreads = kWaves * kWave;
   __shared__ uint32_t lds_hist[HM == 1 ? S::HDW : 4];
@@ -257,7 +274,8 @@ __global__ __launch_bounds__((p1_waves<LOAD, P>() * kWave)) void k_margins_topk(
   b += int64_t(layer / bdiv) * E;  // bdiv consecutive layers share a bias row
   alpha += int64_t(layer) * N;
   int32_t* ghist = HM == 2 ? hist_hi + int64_t(layer) * E * 65536 : nullptr;
-  if (LOAD && load_mb) load_mb += int64_t(layer) * (N / n_mb) * E;
+  if (LOAD) load += int64_t(layer) * E;
+  if (MB) load_mb += int64_t(layer) * (N / n_mb) * E;
 
   if constexpr (HM == 1) hist16_zero<E>(lds_hist, tid, kThreads);
   for (int j = tid; j < E; j += kThreads) {
@@ -270,32 +288,57 @@ __global__ __launch_bounds__((p1_waves<LOAD, P>() * kWave)) void k_margins_topk(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int rho = lane / S::LPR;
   const int ql = lane % S::LPR;
-  // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
   constexpr int64_t kTrip = int64_t(kWaves) * S::RPW;
-  const int64_t stride = int64_t(wg_per_layer) * kTrip;
-  int64_t base = int64_t(g) * kTrip + int64_t(wave) * S::RPW;
-
-  for (; base < N; base += stride) {
-    float4 x[S::F4];
-    p1_load<E>(s, base, N, rho, ql, x);
-    p1_rows<E, P, HM, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist, load_mb,
-                            n_mb);
+  if constexpr (!MB) {
+    // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
+    const int64_t stride = int64_t(wg_per_layer) * kTrip;
+    for (int64_t base = int64_t(g) * kTrip + int64_t(wave) * S::RPW; base < N; base += stride) {
+      float4 x[S::F4];
+      p1_load<E>(s, base, N, rho, ql, x);
+      p1_rows<E, P, HM, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist);
+    }
+  } else {
+    // Contiguous block of whole trips, split at microbatch boundaries.
+    const int64_t trips = (N + kTrip - 1) / kTrip;
+    const int64_t chunk = (trips + wg_per_layer - 1) / wg_per_layer * kTrip;
+    const int64_t r0 = int64_t(g) * chunk;
+    const int64_t r1 = r0 + chunk < N ? r0 + chunk : N;
+    for (int64_t seg0 = r0; seg0 < r1;) {
+      const int64_t mb = seg0 / n_mb;
+      const int64_t seg1 = (mb + 1) * n_mb < r1 ? (mb + 1) * n_mb : r1;
+      for (int64_t base = seg0 + int64_t(wave) * S::RPW; base < seg1; base += kTrip) {
+        float4 x[S::F4];
+        p1_load<E>(s, base, seg1, rho, ql, x);
+        p1_rows<E, P, HM, LOAD>(x, base, seg1, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist);
+      }
+      __syncthreads();
+      for (int j = tid; j < E; j += kThreads) {
+        const int32_t v = lds_load[j];
+        if (v) {
+          atomicAdd(load_mb + mb * E + j, v);
+          atomicAdd(load + j, v);
+          lds_load[j] = 0;
+        }
+      }
+      __syncthreads();
+      seg0 = seg1;
+    }
   }
   __syncthreads();
   if constexpr (HM == 1) hist16_flush<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
-  if constexpr (LOAD) {
+  if constexpr (LOAD && !MB) {
     for (int j = tid; j < E; j += kThreads)
-      if (lds_load[j]) atomicAdd(load + int64_t(layer) * E + j, lds_load[j]);
+      if (lds_load[j]) atomicAdd(load + j, lds_load[j]);
   }
 }
 
-template <int E, int P, int HM, bool LOAD>
+template <int E, int P, int HM, bool LOAD, bool MB = false>
 static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb = nullptr,
                        int64_t n_mb = 1) {
   constexpr int kThreads = p1_waves<LOAD, P>() * kWave;
   const RowSplit sp = split_rows(L, N, p1_waves<LOAD, P>() * P1Shape<E>::RPW, QB_P1_MAXROWS);
-  hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD>), dim3(unsigned(sp.blocks)), dim3(kThreads),
+  hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD, MB>), dim3(unsigned(sp.blocks)), dim3(kThreads),
                      0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi, load_mb, n_mb);
   return int(hipGetLastError());
 }
@@ -303,10 +346,14 @@ static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t 
 template <int E, int P>
 static int launch_p1(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                      int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb, int64_t n_mb) {
-  if (hist_hi && load)
-    return launch_p1_v<E, P, 1, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+  if (load && load_mb) {
+    if (hist_hi)
+      return launch_p1_v<E, P, 1, true, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+    return launch_p1_v<E, P, 0, true, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+  }
+  if (hist_hi && load) return launch_p1_v<E, P, 1, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
   if (hist_hi) return launch_p1_v<E, P, 1, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-  if (load) return launch_p1_v<E, P, 0, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
+  if (load) return launch_p1_v<E, P, 0, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
   return launch_p1_v<E, P, 0, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
 }
 
