@@ -32,6 +32,9 @@ class BiasController:
         self.b = (torch.zeros((L, E), dtype=torch.float32, **kw) if b0 is None
                   else b0.to(device=device, dtype=torch.float32).reshape(L, E).clone())
         self.buf = qb.EqbBuffers(L, E, device=device)
+        # pass 2 merges its counts through a workspace; the low-byte select
+        # also clears the high-byte histogram for the next step
+        self.ws = torch.empty(qb.qb_hist_lo_workspace_bytes(L, N, E), dtype=torch.uint8, **kw)
         self.alpha = torch.empty((L, N), dtype=torch.float32, **kw)
         # one int32 block: global loads [L][E] then microbatch loads [L][C][E],
         # cleared by one fill per step
@@ -53,7 +56,6 @@ class BiasController:
         L, N, E, K = self.L, self.N, self.E, self.K
         s3 = s.view(L, N, E)
         buf = self.buf
-        buf.reset(stream)
         qb.qb_fill_i32(self.loads, 0, stream)
         # pass 1 with the bias in force: alpha, loads, per-microbatch loads
         # and the high-byte histogram in one read of the scores
@@ -66,7 +68,7 @@ class BiasController:
         # EQB update of this batch, written over b
         qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
                             err=buf.err, stream=stream)
-        qb.qb_radix_hist_lo(s3, self.alpha, buf.sel_hi, buf.hist_lo, stream=stream)
-        qb.qb_select_update(qb.QB_SELECT_LO, K, buf.hist_lo, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
-                            key_out=buf.key, q_out=buf.q, b=self.b, bounds=buf.bounds, err=buf.err,
-                            stream=stream)
+        qb.qb_radix_hist_lo_ws(s3, self.alpha, buf.sel_hi, self.ws, stream=stream)
+        qb.qb_select_lo_ws(N, self.ws, buf.sel_hi, buf.rank_lo, buf.q, self.b, buf.bounds,
+                           hist_lo=buf.hist_lo, key_out=buf.key, err=buf.err, hist_hi=buf.hist_hi,
+                           stream=stream)
