@@ -569,18 +569,31 @@ def controller_suite(torch, qb, synth, dev, args, T=8):
     g.manual_seed(0)
     batches = [torch.sigmoid(torch.randn((N, E), generator=g, device=dev) + off) for _ in range(T)]
     ctl = BiasController(1, N, E, K, n_mb, device=dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(T + 1)]
     traj = []
-    torch.cuda.synchronize()
-    ev[0].record()
     for t in range(T):
         ctl.step(batches[t])
-        ev[t + 1].record()
         traj.append((ctl.worst_global.clone(), ctl.worst_local.clone()))
     torch.cuda.synchronize()
-    step_us = [ev[t].elapsed_time(ev[t + 1]) * 1e3 for t in range(T)]
+    # timing: the T closed-loop steps from one graph (eager launching of the
+    # dozen small calls per step would measure the host), from a zero bias
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for t in range(T):
+            ctl.step(batches[t])
+    ctl.b.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ctl.worst_global, traj[-1][0]))
+    ctl.b.zero_()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    step_us = (time.perf_counter() - t0) * 1e6 / T
+    del graph
     out = dict(N=N, E=E, K=K, n_mb=n_mb, steps=T,
-               step_us_median=round(float(np.median(step_us)), 2),
+               step_us=round(step_us, 2), graph_replay_matches_eager=same,
                global_maxvio=[round(float(a[0]), 4) for a, _ in traj],
                local_maxvio_mean=[round(float(b[1]), 4) for _, b in traj],
                local_maxvio_max=[round(float(b[0]), 4) for _, b in traj],
@@ -626,18 +639,18 @@ def router_suite(torch, qb, synth, dev, args):
     t_pass1 = reps(lambda: qb.qb_margins_topk(s, b, K, alpha), n)
     t_gemm = t_fused - t_pass1
 
+    ws = torch.empty(qb.qb_hist_lo_workspace_bytes(1, N, E), dtype=torch.uint8, device=dev)
+
     class Chain:
         def run(self_):
             b.copy_(b0)
-            buf.reset()
             qb.qb_fill_i32(load, 0)
             qb.qb_router_fused(hidden, w, b, K, s, alpha, load=load, hist_hi=buf.hist_hi)
             qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi,
                                 rank_lo=buf.rank_lo, err=buf.err)
-            qb.qb_radix_hist_lo(s, alpha, buf.sel_hi, buf.hist_lo)
-            qb.qb_select_update(qb.QB_SELECT_LO, K, buf.hist_lo, sel_hi=buf.sel_hi,
-                                rank_lo=buf.rank_lo, key_out=buf.key, q_out=buf.q, b=b,
-                                bounds=buf.bounds, err=buf.err)
+            qb.qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws)
+            qb.qb_select_lo_ws(N, ws, buf.sel_hi, buf.rank_lo, buf.q, b, buf.bounds, key_out=buf.key,
+                               err=buf.err, hist_hi=buf.hist_hi)  # clears hist_hi for the next run
             qb.qb_lei_grad(grad, load, K, 1e-5)
 
     sec, _ = time_graph(Chain(), torch, n, 1)
