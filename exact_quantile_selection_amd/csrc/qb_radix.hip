@@ -118,30 +118,36 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
   // keys are counted.  The next set is always loaded -- after its last full
   // trip a wave re-reads that trip's (cached) rows -- so the loop has one
   // path and the compiler waits for each load alone instead of for both
-  // sets.  Only a wave's last trip can be partial; it runs after the loop.
-  const int64_t stride = int64_t(wg_per_layer) * S::STEP;
-  int64_t base = int64_t(g) * S::STEP + int64_t(wave) * S::RPW;
+  // sets.  The loop runs over the trips whose rows are all below N, the same
+  // count for every wave, and the waves meet at a bare barrier after each
+  // trip: kept in step, the workgroup reads each block of rows together
+  // (190 us against 197 us for 1M x 256 when the waves drift apart).  The
+  // barrier orders nothing (the counters need no ordering until the flush,
+  // which a full barrier precedes).  The workgroup's last trip, if partial,
+  // runs after the loop.
+  const int64_t full_trips = N / S::STEP;
+  const int64_t nF = full_trips > g ? (full_trips - 1 - g) / wg_per_layer + 1 : 0;
+  auto trip_base = [&](int64_t k) { return (int64_t(g) + k * wg_per_layer) * S::STEP + int64_t(wave) * S::RPW; };
   float4 xa[kRHUnroll], xb[kRHUnroll];
   float aa[kRHUnroll], ab[kRHUnroll];
-  if (base + S::RPW <= N) {
-    load_full(base, xa, aa);
-    for (;;) {
-      const int64_t nb = base + stride;
-      const bool nfull = nb + S::RPW <= N;
-      load_full(nfull ? nb : base, xb, ab);
+  if (nF > 0) {
+    load_full(trip_base(0), xa, aa);
+    for (int64_t k = 0;; k += 2) {
+      const bool more = k + 1 < nF;
+      load_full(trip_base(more ? k + 1 : k), xb, ab);
 #pragma unroll
       for (int u = 0; u < kRHUnroll; ++u) count1(xa[u], aa[u]);
-      base = nb;
-      if (!nfull) break;
-      const int64_t nb2 = base + stride;
-      const bool nfull2 = nb2 + S::RPW <= N;
-      load_full(nfull2 ? nb2 : base, xa, aa);
+      __builtin_amdgcn_s_barrier();
+      if (!more) break;
+      const bool more2 = k + 2 < nF;
+      load_full(trip_base(more2 ? k + 2 : k + 1), xa, aa);
 #pragma unroll
       for (int u = 0; u < kRHUnroll; ++u) count1(xb[u], ab[u]);
-      base = nb2;
-      if (!nfull2) break;
+      __builtin_amdgcn_s_barrier();
+      if (!more2) break;
     }
   }
+  const int64_t base = trip_base(nF);
   if (base < N) {
     // the partial trip: rows clamped to N - 1 for the loads, not counted
 #pragma unroll
