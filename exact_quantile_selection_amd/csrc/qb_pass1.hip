@@ -292,18 +292,28 @@ __global__ __launch_bounds__((p1_waves<LOAD, P>() * kWave)) void k_margins_topk(
   if constexpr (!MB) {
     // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
     // Every wave runs the same number of trips (rows past N are clamped and
-    // masked), and the waves meet at a bare barrier after each trip: kept in
-    // step, the workgroup reads each 256-row block together (193-195 us
+    // masked), and the waves meet at a bare barrier once per trip: kept in
+    // step, the workgroup reads each block of rows together (193-195 us
     // against 201-202 us for 1M x 256 when the waves drift apart).  The
-    // barrier orders nothing: the histogram atomics need no ordering until
-    // the flush, which a full barrier precedes.
+    // upper half of the waves issues its loads before the barrier and the
+    // lower half after it, so the scores of one half are in flight while
+    // the other half still ranks and counts its rows (190-191 us; all waves
+    // loading on the same side of the barrier leaves HBM idle while they
+    // all compute).  The barrier orders nothing: the histogram atomics need
+    // no ordering until the flush, which a full barrier precedes.
     const int64_t trips = (N + kTrip - 1) / kTrip;
+    const bool early = wave >= kWaves / 2;
     for (int64_t T = g; T < trips; T += wg_per_layer) {
       const int64_t base = T * kTrip + int64_t(wave) * S::RPW;
       float4 x[S::F4];
-      p1_load<E>(s, base, N, rho, ql, x);
+      if (early) {
+        p1_load<E>(s, base, N, rho, ql, x);
+        __builtin_amdgcn_s_barrier();
+      } else {
+        __builtin_amdgcn_s_barrier();
+        p1_load<E>(s, base, N, rho, ql, x);
+      }
       p1_rows<E, P, HM, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist);
-      __builtin_amdgcn_s_barrier();
     }
   } else {
     // Contiguous block of whole trips, split at microbatch boundaries.

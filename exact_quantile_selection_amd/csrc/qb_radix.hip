@@ -9,9 +9,10 @@
 //
 // Layout on gfx950: lane l of a wave owns float4 column block (quad)
 // l % (E/4) of its row, so one load instruction covers 64*16 contiguous bytes
-// (one row at E=256) and a wave trip reads kRHUnroll consecutive rows.  Trips
-// are block-cyclic over the workgroups, so the workgroups in flight read
-// neighbouring rows.  Each lane keeps two register sets of rows in flight.
+// (one row at E=256) and a wave trip reads RHShape::U load instructions
+// (16 consecutive rows at E=256).  Trips are block-cyclic over the
+// workgroups, so the workgroups in flight read neighbouring rows; half of a
+// workgroup's waves load while the other half counts.
 // Counters are the packed 16-bit LDS histogram of qb_device.hpp (bank swizzle
 // by quad), flushed once per workgroup.  A lane's experts are fixed for the
 // whole kernel, so the low-byte pass keeps their selected high bytes in
@@ -34,13 +35,15 @@ namespace qbk {
 #endif
 constexpr int kRHWaves = QB_RH_WAVES;
 constexpr int kRHThreads = kRHWaves * kWave;
-constexpr int kRHUnroll = 8;  // rows per lane per register set
 
 template <int E>
 struct RHShape {
   static constexpr int QPR = E / 4;            // lanes per row
   static constexpr int RPI = kWave / QPR;      // rows per load instruction
-  static constexpr int RPW = RPI * kRHUnroll;  // rows per wave trip
+  // rows per lane per trip: 16 at E = 256 (one row per load instruction);
+  // 8 for narrower rows, whose row offsets take more registers per lane
+  static constexpr int U = E >= 256 ? 16 : 8;
+  static constexpr int RPW = RPI * U;          // rows per wave trip
   static constexpr int STEP = kRHWaves * RPW;  // rows per workgroup trip
   static_assert(QPR <= kWave && (kWave % QPR) == 0, "row split");
 };
@@ -89,11 +92,11 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
   // Full trips (every row < N): addresses from the wave-uniform row base
   // with 32-bit lane offsets, no clamps and no per-row tests, so the loop
   // body is straight-line and each set's loads are waited for one by one.
-  auto load_full = [&](int64_t base, float4 (&x)[kRHUnroll], float (&a)[kRHUnroll]) {
+  auto load_full = [&](int64_t base, float4 (&x)[S::U], float (&a)[S::U]) {
     const float* sw = s + base * E;
     const float* aw = alpha + base;
 #pragma unroll
-    for (int u = 0; u < kRHUnroll; ++u) {
+    for (int u = 0; u < S::U; ++u) {
       x[u] = ld4(sw + uint32_t((u * S::RPI + rsub) * E + 4 * quad));
       a[u] = aw[u * S::RPI + rsub];
     }
@@ -114,52 +117,47 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     }
   };
   // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
-  // Two register sets: the next trip's rows are in flight while this trip's
-  // keys are counted.  The next set is always loaded -- after its last full
-  // trip a wave re-reads that trip's (cached) rows -- so the loop has one
-  // path and the compiler waits for each load alone instead of for both
-  // sets.  The loop runs over the trips whose rows are all below N, the same
-  // count for every wave, and the waves meet at a bare barrier after each
-  // trip: kept in step, the workgroup reads each block of rows together
-  // (190 us against 197 us for 1M x 256 when the waves drift apart).  The
+  // The loop runs over the trips whose rows are all below N, the same count
+  // for every wave, and the waves meet at a bare barrier once per trip: kept
+  // in step, the workgroup reads each block of rows together (190 us against
+  // 197 us for 1M x 256 when the waves drift apart).  The upper half of the
+  // waves issues its loads before the barrier and the lower half after it,
+  // so one half's rows are in flight while the other half counts.  With 16
+  // rows per lane in one register set this takes 186-187 us; two sets of 8
+  // (the next trip loaded while this one is counted) took 190-191 us.  The
   // barrier orders nothing (the counters need no ordering until the flush,
   // which a full barrier precedes).  The workgroup's last trip, if partial,
   // runs after the loop.
   const int64_t full_trips = N / S::STEP;
   const int64_t nF = full_trips > g ? (full_trips - 1 - g) / wg_per_layer + 1 : 0;
   auto trip_base = [&](int64_t k) { return (int64_t(g) + k * wg_per_layer) * S::STEP + int64_t(wave) * S::RPW; };
-  float4 xa[kRHUnroll], xb[kRHUnroll];
-  float aa[kRHUnroll], ab[kRHUnroll];
-  if (nF > 0) {
-    load_full(trip_base(0), xa, aa);
-    for (int64_t k = 0;; k += 2) {
-      const bool more = k + 1 < nF;
-      load_full(trip_base(more ? k + 1 : k), xb, ab);
-#pragma unroll
-      for (int u = 0; u < kRHUnroll; ++u) count1(xa[u], aa[u]);
+  const bool early = wave >= kRHWaves / 2;
+  float4 x[S::U];
+  float a[S::U];
+  for (int64_t k = 0; k < nF; ++k) {
+    if (early) {
+      load_full(trip_base(k), x, a);
       __builtin_amdgcn_s_barrier();
-      if (!more) break;
-      const bool more2 = k + 2 < nF;
-      load_full(trip_base(more2 ? k + 2 : k + 1), xa, aa);
-#pragma unroll
-      for (int u = 0; u < kRHUnroll; ++u) count1(xb[u], ab[u]);
+    } else {
       __builtin_amdgcn_s_barrier();
-      if (!more2) break;
+      load_full(trip_base(k), x, a);
     }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) count1(x[u], a[u]);
   }
   const int64_t base = trip_base(nF);
   if (base < N) {
     // the partial trip: rows clamped to N - 1 for the loads, not counted
 #pragma unroll
-    for (int u = 0; u < kRHUnroll; ++u) {
+    for (int u = 0; u < S::U; ++u) {
       int64_t row = base + u * S::RPI + rsub;
       row = row < N ? row : N - 1;
-      xa[u] = ld4(s + row * E + 4 * quad);
-      aa[u] = alpha[row];
+      x[u] = ld4(s + row * E + 4 * quad);
+      a[u] = alpha[row];
     }
 #pragma unroll
-    for (int u = 0; u < kRHUnroll; ++u)
-      if (base + u * S::RPI + rsub < N) count1(xa[u], aa[u]);
+    for (int u = 0; u < S::U; ++u)
+      if (base + u * S::RPI + rsub < N) count1(x[u], a[u]);
   }
   __syncthreads();
   if constexpr (WS) {
