@@ -227,6 +227,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1048576)
     ap.add_argument("--router", action="store_true",
                     help="time only the fused-router workload and print its JSON line")
+    ap.add_argument("--only", default=None,
+                    help="time only this workload of the suite and print its JSON line "
+                         "(single, step_48_layers, router, controller, sharding, "
+                         "one_pass_full_hist, k3_skew, lei_backward)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the update shards over "
@@ -242,10 +246,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    if args.router:
-        log("router workload")
-        print(json.dumps({"workload": "router", "router": router_suite(torch, qb, synth, dev, args)}),
-              flush=True)
+    only = "router" if args.router else args.only
+    if only:
+        if only not in SUITES:
+            print(f"unknown workload {only!r}; one of {', '.join(SUITES)}", file=sys.stderr)
+            sys.exit(2)
+        log(f"{only} workload")
+        print(json.dumps({"workload": only, only: SUITES[only](torch, qb, synth, dev, args)}), flush=True)
         return
 
     p = synth.WORKLOADS["skew"]
@@ -322,9 +329,10 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def suite(torch, qb, synth, dev, args):
+def single_suite(torch, qb, synth, dev, args):
+    """The 65,536-token layer (64 MiB of scores: they fit in the 256 MB
+    Infinity Cache), EQB and K3, each step from one graph."""
     res = {}
-    # 65,536-token layer: EQB and K3 (scores fit in the 256 MB infinity cache)
     s_np, b_np, K = synth.single()
     N, E = s_np.shape
     s = torch.from_numpy(s_np).to(dev)
@@ -352,7 +360,13 @@ def suite(torch, qb, synth, dev, args):
     res["single_k3"] = dict(N=N, n_bins=1000, us_per_step=round(sec * 1e6, 2), tokens_per_s=N / sec,
                             effective_GBps=round(N * (8 * E + 8) / sec / 1e9, 1))
     del s, st
-    # 48-layer step on device-generated scores of the same recipe
+    torch.cuda.empty_cache()
+    return res
+
+
+def step48_suite(torch, qb, synth, dev, args):
+    """The 48-layer step on device-generated scores of the same recipe
+    (layer-batched launches, 12 GiB of scores)."""
     p = synth.WORKLOADS["step"]
     L, N, E, K = p["L"], p["N"], p["E"], p["K"]
     g = torch.Generator(device=dev)
@@ -365,17 +379,18 @@ def suite(torch, qb, synth, dev, args):
     b0 = (torch.rand((L, E), generator=g, device=dev) * 0.2 - 0.1).contiguous()
     st = EqbStep(s, b0, K, qb, torch)
     sec, _ = time_graph(st, torch, max(3, args.steps // 4), 1)
-    res["step_48_layers"] = dict(L=L, N=N, ms_per_step=round(sec * 1e3, 3),
-                                 tokens_per_s_per_layer=L * N / sec,
-                                 GBps=round(L * N * (8 * E + 8) / sec / 1e9, 1))
+    out = dict(L=L, N=N, ms_per_step=round(sec * 1e3, 3), tokens_per_s_per_layer=L * N / sec,
+               GBps=round(L * N * (8 * E + 8) / sec / 1e9, 1))
     del s, st
     torch.cuda.empty_cache()
-    res["router"] = router_suite(torch, qb, synth, dev, args)
-    res["controller"] = controller_suite(torch, qb, synth, dev, args)
-    res["sharding"] = sharding_suite(torch, qb, synth, dev, args)
-    res["one_pass_full_hist"] = full_hist_suite(torch, qb, synth, dev, args)
-    res["k3_skew"] = k3_skew_suite(torch, qb, synth, dev, args)
-    res["lei_backward"] = lei_backward_suite(torch, qb, synth, dev, args)
+    return out
+
+
+def suite(torch, qb, synth, dev, args):
+    res = single_suite(torch, qb, synth, dev, args)
+    for name, f in SUITES.items():
+        if name != "single":
+            res[name] = f(torch, qb, synth, dev, args)
     return res
 
 
@@ -667,6 +682,18 @@ def router_suite(torch, qb, synth, dev, args):
     del hidden, w, grad, s
     torch.cuda.empty_cache()
     return out
+
+
+SUITES = {
+    "single": single_suite,
+    "step_48_layers": step48_suite,
+    "router": router_suite,
+    "controller": controller_suite,
+    "sharding": sharding_suite,
+    "one_pass_full_hist": full_hist_suite,
+    "k3_skew": k3_skew_suite,
+    "lei_backward": lei_backward_suite,
+}
 
 
 if __name__ == "__main__":
