@@ -269,7 +269,7 @@ QB_API int qb_lei_backward(const float* g, const float* s, const int32_t* load_m
 
 QB_API int64_t qb_hist_lo_workspace_bytes(int L, int64_t N, int E) {
   if (L < 1 || N < 1 || !qbk::supported_E(E)) return QB_EINVAL;
-  return int64_t(L) * E * qbk::radix_wg_per_layer(L, N, E) * 256 * 2;
+  return qbk::lo_ws_layout(L, E, qbk::radix_wg_per_layer(L, N, E)).bytes;
 }
 
 QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E, const int32_t* sel_hi,
@@ -283,7 +283,7 @@ QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_
     return fail(QB_EINVAL, "%s: ws_bytes=%lld, this shape needs %lld (qb_hist_lo_workspace_bytes)", fn,
                 (long long)ws_bytes, (long long)need);
   if (!aligned16(ws)) return fail(QB_EINVAL, "%s: ws must be 16-byte aligned", fn);
-  return hip_status(qbk::launch_radix_hist_lo_ws(s, alpha, L, N, E, sel_hi, static_cast<uint16_t*>(ws), stream), fn);
+  return hip_status(qbk::launch_radix_hist_lo_ws(s, alpha, L, N, E, sel_hi, static_cast<uint8_t*>(ws), stream), fn);
 }
 
 QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_t* sel_hi, const int32_t* rank_lo,
@@ -299,7 +299,7 @@ QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_
                 fn, L, E);
   if (!aligned16(ws) || (hist_lo && !aligned4(hist_lo)) || (hist_hi && !aligned4(hist_hi)))
     return fail(QB_EINVAL, "%s: ws must be 16-byte aligned, hist_lo and hist_hi 4-byte aligned", fn);
-  return hip_status(qbk::launch_select_lo_ws(L, E, qbk::radix_wg_per_layer(L, N, E), static_cast<const uint16_t*>(ws),
+  return hip_status(qbk::launch_select_lo_ws(L, E, qbk::radix_wg_per_layer(L, N, E), static_cast<const uint8_t*>(ws),
                                              sel_hi, rank_lo, hist_lo, key_out, q_out, b, bounds, hist_hi, err,
                                              stream),
                     fn);

@@ -31,9 +31,29 @@ int launch_margins_topk(const float* s, const float* b, int L, int64_t N, int E,
                         float* alpha, int32_t* load, int32_t* hist_hi, hipStream_t st, int bdiv = 1,
                         int32_t* load_mb = nullptr, int64_t n_mb = 1);
 int radix_wg_per_layer(int L, int64_t N, int E);
+
+// Workspace of the low-byte pass: one partial histogram row per (layer,
+// expert, workgroup), row r = (layer * E + j) * G + g.  A row whose 256
+// counts are all <= 255 is stored as bytes (p8: uint8 [rows][256]); any
+// other as uint16 (p16: uint16 [rows][256]); flag[r] (uint8) says which.
+// Every row's flag is written on every pass, so the contents on entry do
+// not matter.
+struct LoWs {
+  int64_t flag;   // byte offset of the flags
+  int64_t p16;    // byte offset of the uint16 rows (16-byte aligned)
+  int64_t bytes;  // total
+};
+inline LoWs lo_ws_layout(int L, int E, int G) {
+  const int64_t rows = int64_t(L) * E * G;
+  LoWs w;
+  w.flag = rows * 256;
+  w.p16 = (w.flag + rows + 15) / 16 * 16;
+  w.bytes = w.p16 + rows * 512;
+  return w;
+}
 int launch_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E,
-                            const int32_t* sel_hi, uint16_t* ws, hipStream_t st);
-int launch_select_lo_ws(int L, int E, int G, const uint16_t* ws, const int32_t* sel_hi, const int32_t* rank_lo,
+                            const int32_t* sel_hi, uint8_t* ws, hipStream_t st);
+int launch_select_lo_ws(int L, int E, int G, const uint8_t* ws, const int32_t* sel_hi, const int32_t* rank_lo,
                         int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
                         int32_t* hist_hi, int32_t* err, hipStream_t st);
 int launch_lei_bwd(const float* g, const float* s, const int32_t* load_mb, int64_t N, int E, int K,

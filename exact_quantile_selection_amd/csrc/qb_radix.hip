@@ -49,13 +49,15 @@ struct RHShape {
 };
 
 // WS: instead of adding its counts into the global histogram with atomics,
-// the workgroup stores them, dense, as its own partial histogram
-// ws[layer][j][g][h] (uint16; at most 65535 rows per workgroup), for a
-// select that sums the partials (no atomics, no zeroing).
+// the workgroup stores them, dense, as its own partial histogram row per
+// expert in the workspace (LoWs in qb_internal.hpp: bytes when all 256
+// counts of the row are <= 255, uint16 otherwise, and a flag saying which),
+// for a select that sums the partials (no atomics, no zeroing).
 template <int E, bool LO, bool WS>
 __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int wg_per_layer,
-    const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist, uint16_t* __restrict__ ws) {
+    const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist, uint8_t* __restrict__ ws,
+    int64_t ws_flag, int64_t ws_p16) {
   using S = RHShape<E>;
   __shared__ uint32_t lds_hist[(E / 2) * 256];
   const int tid = threadIdx.x;
@@ -164,11 +166,16 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     // Item i covers bins 8k .. 8k+7 (k = i & 31) of dword row pair = i >> 5
     // (experts 2 pair and 2 pair + 1).  Its eight counters are one aligned
     // 8-dword block of LDS, permuted by the row's bank swizzle
-    // (quad = pair >> 1: c[m] holds bin 8k + (m ^ (quad & 7))), and leave
-    // as one 16-byte store per expert.  The 64 items of a wave are the two
-    // rows of one quad, so the permutation is the same across the wave.
+    // (quad = pair >> 1: c[m] holds bin 8k + (m ^ (quad & 7))).  The 32
+    // items of a pair are one half of a wave, so a half-wave ballot tells
+    // whether any of an expert's 256 counts exceeds 255: if none does, the
+    // row leaves as 8 bytes per item, else as 8 uint16 (16 bytes) per item.
+    // Lane k = 0 writes the row's flag.  A workgroup writes 64 KiB at
+    // E = 256 when every row fits in bytes, half the uint16 partials.
     const int G = wg_per_layer;
-    uint16_t* w = ws + int64_t(layer) * E * G * 256;
+    const int64_t row_base = int64_t(layer) * E * G + g;  // row of expert j: row_base + j * G
+    uint8_t* flag = ws + ws_flag;
+    uint16_t* p16 = reinterpret_cast<uint16_t*>(ws + ws_p16);
     for (int i = tid; i < (E / 2) * 32; i += kRHThreads) {
       const int pair = i >> 5, k = i & 31;
       const int sw = (pair >> 1) & 63;
@@ -188,17 +195,50 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
             }
         }
       }
-      uint4 lo, hi;  // expert 2 pair: low halves; expert 2 pair + 1: high halves
-      lo.x = (c[0] & 0xFFFFu) | (c[1] << 16);
-      lo.y = (c[2] & 0xFFFFu) | (c[3] << 16);
-      lo.z = (c[4] & 0xFFFFu) | (c[5] << 16);
-      lo.w = (c[6] & 0xFFFFu) | (c[7] << 16);
-      hi.x = (c[0] >> 16) | (c[1] & 0xFFFF0000u);
-      hi.y = (c[2] >> 16) | (c[3] & 0xFFFF0000u);
-      hi.z = (c[4] >> 16) | (c[5] & 0xFFFF0000u);
-      hi.w = (c[6] >> 16) | (c[7] & 0xFFFF0000u);
-      *reinterpret_cast<uint4*>(w + (int64_t(2 * pair) * G + g) * 256 + 8 * k) = lo;
-      *reinterpret_cast<uint4*>(w + (int64_t(2 * pair + 1) * G + g) * 256 + 8 * k) = hi;
+      // expert 2 pair: the low halves of c; expert 2 pair + 1: the high halves
+      uint32_t big_lo = 0, big_hi = 0;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        big_lo |= c[m] & 0xFF00u;
+        big_hi |= c[m] & 0xFF000000u;
+      }
+      const uint64_t bal_lo = __ballot(big_lo != 0), bal_hi = __ballot(big_hi != 0);
+      const int half = (tid & (kWave - 1)) >> 5;  // which pair of the wave
+      const bool wide_lo = uint32_t(bal_lo >> (32 * half)) != 0;
+      const bool wide_hi = uint32_t(bal_hi >> (32 * half)) != 0;
+      const int64_t r_lo = row_base + int64_t(2 * pair) * G, r_hi = r_lo + G;
+      if (wide_lo) {
+        uint4 o;
+        o.x = (c[0] & 0xFFFFu) | (c[1] << 16);
+        o.y = (c[2] & 0xFFFFu) | (c[3] << 16);
+        o.z = (c[4] & 0xFFFFu) | (c[5] << 16);
+        o.w = (c[6] & 0xFFFFu) | (c[7] << 16);
+        *reinterpret_cast<uint4*>(p16 + r_lo * 256 + 8 * k) = o;
+      } else {
+        uint2 o;
+        o.x = (c[0] & 0xFFu) | ((c[1] & 0xFFu) << 8) | ((c[2] & 0xFFu) << 16) | ((c[3] & 0xFFu) << 24);
+        o.y = (c[4] & 0xFFu) | ((c[5] & 0xFFu) << 8) | ((c[6] & 0xFFu) << 16) | ((c[7] & 0xFFu) << 24);
+        *reinterpret_cast<uint2*>(ws + r_lo * 256 + 8 * k) = o;
+      }
+      if (wide_hi) {
+        uint4 o;
+        o.x = (c[0] >> 16) | (c[1] & 0xFFFF0000u);
+        o.y = (c[2] >> 16) | (c[3] & 0xFFFF0000u);
+        o.z = (c[4] >> 16) | (c[5] & 0xFFFF0000u);
+        o.w = (c[6] >> 16) | (c[7] & 0xFFFF0000u);
+        *reinterpret_cast<uint4*>(p16 + r_hi * 256 + 8 * k) = o;
+      } else {
+        uint2 o;
+        o.x = ((c[0] >> 16) & 0xFFu) | (((c[1] >> 16) & 0xFFu) << 8) | (((c[2] >> 16) & 0xFFu) << 16) |
+              ((c[3] >> 16) << 24);
+        o.y = ((c[4] >> 16) & 0xFFu) | (((c[5] >> 16) & 0xFFu) << 8) | (((c[6] >> 16) & 0xFFu) << 16) |
+              ((c[7] >> 16) << 24);
+        *reinterpret_cast<uint2*>(ws + r_hi * 256 + 8 * k) = o;
+      }
+      if (k == 0) {
+        flag[r_lo] = wide_lo ? 1 : 0;
+        flag[r_hi] = wide_hi ? 1 : 0;
+      }
     }
   } else {
     hist16_flush<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads, g);
@@ -211,19 +251,20 @@ static int launch_rh(bool lo, const float* s, const float* alpha, int L, int64_t
   const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, QB_RH_MAXROWS);
   if (lo)
     hipLaunchKernelGGL((k_radix_hist<E, true, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
-                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr);
+                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr, int64_t(0), int64_t(0));
   else
     hipLaunchKernelGGL((k_radix_hist<E, false, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
-                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr);
+                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr, int64_t(0), int64_t(0));
   return int(hipGetLastError());
 }
 
 template <int E>
 static int launch_rh_ws(const float* s, const float* alpha, int L, int64_t N, const int32_t* sel_hi,
-                        uint16_t* ws, hipStream_t st) {
+                        uint8_t* ws, hipStream_t st) {
   const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, QB_RH_MAXROWS);
+  const LoWs lay = lo_ws_layout(L, E, sp.wg_per_layer);
   hipLaunchKernelGGL((k_radix_hist<E, true, true>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st, s,
-                     alpha, N, sp.wg_per_layer, sel_hi, nullptr, ws);
+                     alpha, N, sp.wg_per_layer, sel_hi, nullptr, ws, lay.flag, lay.p16);
   return int(hipGetLastError());
 }
 
@@ -239,7 +280,7 @@ int radix_wg_per_layer(int L, int64_t N, int E) {
 }
 
 int launch_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E,
-                            const int32_t* sel_hi, uint16_t* ws, hipStream_t st) {
+                            const int32_t* sel_hi, uint8_t* ws, hipStream_t st) {
   switch (E) {
     case 16: return launch_rh_ws<16>(s, alpha, L, N, sel_hi, ws, st);
     case 32: return launch_rh_ws<32>(s, alpha, L, N, sel_hi, ws, st);

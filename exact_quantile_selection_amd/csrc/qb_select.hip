@@ -309,15 +309,17 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(int E, const float* __
 
 // Low-byte select from per-workgroup partial histograms (the workspace of
 // qb_radix_hist_lo_ws): one workgroup per (expert, layer).  Expert j's G
-// partial rows are contiguous (G x 512 bytes); 32 lanes read one row with
-// 16-byte loads (8 bins each), so the workgroup reads kLoWsRows rows per
-// trip.  The per-thread sums meet in LDS and thread h adds bin h over the
+// partial rows are contiguous (G x 256 bytes, or G x 512 for the rows
+// stored as uint16, picked by the row flags); 32 lanes read one row with
+// 8-byte (16-byte) loads of 8 bins each, so the workgroup reads kLoWsRows
+// rows per trip.  The per-thread sums meet in LDS and thread h adds bin h over the
 // row groups: integer sums, so the counts equal those of the atomic path.
 // The summed row optionally goes to hist_lo; then the first bin whose
 // running count reaches rank_lo is the low byte.
 constexpr int kLoWsThreads = 1024;
 constexpr int kLoWsRows = kLoWsThreads / 32;
-__global__ __launch_bounds__(kLoWsThreads) void k_select_lo_ws(int E, int G, const uint16_t* __restrict__ ws,
+__global__ __launch_bounds__(kLoWsThreads) void k_select_lo_ws(int E, int G, const uint8_t* __restrict__ ws,
+                                                               int64_t ws_flag, int64_t ws_p16,
                                                                const int32_t* __restrict__ sel_hi,
                                                                const int32_t* __restrict__ rank_lo,
                                                                int32_t* __restrict__ hist_lo,
@@ -331,9 +333,24 @@ __global__ __launch_bounds__(kLoWsThreads) void k_select_lo_ws(int E, int G, con
   const int j = blockIdx.x, layer = blockIdx.y, t = threadIdx.x;
   const int64_t le = int64_t(layer) * E;
   const int c8 = t & 31, r0 = t >> 5;
-  const uint4* rows = reinterpret_cast<const uint4*>(ws + (le + j) * G * 256) + c8;  // row g at rows[32 g]
+  // Partial row g of expert j: bytes at p8[32 g] (8 per thread) unless
+  // its flag says uint16, then p16[32 g] (8 uint16 per thread).
+  const int64_t row0 = (le + j) * G;
+  const uint8_t* flag = ws + ws_flag + row0;
+  const uint2* p8 = reinterpret_cast<const uint2*>(ws + row0 * 256) + c8;
+  const uint4* p16 = reinterpret_cast<const uint4*>(ws + ws_p16 + row0 * 512) + c8;
   int32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  auto add = [&](const uint4& v) {
+  auto add8 = [&](const uint2& v) {
+    acc[0] += int32_t(v.x & 0xFFu);
+    acc[1] += int32_t((v.x >> 8) & 0xFFu);
+    acc[2] += int32_t((v.x >> 16) & 0xFFu);
+    acc[3] += int32_t(v.x >> 24);
+    acc[4] += int32_t(v.y & 0xFFu);
+    acc[5] += int32_t((v.y >> 8) & 0xFFu);
+    acc[6] += int32_t((v.y >> 16) & 0xFFu);
+    acc[7] += int32_t(v.y >> 24);
+  };
+  auto add16 = [&](const uint4& v) {
     acc[0] += int32_t(v.x & 0xFFFFu);
     acc[1] += int32_t(v.x >> 16);
     acc[2] += int32_t(v.y & 0xFFFFu);
@@ -343,18 +360,26 @@ __global__ __launch_bounds__(kLoWsThreads) void k_select_lo_ws(int E, int G, con
     acc[6] += int32_t(v.w & 0xFFFFu);
     acc[7] += int32_t(v.w >> 16);
   };
+  auto add_row = [&](int gg, const uint2& v8, uint8_t f) {
+    if (f)
+      add16(p16[int64_t(gg) * 32]);
+    else
+      add8(v8);
+  };
   int g = r0;
   for (; g + 3 * kLoWsRows < G; g += 4 * kLoWsRows) {
-    const uint4 v0 = rows[int64_t(g) * 32];
-    const uint4 v1 = rows[int64_t(g + kLoWsRows) * 32];
-    const uint4 v2 = rows[int64_t(g + 2 * kLoWsRows) * 32];
-    const uint4 v3 = rows[int64_t(g + 3 * kLoWsRows) * 32];
-    add(v0);
-    add(v1);
-    add(v2);
-    add(v3);
+    const uint8_t f0 = flag[g], f1 = flag[g + kLoWsRows], f2 = flag[g + 2 * kLoWsRows],
+                  f3 = flag[g + 3 * kLoWsRows];
+    const uint2 v0 = p8[int64_t(g) * 32];
+    const uint2 v1 = p8[int64_t(g + kLoWsRows) * 32];
+    const uint2 v2 = p8[int64_t(g + 2 * kLoWsRows) * 32];
+    const uint2 v3 = p8[int64_t(g + 3 * kLoWsRows) * 32];
+    add_row(g, v0, f0);
+    add_row(g + kLoWsRows, v1, f1);
+    add_row(g + 2 * kLoWsRows, v2, f2);
+    add_row(g + 3 * kLoWsRows, v3, f3);
   }
-  for (; g < G; g += kLoWsRows) add(rows[int64_t(g) * 32]);
+  for (; g < G; g += kLoWsRows) add_row(g, p8[int64_t(g) * 32], flag[g]);
   int4* dst = reinterpret_cast<int4*>(&s_part[r0][8 * c8]);
   dst[0] = make_int4(acc[0], acc[1], acc[2], acc[3]);
   dst[1] = make_int4(acc[4], acc[5], acc[6], acc[7]);
@@ -426,11 +451,12 @@ int launch_select(int phase, int L, int E, int K, const int32_t* hist, int n_bin
   return int(hipGetLastError());
 }
 
-int launch_select_lo_ws(int L, int E, int G, const uint16_t* ws, const int32_t* sel_hi, const int32_t* rank_lo,
+int launch_select_lo_ws(int L, int E, int G, const uint8_t* ws, const int32_t* sel_hi, const int32_t* rank_lo,
                         int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
                         int32_t* hist_hi, int32_t* err, hipStream_t st) {
-  hipLaunchKernelGGL(k_select_lo_ws, dim3(unsigned(E), unsigned(L)), dim3(kLoWsThreads), 0, st, E, G, ws, sel_hi,
-                     rank_lo, hist_lo, key_out, q_out, hist_hi, err);
+  const LoWs lay = lo_ws_layout(L, E, G);
+  hipLaunchKernelGGL(k_select_lo_ws, dim3(unsigned(E), unsigned(L)), dim3(kLoWsThreads), 0, st, E, G, ws, lay.flag,
+                     lay.p16, sel_hi, rank_lo, hist_lo, key_out, q_out, hist_hi, err);
   if (int rc = int(hipGetLastError())) return rc;
   hipLaunchKernelGGL(k_finalize, dim3(unsigned(L)), dim3(kFinThreads), 0, st, E, q_out, b, bounds, err);
   return int(hipGetLastError());

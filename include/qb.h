@@ -172,15 +172,17 @@ QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist,
  * Pass 2 and the low-byte select without global atomics, for one update per
  * call (no accumulation across calls).  Same results as qb_radix_hist_lo +
  * qb_select_update(QB_SELECT_LO), bit for bit: every workgroup of pass 2
- * stores its counts as a dense partial histogram in a caller workspace
- * (uint16 [L][E][G][256], G = workgroups per layer), and the select sums the
- * G partials of each bin in workgroup order (integer sums) before the rank
- * scan.  The EQB paragraph's low-byte histogram, with the merge moved from
- * global atomics to the select.
+ * stores its counts as a dense partial histogram row per expert in a caller
+ * workspace (G = workgroups per layer; a row whose 256 counts are all
+ * <= 255 as uint8, any other as uint16, with a byte flag per row saying
+ * which), and the select sums the G partials of each bin in workgroup
+ * order (integer sums) before the rank scan.  The EQB paragraph's low-byte
+ * histogram, with the merge moved from global atomics to the select.
  *   qb_hist_lo_workspace_bytes: bytes the workspace needs for this shape
- *     (L * E * G * 512; 32 MiB for one 1,048,576 x 256 layer), or a negative
- *     status.  ws must be 16-byte aligned; its contents on entry do not
- *     matter.
+ *     (L * E * G * 769 rounded up to 16; 48 MiB for one 1,048,576 x 256
+ *     layer, of which a pass whose rows all fit in bytes writes 16 MiB), or
+ *     a negative status.  ws must be 16-byte aligned; its contents on entry
+ *     do not matter (every row's flag is written).
  *   qb_radix_hist_lo_ws: as qb_radix_hist_lo, writing ws (overwritten).
  *   qb_select_lo_ws: as qb_select_update(QB_SELECT_LO) from ws; ws must be
  *     the workspace the preceding qb_radix_hist_lo_ws call wrote, with the

@@ -20,7 +20,7 @@ def _gpu():
     qb.lib()
 
 
-def run_ws(s_np, b_np, K, reset=False):
+def run_ws(s_np, b_np, K, reset=False, keep_ws=False):
     lead = s_np.shape[:-2]
     L = int(np.prod(lead)) if lead else 1
     N, E = s_np.shape[-2:]
@@ -32,10 +32,13 @@ def run_ws(s_np, b_np, K, reset=False):
     ws.fill_(0xAB)  # stale bytes: the path overwrites, never accumulates
     qb.eqb_update_ws(s, b, K, alpha, buf, ws, load=load, reset_hist_hi=reset)
     torch.cuda.synchronize()
-    return dict(alpha=G.host(alpha), hist_hi=G.host(buf.hist_hi), sel_hi=G.host(buf.sel_hi),
-                rank_lo=G.host(buf.rank_lo), hist_lo=G.host(buf.hist_lo), key=G.host(buf.key),
-                q=G.host(buf.q), b_next=G.host(b), bounds=G.host(buf.bounds), err=int(buf.err.item()),
-                load=G.host(load))
+    out = dict(alpha=G.host(alpha), hist_hi=G.host(buf.hist_hi), sel_hi=G.host(buf.sel_hi),
+               rank_lo=G.host(buf.rank_lo), hist_lo=G.host(buf.hist_lo), key=G.host(buf.key),
+               q=G.host(buf.q), b_next=G.host(b), bounds=G.host(buf.bounds), err=int(buf.err.item()),
+               load=G.host(load))
+    if keep_ws:
+        out["ws"] = G.host(ws)
+    return out
 
 
 @pytest.mark.parametrize("N,E,K,quant", [(5000, 256, 6, None), (3333, 64, 4, 16.0), (1, 16, 2, None),
@@ -44,6 +47,30 @@ def test_ws_update_vs_oracle(O, N, E, K, quant):
     G.say(f"ws update N={N} E={E} K={K}")
     s, b, _ = synth.random_case(71, N, E, K, quant=quant)
     G.compare_eqb(run_ws(s, b, K), O.eqb_layer(s, b, K), tag="ws ")
+
+
+def test_ws_update_mixed_byte_and_wide_rows(O):
+    """Partial rows with a count above 255 leave pass 2 as uint16, the
+    others as bytes.  Experts 0-7 are constant and highest in every row, so
+    alpha is the same for all rows; experts 8-127 are constant too, so each
+    of them has one key and a workgroup's count in its selected bin is the
+    workgroup's row count (256 rows: above 255); experts 128-255 are random
+    below them (counts of a few per bin).  Both kinds of row meet in one
+    select; N is ragged, so two workgroups also take a partial trip."""
+    N, E, K = 65536 + 300, 256, 6
+    G.say("ws update, byte and uint16 partial rows")
+    rng = np.random.default_rng(12)
+    s = np.empty((N, E), dtype=np.float32)
+    s[:, :8] = (0.99 - 0.01 * np.arange(8)).astype(np.float32)
+    s[:, 8:128] = rng.uniform(0.05, 0.6, 120).astype(np.float32)
+    s[:, 128:] = rng.uniform(0.0, 0.7, (N, E - 128)).astype(np.float32)
+    b = np.zeros(E, dtype=np.float32)
+    got = run_ws(s, b, K, keep_ws=True)
+    G.compare_eqb(got, O.eqb_layer(s, b, K), tag="ws mixed ")
+    ws = got["ws"]
+    rows = ws.size // 769  # L * E * G rows of (256 + 1 + 512) bytes, plus < 16 bytes of padding
+    flags = ws[rows * 256: rows * 257]
+    assert set(np.unique(flags).tolist()) == {0, 1}, "expected both byte and uint16 rows"
 
 
 def test_ws_update_three_layers(O):
