@@ -177,6 +177,39 @@ __device__ __forceinline__ void hist16_flush(const uint32_t* lds, int32_t* out, 
   }
 }
 
+// As hist16_flush, two adjacent bins of an expert per 64-bit atomic (the
+// pair of LDS dwords 2 i, 2 i + 1 holds the bins 2 m, 2 m + 1 of the same
+// two experts, in either order).  out must be 8-byte aligned.  Each 32-bit
+// half takes its own sum: counts stay below 2^31, so the low half never
+// carries into the high one.
+template <int E>
+__device__ __forceinline__ void hist16_flush_pairs(const uint32_t* lds, int32_t* out, int tid, int nthreads,
+                                                   int start) {
+  constexpr int HDW2 = (E / 2) * 128;
+  const int nblk = (HDW2 + nthreads - 1) / nthreads;
+  const int b0 = start % nblk;
+  const uint2* l2 = reinterpret_cast<const uint2*>(lds);
+  for (int k = 0; k < nblk; ++k) {
+    int blk = b0 + k;
+    blk = blk >= nblk ? blk - nblk : blk;
+    const int d2 = blk * nthreads + tid;
+    if (d2 >= HDW2) continue;
+    const uint2 v = l2[d2];
+    if ((v.x | v.y) == 0u) continue;
+    const int d = 2 * d2;
+    const int pair = d >> 8;
+    const int h0 = (d & 255) ^ ((pair >> 1) & 63);  // bin of dword d; dword d + 1 holds h0 ^ 1
+    const int hb = h0 & ~1;
+    const uint32_t a = (h0 & 1) ? v.y : v.x;  // bin hb
+    const uint32_t c = (h0 & 1) ? v.x : v.y;  // bin hb + 1
+    const uint64_t lo = uint64_t(a & 0xFFFFu) | (uint64_t(c & 0xFFFFu) << 32);
+    const uint64_t hi = uint64_t(a >> 16) | (uint64_t(c >> 16) << 32);
+    const int j0 = 2 * pair;
+    if (lo) atomicAdd(reinterpret_cast<unsigned long long*>(out + j0 * 256 + hb), (unsigned long long)lo);
+    if (hi) atomicAdd(reinterpret_cast<unsigned long long*>(out + (j0 + 1) * 256 + hb), (unsigned long long)hi);
+  }
+}
+
 template <int E>
 __device__ __forceinline__ void hist16_zero(uint32_t* lds, int tid, int nthreads) {
   constexpr int HDW = (E / 2) * 256;

@@ -240,8 +240,11 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
         flag[r_hi] = wide_hi ? 1 : 0;
       }
     }
-  } else {
+  } else if constexpr (LO) {
+    // low-byte counts spread over the bins: one 32-bit atomic per counter
     hist16_flush<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads, g);
+  } else {
+    hist16_flush_pairs<E>(lds_hist, hist + int64_t(layer) * E * 256, tid, kRHThreads, g);
   }
 }
 
