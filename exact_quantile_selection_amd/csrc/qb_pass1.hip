@@ -218,7 +218,9 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
     top_merge<P, kQuadXor1>(top);
     a = top_merge_last<P, kQuadXor2>(top);
   }
-  if (valid && ql == 0) alpha[row] = a;
+  // alpha is read again only by the next pass: a non-temporal store keeps
+  // it from sitting dirty in L2 until the end of the kernel
+  if (valid && ql == 0) __builtin_nontemporal_store(a, alpha + row);
   if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load);
   if constexpr (HM == 2) {
     // full 16-bit key histogram, [E][65536] int32 in global memory

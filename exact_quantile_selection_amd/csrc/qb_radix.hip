@@ -30,6 +30,10 @@
 
 namespace qbk {
 
+// vector types the non-temporal store builtin accepts
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 #ifndef QB_RH_WAVES
 #define QB_RH_WAVES 16
 #endif
@@ -171,7 +175,9 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     // whether any of an expert's 256 counts exceeds 255: if none does, the
     // row leaves as 8 bytes per item, else as 8 uint16 (16 bytes) per item.
     // Lane k = 0 writes the row's flag.  A workgroup writes 64 KiB at
-    // E = 256 when every row fits in bytes, half the uint16 partials.
+    // E = 256 when every row fits in bytes, half the uint16 partials.  The
+    // rows leave with non-temporal stores (read once, by the select): at the
+    // end of the pass less dirty data waits in L2 (182 -> 180 us at 1M).
     const int G = wg_per_layer;
     const int64_t row_base = int64_t(layer) * E * G + g;  // row of expert j: row_base + j * G
     uint8_t* flag = ws + ws_flag;
@@ -208,32 +214,32 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
       const bool wide_hi = uint32_t(bal_hi >> (32 * half)) != 0;
       const int64_t r_lo = row_base + int64_t(2 * pair) * G, r_hi = r_lo + G;
       if (wide_lo) {
-        uint4 o;
+        u32x4 o;
         o.x = (c[0] & 0xFFFFu) | (c[1] << 16);
         o.y = (c[2] & 0xFFFFu) | (c[3] << 16);
         o.z = (c[4] & 0xFFFFu) | (c[5] << 16);
         o.w = (c[6] & 0xFFFFu) | (c[7] << 16);
-        *reinterpret_cast<uint4*>(p16 + r_lo * 256 + 8 * k) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p16 + r_lo * 256 + 8 * k));
       } else {
-        uint2 o;
+        u32x2 o;
         o.x = (c[0] & 0xFFu) | ((c[1] & 0xFFu) << 8) | ((c[2] & 0xFFu) << 16) | ((c[3] & 0xFFu) << 24);
         o.y = (c[4] & 0xFFu) | ((c[5] & 0xFFu) << 8) | ((c[6] & 0xFFu) << 16) | ((c[7] & 0xFFu) << 24);
-        *reinterpret_cast<uint2*>(ws + r_lo * 256 + 8 * k) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(ws + r_lo * 256 + 8 * k));
       }
       if (wide_hi) {
-        uint4 o;
+        u32x4 o;
         o.x = (c[0] >> 16) | (c[1] & 0xFFFF0000u);
         o.y = (c[2] >> 16) | (c[3] & 0xFFFF0000u);
         o.z = (c[4] >> 16) | (c[5] & 0xFFFF0000u);
         o.w = (c[6] >> 16) | (c[7] & 0xFFFF0000u);
-        *reinterpret_cast<uint4*>(p16 + r_hi * 256 + 8 * k) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p16 + r_hi * 256 + 8 * k));
       } else {
-        uint2 o;
+        u32x2 o;
         o.x = ((c[0] >> 16) & 0xFFu) | (((c[1] >> 16) & 0xFFu) << 8) | (((c[2] >> 16) & 0xFFu) << 16) |
               ((c[3] >> 16) << 24);
         o.y = ((c[4] >> 16) & 0xFFu) | (((c[5] >> 16) & 0xFFu) << 8) | (((c[6] >> 16) & 0xFFu) << 16) |
               ((c[7] >> 16) << 24);
-        *reinterpret_cast<uint2*>(ws + r_hi * 256 + 8 * k) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(ws + r_hi * 256 + 8 * k));
       }
       if (k == 0) {
         flag[r_lo] = wide_lo ? 1 : 0;
