@@ -38,36 +38,60 @@ __global__ __launch_bounds__(kMvThreads) void k_maxvio_rows(const int32_t* __res
   }
 }
 
-// Per-layer summary and the worst layer; one workgroup.
+// Per-layer summary and the worst layer; one workgroup.  Thread t owns
+// layer l0 + t of a group of up to kMvThreads layers; the group's rows are
+// staged through LDS in column chunks (all threads load, coalesced), and
+// each thread then folds its own row in microbatch order (max, and the
+// float64 sum).  Staged, the loads of a row are issued together instead
+// of one dependent load per microbatch (8 -> ~2 us at 64 microbatches).
+constexpr int kMvStage = 8192;  // staged floats (32 KiB)
 __global__ __launch_bounds__(kMvThreads) void k_maxvio_summary(const float* __restrict__ v, int L,
                                                                int C, float* __restrict__ summary,
                                                                float* __restrict__ worst) {
+  __shared__ float s_v[kMvStage];
   __shared__ float s_max[kMvThreads], s_mean[kMvThreads];
+  const int t = threadIdx.x;
   float wmax = -__builtin_inff(), wmean = -__builtin_inff();
-  for (int l = threadIdx.x; l < L; l += kMvThreads) {
-    const float* row = v + int64_t(l) * C;
-    float mx = row[0];
+  for (int l0 = 0; l0 < L; l0 += kMvThreads) {
+    const int nl = min(kMvThreads, L - l0);
+    const int cc = kMvStage / nl - 1;  // columns per chunk; row stride cc + 1 (odd: no bank conflicts)
+    float mx = __builtin_nanf("");     // fmaxf(NaN, x) = x: the fold starts at the row's first value
     double sum = 0.0;
-    for (int c = 0; c < C; ++c) {
-      mx = fmaxf(mx, row[c]);
-      sum += double(row[c]);
+    for (int c0 = 0; c0 < C; c0 += cc) {
+      const int nc = min(cc, C - c0);
+      __syncthreads();  // the previous chunk is consumed
+      for (int i = t; i < nl * nc; i += kMvThreads) {
+        const int li = i / nc, ci = i - li * nc;
+        s_v[li * (cc + 1) + ci] = v[int64_t(l0 + li) * C + c0 + ci];
+      }
+      __syncthreads();
+      if (t < nl) {
+        const float* r = s_v + t * (cc + 1);
+        for (int c = 0; c < nc; ++c) {
+          mx = fmaxf(mx, r[c]);
+          sum += double(r[c]);
+        }
+      }
     }
-    const float mean = float(sum / double(C));
-    if (summary) {
-      summary[2 * l] = mx;
-      summary[2 * l + 1] = mean;
+    if (t < nl) {
+      const int l = l0 + t;
+      const float mean = float(sum / double(C));
+      if (summary) {
+        summary[2 * l] = mx;
+        summary[2 * l + 1] = mean;
+      }
+      wmax = fmaxf(wmax, mx);
+      wmean = fmaxf(wmean, mean);
     }
-    wmax = fmaxf(wmax, mx);
-    wmean = fmaxf(wmean, mean);
   }
-  s_max[threadIdx.x] = wmax;
-  s_mean[threadIdx.x] = wmean;
+  s_max[t] = wmax;
+  s_mean[t] = wmean;
   __syncthreads();
-  if (threadIdx.x == 0 && worst) {
+  if (t == 0 && worst) {
     float a = s_max[0], b = s_mean[0];
-    for (int t = 1; t < kMvThreads; ++t) {
-      a = fmaxf(a, s_max[t]);
-      b = fmaxf(b, s_mean[t]);
+    for (int i = 1; i < kMvThreads; ++i) {
+      a = fmaxf(a, s_max[i]);
+      b = fmaxf(b, s_mean[i]);
     }
     worst[0] = a;
     worst[1] = b;

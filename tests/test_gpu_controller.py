@@ -22,7 +22,8 @@ def _gpu():
 
 
 @pytest.mark.parametrize("L,C,E,K,n", [(1, 1, 256, 6, 262144), (3, 64, 256, 6, 4096), (2, 7, 16, 2, 100),
-                                       (1, 300, 37, 5, 64)])
+                                       (1, 300, 37, 5, 64), (300, 40, 16, 2, 64), (1, 20000, 16, 3, 32),
+                                       (2, 5000, 32, 4, 128)])
 def test_maxvio_vs_oracle(O, L, C, E, K, n):
     G.say(f"maxvio L={L} C={C} E={E}")
     rng = np.random.default_rng([L, C, E])
