@@ -385,11 +385,20 @@ def k3_update(s, b, K, alpha, bounds, hist_u, q_out, err=None, stream=None):
                      stream=stream)
 
 
-def runtime_libraries():
-    """Paths of HIP runtime libraries mapped into this process."""
+def _mapped(tag):
     out = set()
     with open("/proc/self/maps") as f:
         for line in f:
-            if "libamdhip64" in line:
+            if tag in line:
                 out.add(line.split()[-1])
     return sorted(out)
+
+
+def runtime_libraries():
+    """Paths of HIP runtime libraries mapped into this process."""
+    return _mapped("libamdhip64")
+
+
+def loaded_libqb():
+    """Paths of the libqb shared objects mapped into this process."""
+    return _mapped("libqb")

@@ -1,6 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle, bit
 for bit, on seeded inputs that span several workgroup tiles and a ragged
 tail, plus accumulation, reset, error and graph-capture behaviour."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -23,6 +25,8 @@ def test_single_hip_runtime():
     torch.zeros(1, device="cuda")
     libs = qb.runtime_libraries()
     assert len(libs) == 1, libs
+    # the in-tree library is the one mapped
+    assert [os.path.realpath(p) for p in qb.loaded_libqb()] == [os.path.realpath(qb.LIB_PATH)]
 
 
 def test_tiny_workload(O):
