@@ -144,10 +144,18 @@ void k_router_gemm(const uint16_t* __restrict__ hidden,
     b_slot[j] = g;
   }
 
+  // Workgroup b walks the K tiles starting at tile b mod KT: the workgroups
+  // in flight then read different column offsets of their rows, which
+  // spreads their requests over the HBM channels (streaming `hidden` alone,
+  // without the matrix work, took 255 us in K order and 186 us rotated; the
+  // whole kernel 413-421 against 410-412 us).  The fp32 sums run in a
+  // rotated order; the scores stay within the same tolerance.
+  const int krot = int(blockIdx.x % unsigned(KT));
   auto issue = [&](int kt) {
     uint8_t* sa = lds + (kt % S) * A_BYTES;
     uint8_t* sb = lds + S * A_BYTES + (kt % S) * B_BYTES;
-    const int koff = kt * BK;
+    const int kr = kt + krot;
+    const int koff = (kr < KT ? kr : kr - KT) * BK;
 #pragma unroll
     for (int j = 0; j < A_PER_WAVE; ++j)
       __builtin_amdgcn_global_load_lds((glb_vptr)(a_src[j] + koff),
