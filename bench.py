@@ -232,6 +232,9 @@ def main():
                          "(single, step_48_layers, router, controller, sharding, "
                          "one_pass_full_hist, k3_skew, lei_backward)")
     args = ap.parse_args()
+    if args.only and args.only not in SUITES:
+        print(f"unknown workload {args.only!r}; one of {', '.join(SUITES)}", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the update shards over "
               "tokens with one histogram all-reduce per pass, which this build does not run.",
@@ -248,9 +251,6 @@ def main():
 
     only = "router" if args.router else args.only
     if only:
-        if only not in SUITES:
-            print(f"unknown workload {only!r}; one of {', '.join(SUITES)}", file=sys.stderr)
-            sys.exit(2)
         log(f"{only} workload")
         print(json.dumps({"workload": only, only: SUITES[only](torch, qb, synth, dev, args)}), flush=True)
         return
