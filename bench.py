@@ -237,7 +237,7 @@ def main():
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the update shards over "
-              "tokens with one histogram all-reduce per pass, which this build does not run.",
+              "tokens with one histogram all-reduce per pass, which this library does not implement.",
               file=sys.stderr)
         sys.exit(2)
 
