@@ -123,6 +123,32 @@ def test_k3_sweep(O, N, E, K, n_bins, quant):
         G.assert_same(k, got[k], ref[k])
 
 
+@pytest.mark.parametrize("n_bins", [1000, 77])
+def test_k3_multi_layer(O, n_bins):
+    """K3 over 3 layers in one launch sequence: each layer bins against its
+    own bounds (different bias ranges), selects and updates its own bias."""
+    L, N, E, K = 3, 3001, 256, 6
+    cases = [synth.random_case(60 + l, N, E, K, quant=16.0 if l == 2 else None) for l in range(L)]
+    s_np = np.stack([c[0] for c in cases])
+    b_np = np.stack([c[1] * (l + 1) for l, c in enumerate(cases)]).astype(np.float32)
+    bounds_np = np.stack([O.bounds_of(b_np[l]) for l in range(L)]).astype(np.float32)
+    G.say(f"k3 multi-layer L={L} bins={n_bins}")
+    s, b, bounds = G.dev(s_np), G.dev(b_np), G.dev(bounds_np)
+    alpha = torch.empty((L, N), dtype=torch.float32, device=G.DEV)
+    hist_u = torch.zeros((L, E, n_bins), dtype=torch.int32, device=G.DEV)
+    q = torch.zeros((L, E), dtype=torch.float32, device=G.DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+    qb.k3_update(s, b, K, alpha, bounds, hist_u, q, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for l in range(L):
+        ref = O.k3_layer(s_np[l], b_np[l], K, bounds_np[l], n_bins)
+        got = dict(alpha=G.host(alpha[l]), hist_u=G.host(hist_u[l]), q=G.host(q[l]), b_next=G.host(b[l]),
+                   bounds=G.host(bounds[l]))
+        for k in ("alpha", "hist_u", "q", "b_next", "bounds"):
+            G.assert_same(f"layer {l} {k}", got[k], ref[k])
+
+
 def test_bias_bounds(O):
     b_np = np.random.default_rng(3).uniform(-0.3, 0.3, (5, 64)).astype(np.float32)
     bounds = torch.zeros((5, 2), dtype=torch.float32, device=G.DEV)
