@@ -41,7 +41,9 @@
  *   - Histograms and loads are ACCUMULATED (+=) so that several token chunks
  *     (microbatches) of one global batch can be added into one buffer.  The
  *     caller clears them in place (qb_fill_i32) after the update; buffer
- *     addresses never change.
+ *     addresses never change.  Accumulated counts must stay below 2^31 (the
+ *     int32 range): the high-byte and K3 histograms are flushed with 64-bit
+ *     atomics over two adjacent bins, exact only while no low half carries.
  *   - Scores are sigmoid outputs: finite, >= +0.  Bias values are finite.
  *     NaN/Inf inputs give unspecified (but memory-safe) results.
  *   - Supported shapes: E in {16, 32, 64, 128, 256}; 1 <= K <= 15 and K < E;
