@@ -376,6 +376,63 @@ def test_k3_interpolation_hand_example(O):
     np.testing.assert_array_equal(out["q"], [0.0, 0.0])
 
 
+def test_k3_interpolation_strictly_inside_a_bin(O):
+    """Rank m falls strictly inside a bin (h = 4, m - below = 1): the golden
+    fixes q to the linear interpolation and rejects the lower edge, centre,
+    upper edge, off-by-one and half-rank estimates ("[Dev] Add global-batch
+    quantile balancing", section "Quantile estimator")."""
+    g = json.load(open(os.path.join(GOLDEN, "k3_interpolation.json")))
+    s = np.array(g["s"], np.float32)
+    b = np.array(g["b"], np.float32)
+    out = O.k3_layer(s, b, g["K"], np.array(g["bounds_in"], np.float32), g["n_bins"])
+    np.testing.assert_array_equal(out["alpha"], g["alpha"])
+    np.testing.assert_array_equal(out["hist_u"], g["hist_u"])
+    np.testing.assert_array_equal(out["q"], g["q"])
+    np.testing.assert_array_equal(out["b_next"], g["b_next"])
+    np.testing.assert_array_equal(out["bounds"], g["bounds"])
+    for name, v in g["q_rejected"].items():
+        assert out["q"][0] != np.float32(v), name
+    # the rank really is strictly inside its bin and the fixture's arithmetic
+    # holds: lo + w * (c + (m - below) / h) with the counts it lists
+    h = np.array(g["hist_u"][0])
+    m = rank_m(s.shape[0], s.shape[1], g["K"])
+    c = int(np.searchsorted(np.cumsum(h), m))
+    below = int(h[:c].sum())
+    assert 0 < m - below < h[c]
+    lo, hi = g["bounds_in"]
+    w = (hi - lo) / g["n_bins"]
+    assert g["q"][0] == lo + w * (c + (m - below) / h[c])
+
+
+def test_mean_is_float64_sum_rounded_once(O):
+    """The mean of the quantiles ("Quantile estimator": b_next minus its
+    mean) is a float64 sum in expert order, subtracted in float64 and
+    rounded once: on this golden an fp32 running sum, or a float64 mean
+    rounded to fp32 before the subtraction, changes b_next[3] from 2^-32
+    to 0."""
+    g = json.load(open(os.path.join(GOLDEN, "mean_precision.json")))
+    s = np.array(g["s"], np.float32)
+    b = np.array(g["b"], np.float32)
+    out = O.eqb_layer(s, b, g["K"])
+    np.testing.assert_array_equal(out["alpha"], g["alpha"])
+    np.testing.assert_array_equal(out["load"], g["load"])
+    np.testing.assert_array_equal(out["q"], np.array(g["q"], np.float32))
+    np.testing.assert_array_equal(out["b_next"], np.array(g["b_next"], np.float32))
+    np.testing.assert_array_equal(out["bounds"], g["bounds"])
+    assert out["b_next"][3] == np.float32(2.0 ** -32)
+    # the rejected readings really give the other vector (numpy float32)
+    q32 = np.array(g["q"], np.float32)
+    acc = np.float32(0)
+    for x in q32:
+        acc = np.float32(acc + x)
+    alt = (q32 - np.float32(acc / np.float32(q32.size))).astype(np.float32)
+    np.testing.assert_array_equal(alt, np.array(g["b_next_fp32_mean"], np.float32))
+    mean32 = np.float32(np.sum(q32.astype(np.float64)) / q32.size)
+    alt2 = (q32 - mean32).astype(np.float32)
+    np.testing.assert_array_equal(alt2, np.array(g["b_next_fp32_mean"], np.float32))
+    assert not np.array_equal(alt, out["b_next"])
+
+
 # ---------------------------------------------------------------- LEI
 
 def test_lei_hand_example(O):
