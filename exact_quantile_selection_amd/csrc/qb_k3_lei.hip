@@ -6,8 +6,9 @@
 // expert over [min(b) - 1, max(b) + 1], accumulated into an int32 [E, bins]
 // histogram.  The fp32 margin is binned directly (no bf16 rounding).
 // LEI: "Exact Quantile Balancing and Load-Error Injection for
-// Mixture-of-Experts" (summary page), LEI paragraph: add eta * rho_e to the
-// score gradient of expert e for every token of the batch.
+// Mixture-of-Experts" (summary page), LEI paragraph: every token's gradient
+// with respect to expert e's score is shifted by eta * rho_e, rho_e being
+// that expert's relative load error over the batch.
 //
 // Layout of the K3 pass: E x n_bins counters do not fit in LDS, so each
 // workgroup owns a slice of S experts (S = 64 for up to 1024 bins, 32 or 16
@@ -20,6 +21,8 @@
 // same bin land in different banks.  The counts are flushed once per
 // workgroup into the int32 [E][n_bins] histogram with agent-scope atomics.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "qb_device.hpp"
 #include "qb_internal.hpp"
@@ -175,6 +178,35 @@ static int64_t uh_groups(int L, int64_t N, int E, int per_cu) {
   return std::max<int64_t>(1, std::min(G, trips));
 }
 
+// Largest bin count a slice width serves (launch_uniform_hist picks 64-expert
+// slices only up to 1024 bins; the API allows 2048).
+template <int S>
+constexpr int uh_max_bins() { return S == 64 ? 1024 : 2048; }
+
+// Allows k_uniform_hist<S> the dynamic LDS of the largest table any bin count
+// it serves can need (at most 131,200 B), once per device and thread-safe, so
+// a later call with more bins never launches past the allowed size.
+template <int S>
+static int uh_allow_lds() {
+  static std::atomic<uint64_t> done{0};  // bit d: set on device d
+  static std::mutex mu;
+  int dev = 0;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) return int(ge);
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return int(hipSuccess);
+  const size_t lds = size_t(S / 2) * size_t(uh_stride(uh_max_bins<S>())) * sizeof(uint32_t);
+  std::lock_guard<std::mutex> lock(mu);
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return int(hipSuccess);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uniform_hist<S>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return int(e);
+  }
+  done.fetch_or(bit, std::memory_order_release);
+  return int(hipSuccess);
+}
+
 template <int S>
 static int launch_uh(const float* s, const float* alpha, int L, int64_t N, int E, const float* bounds,
                      int n_bins, int32_t* hist_u, hipStream_t st) {
@@ -185,13 +217,8 @@ static int launch_uh(const float* s, const float* alpha, int L, int64_t N, int E
   const int n_slices = E / S;
   const int64_t G = uh_groups<S>(L, N, E, per_cu);
   const int64_t blocks = int64_t(L) * n_slices * G;
-  static bool attr_set = false;
-  if (!attr_set && lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uniform_hist<S>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return int(e);
-    attr_set = true;
-  }
+  const int ea = uh_allow_lds<S>();
+  if (ea != int(hipSuccess)) return ea;
   hipLaunchKernelGGL((k_uniform_hist<S>), dim3(unsigned(blocks)), dim3(kUHThreads), lds, st, s, alpha, N, E,
                      bounds, n_bins, stride, int(G), hist_u);
   return int(hipGetLastError());
@@ -254,10 +281,11 @@ int launch_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta
 
 // LEI per microbatch, optionally bounded, and the gradient through the
 // sigmoid ("Exact Quantile Balancing and Load-Error Injection for
-// Mixture-of-Experts", summary page, LEI paragraph: add eta * rho_e to the
-// score gradient of expert e for every token of the local batch; the
-// shipped variant bounds the residual with a tanh rescale that keeps its
-// direction and zero-centring).  Microbatch c = rows [c n_mb, (c+1) n_mb):
+// Mixture-of-Experts", summary page, LEI paragraph: each token of a local
+// batch gets eta * rho_e added to its gradient for expert e's score; the
+// page's "normalized" variant limits the size of the residual vector with
+// tanh while leaving its direction and its zero sum unchanged).  Microbatch
+// c = rows [c n_mb, (c+1) n_mb):
 //   rho_e  = fl32(((double)load[c][e] - M) / M),  M = n_mb K / E
 //   bounded: rho_e = fl32((double)rho_e * tanh(|rho|) / |rho|), |rho| the
 //            L2 norm over experts in float64 (sum in expert order)

@@ -9,8 +9,9 @@ Injection for Mixture-of-Experts" (background and EQB paragraphs):
   every rank finds the global quantile; integer sums make the result
   bit-identical to the unsharded update whatever the sharding.
 * rank-averaged QB (the MARIN implementation): every rank takes the quantile
-  of its own tokens, and the quantiles are averaged across ranks; the result
-  depends on how the batch is sharded.
+  of its own tokens, and the quantiles are averaged across ranks; since an
+  average of quantiles is not the quantile of the union, the bias changes
+  when the same batch is split over the ranks differently.
 
 Every step is a libqb call; this module only owns buffers and orders calls.
 """

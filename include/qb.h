@@ -292,11 +292,12 @@ QB_API int qb_maxvio(const int32_t* load, int L, int C, int E, int K, int64_t n_
 /*
  * LEI per local batch, optionally bounded, and the gradient through the
  * router sigmoid ("Exact Quantile Balancing and Load-Error Injection for
- * Mixture-of-Experts", summary page, LEI paragraph: eta * rho_e is added to
- * expert e's score gradient for every token of the local batch; the shipped
- * "normalized" variant bounds the residual with a tanh rescale that keeps
- * its direction and zero-centring -- the formula is not printed; the
- * rescale used here is the plainest one with those properties).  The N rows
+ * Mixture-of-Experts", summary page, LEI paragraph: each token of a local
+ * batch gets eta * rho_e added to its gradient for expert e's score; the
+ * page's "normalized" variant limits the size of the residual vector with
+ * tanh while leaving its direction and its zero sum unchanged, without
+ * printing a formula -- the scaling used here is the simplest one with
+ * those properties).  The N rows
  * form C = N / n_mb microbatches of n_mb rows; for microbatch c:
  *   rho_e  = fl32(((double)load_mb[c][e] - M) / M),  M = n_mb * K / E
  *   bounded == 1: rho_e = fl32((double)rho_e * tanh(|rho|) / |rho|), |rho| =

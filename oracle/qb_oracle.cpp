@@ -18,7 +18,7 @@
 //         Mixture-of-Experts" (paper summary page): the EQB paragraph (bf16
 //         margins, two 256-bin byte histograms, the bin holding the rank),
 //         the background paragraph (QB = K/E quantile of the margins) and the
-//         LEI paragraph (add eta * rho_e to expert e's score gradient).
+//         LEI paragraph (expert e's score gradient shifted by eta * rho_e).
 //
 // Readings of points the pages leave open (each is a stated convention):
 //   * rank: the quantile at level K/E of N margins is the order statistic of
@@ -256,8 +256,8 @@ void oq_bounds_of(const float* b, int E, float* bounds) {
   bounds[1] = mx + 1.0f;
 }
 
-// [EQB, LEI paragraph]: add eta * rho_e to the score gradient of expert e for
-// every token, rho_e = relative load error of expert e.
+// [EQB, LEI paragraph]: the gradient of every token with respect to expert
+// e's score is shifted by eta * rho_e, rho_e = relative load error of e.
 void oq_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta) {
   const double M = double(N) * double(K) / double(E);
   std::vector<float> add(E);
@@ -269,10 +269,10 @@ void oq_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta) {
     for (int e = 0; e < E; ++e) g[i * E + e] = g[i * E + e] + add[e];
 }
 
-// LEI per microbatch ([EQB] LEI paragraph: eta * rho_e added to expert e's
-// score gradient for every token of the local batch), optionally with the
-// bounded ("normalized") residual -- a tanh rescale keeping direction and
-// zero-centring; the formula is not printed, so this reading (rho scaled by
+// LEI per microbatch ([EQB] LEI paragraph: the shift eta * rho_e applies to
+// every token of the local batch), optionally with the bounded
+// ("normalized") residual -- its size limited by tanh, its direction and
+// zero sum kept; no formula is printed, so this reading (rho scaled by
 // tanh(|rho|) / |rho|, L2 norm in float64) is parity unpinned against the
 // pages -- and the gradient through the sigmoid:
 //   g' = fl32(g + fl32(eta * rho_e)), dlogit = fl32(g' * fl32(s * fl32(1 - s))).

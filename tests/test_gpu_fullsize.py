@@ -1,7 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times: the 65,536-token single layer (EQB and K3), the 1,048,576-
 token skewed layer with forced bf16 ties, and the 48-layer step (every layer
-checked against invariants, three sampled layers against the full oracle)."""
+against the full oracle and the radix invariants)."""
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -64,12 +64,16 @@ def _invariants(l, N, E, K, hist_hi, sel_hi, rank_lo, hist_lo, key, b_next):
 
 @pytest.mark.timeout(900)
 def test_step_48_layers(O):
+    """All 48 layers of the step in one launch sequence, every layer
+    compared with the oracle bit for bit (alpha, both histograms, the
+    selections, key, q, b_next, bounds) as well as checked against the
+    radix invariants.  The oracle runs layer by layer in a thread pool (its
+    calls release the GIL), regenerating each layer's seeded inputs."""
     p = synth.WORKLOADS["step"]
     L, N, E, K = p["L"], p["N"], p["E"], p["K"]
     s = torch.empty((L, N, E), dtype=torch.float32, device=G.DEV)
     b = torch.empty((L, E), dtype=torch.float32, device=G.DEV)
     G.say(f"step: generating {L} layers")
-    sampled = {0: None, 23: None, 47: None}
 
     def gen(l):
         sl, bl, _ = synth.step_layer(l)
@@ -79,25 +83,35 @@ def test_step_48_layers(O):
         for l, sl, bl in ex.map(gen, range(L)):
             s[l].copy_(torch.from_numpy(sl))
             b[l].copy_(torch.from_numpy(bl))
-            if l in sampled:
-                sampled[l] = (sl, bl)
     alpha = torch.empty((L, N), dtype=torch.float32, device=G.DEV)
     buf = qb.EqbBuffers(L, E, device=G.DEV)
     G.say("step: EQB over 48 layers")
     qb.eqb_update(s, b, K, alpha, buf)
     torch.cuda.synchronize()
     assert int(buf.err.item()) == 0
+    del s
     hh, hl = G.host(buf.hist_hi), G.host(buf.hist_lo)
     sel, rk, key, bn = G.host(buf.sel_hi), G.host(buf.rank_lo), G.host(buf.key), G.host(b)
+    al, q, bounds = G.host(alpha), G.host(buf.q), G.host(buf.bounds)
     for l in range(L):
         _invariants(l, N, E, K, hh[l], sel[l], rk[l], hl[l], key[l], bn[l])
-    for l, (sl, bl) in sampled.items():
-        G.say(f"step: oracle layer {l}")
+
+    def check(l):
+        sl, bl, _ = synth.step_layer(l)
         ref = O.eqb_layer(sl, bl, K)
-        got = dict(alpha=G.host(alpha[l]), hist_hi=hh[l], sel_hi=sel[l], rank_lo=rk[l],
-                   hist_lo=hl[l], key=key[l], q=G.host(buf.q[l]), b_next=bn[l],
-                   bounds=G.host(buf.bounds[l]), err=0)
+        got = dict(alpha=al[l], hist_hi=hh[l], sel_hi=sel[l], rank_lo=rk[l], hist_lo=hl[l],
+                   key=key[l], q=q[l], b_next=bn[l], bounds=bounds[l], err=0)
         G.compare_eqb(got, ref, with_load=False, tag=f"step layer {l} ")
+        return l
+
+    G.say("step: oracle on all 48 layers")
+    done = 0
+    with ThreadPoolExecutor(8) as ex:
+        for l in ex.map(check, range(L)):
+            done += 1
+            if done % 8 == 0:
+                G.say(f"step: {done} of {L} layers equal to the oracle")
+    assert done == L
 
 
 @pytest.mark.timeout(600)
@@ -172,4 +186,34 @@ def test_k3_tiled_layer(O, E, T, n_bins):
     G.assert_same("hist_u", G.host(hist_u), T * ref["hist_u"])
     for k, t in (("q", q), ("b_next", b), ("bounds", bnd)):
         G.assert_same(k, G.host(t), ref[k])
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_k3_more_bins_on_a_later_call(O):
+    """Two K3 binning calls in a row that take the same 64-expert slice
+    width, the second with more bins (a larger LDS table) than the first:
+    600 then 1000 bins over 524,288 tokens x 256 experts (a 4096-row block
+    repeated 128 times, so the expected results are the block's)."""
+    P, E, K, T = 4096, 256, 6, 128
+    blk, b_np, _ = synth.random_case(29, P, E, K, quant=8.0)
+    bounds = O.bounds_of(b_np)
+    N = P * T
+    s = G.dev(blk).repeat(T, 1)
+    for n_bins in (600, 1000):
+        ref = O.k3_layer(blk, b_np, K, bounds, n_bins)
+        G.say(f"k3 N={N} E={E} bins={n_bins} after a smaller table")
+        b = G.dev(b_np)
+        bnd = G.dev(bounds.astype(np.float32))
+        alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+        hist_u = torch.zeros((E, n_bins), dtype=torch.int32, device=G.DEV)
+        q = torch.zeros(E, dtype=torch.float32, device=G.DEV)
+        err = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+        qb.k3_update(s, b, K, alpha, bnd, hist_u, q_out=q, err=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        G.assert_same(f"hist_u ({n_bins} bins)", G.host(hist_u), T * ref["hist_u"])
+        for k, t in (("q", q), ("b_next", b), ("bounds", bnd)):
+            G.assert_same(f"{k} ({n_bins} bins)", G.host(t), ref[k])
+    del s
     torch.cuda.empty_cache()
