@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/qb.h"
@@ -303,6 +304,94 @@ QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_
                                              sel_hi, rank_lo, hist_lo, key_out, q_out, b, bounds, hist_hi, err,
                                              stream),
                     fn);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of qb_radix_lo_select_noalloc: the pass-2 partial histograms
+// (the workspace of qb_radix_hist_lo_ws) for one group of layers at a time.
+// A device array, so the entry point allocates nothing; every GPU the
+// library runs on holds its own copy from the first use until the process
+// ends.  In host code `scratch` only names the symbol: its device address
+// comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[QB_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device, with that device current).
+int scratch_on_current_device(const char* fn, uint8_t** out) {
+  int dev = -1;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) return fail(QB_EHIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(ge));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QB_EUNSUPPORTED, "%s: device %d, the scratch table holds devices 0..%d", fn, dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(QB_EHIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+  return QB_OK;
+}
+
+// Workspace bytes of a group of Lg layers (the same layout and workgroup
+// count the launches use for that group).
+int64_t group_ws_bytes(int Lg, int64_t N, int E) {
+  return qbk::lo_ws_layout(Lg, E, qbk::radix_wg_per_layer(Lg, N, E)).bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+QB_API int qb_radix_lo_select_noalloc(const float* s, const float* alpha, int L, int64_t N, int E,
+                                      const int32_t* sel_hi, const int32_t* rank_lo, int32_t* hist_lo,
+                                      uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* hist_hi,
+                                      int32_t* err, qb_stream_t stream) {
+  const char* fn = "qb_radix_lo_select_noalloc";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!alpha || !sel_hi || !rank_lo || !q_out || !b || !bounds)
+    return fail(QB_EINVAL,
+                "%s: alpha (float [L][N]), sel_hi, rank_lo (int32 [L=%d][E=%d]), q_out, b (float [L][E]) and "
+                "bounds (float [L][2]) are required",
+                fn, L, E);
+  if ((hist_lo && !aligned4(hist_lo)) || (hist_hi && !aligned4(hist_hi)))
+    return fail(QB_EINVAL, "%s: hist_lo and hist_hi must be 4-byte aligned", fn);
+  const int64_t one = group_ws_bytes(1, N, E);
+  if (one > int64_t(QB_NOALLOC_SCRATCH_BYTES))
+    return fail(QB_EINVAL,
+                "%s: one layer of N=%lld x E=%d needs %lld bytes of scratch, more than the %lld this entry point "
+                "holds; use qb_radix_hist_lo_ws with a caller workspace",
+                fn, (long long)N, E, (long long)one, (long long)QB_NOALLOC_SCRATCH_BYTES);
+  uint8_t* ws = nullptr;
+  if (int rc = scratch_on_current_device(fn, &ws)) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // Layers in groups whose partials fit the scratch; each group's pass 2 and
+  // select run back to back on the stream, so the next group reuses it.
+  for (int l0 = 0; l0 < L;) {
+    int Lg = L - l0;
+    while (Lg > 1 && group_ws_bytes(Lg, N, E) > int64_t(QB_NOALLOC_SCRATCH_BYTES)) --Lg;
+    const int G = qbk::radix_wg_per_layer(Lg, N, E);
+    const int64_t le = int64_t(l0) * E;
+    int rc = qbk::launch_radix_hist_lo_ws(s + int64_t(l0) * N * E, alpha + int64_t(l0) * N, Lg, N, E,
+                                          sel_hi + le, ws, st);
+    if (rc != int(hipSuccess)) return hip_status(rc, fn);
+    rc = qbk::launch_select_lo_ws(Lg, E, G, ws, sel_hi + le, rank_lo + le, hist_lo ? hist_lo + le * 256 : nullptr,
+                                  key_out ? key_out + le : nullptr, q_out + le, b + le, bounds + 2 * int64_t(l0),
+                                  hist_hi ? hist_hi + le * 256 : nullptr, err, st);
+    if (rc != int(hipSuccess)) return hip_status(rc, fn);
+    l0 += Lg;
+  }
+  return ok();
 }
 
 QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N, int E,

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(PKG, "libqb.so")
 QB_OK, QB_EINVAL, QB_EUNSUPPORTED, QB_EHIP = 0, -1, -2, -3
 QB_SELECT_HI, QB_SELECT_LO, QB_SELECT_UNIFORM, QB_SELECT_FULL = 0, 1, 2, 3
 QB_ERR_ROW_TOTALS, QB_ERR_EMPTY, QB_ERR_RANK = 1, 2, 4
+QB_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 SUPPORTED_E = (16, 32, 64, 128, 256)
 MAX_K = 15
@@ -65,6 +66,7 @@ def lib() -> C.CDLL:
             "qb_radix_hist_lo_ws": [vp, vp, i32, i64, i32, vp, vp, i64, vp],
             "qb_select_lo_ws": [i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "qb_rank_average": [vp, i32, i32, vp, vp, vp],
+            "qb_radix_lo_select_noalloc": [vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -296,6 +298,23 @@ def qb_select_lo_ws(N, ws, sel_hi, rank_lo, q_out, b, bounds, hist_lo=None, key_
     _check(lib().qb_select_lo_ws(
         L, N, E, ws.data_ptr(), _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)),
         _ptr(rank_lo, torch.int32, "rank_lo", lead + (E,)),
+        _ptr(hist_lo, torch.int32, "hist_lo", lead + (E, 256), opt=True),
+        _ptr(key_out, torch.uint16, "key_out", lead + (E,), opt=True),
+        _ptr(q_out, torch.float32, "q_out", lead + (E,)), _ptr(b, torch.float32, "b", lead + (E,)),
+        _ptr(bounds, torch.float32, "bounds", lead + (2,)),
+        _ptr(hist_hi, torch.int32, "hist_hi", lead + (E, 256), opt=True),
+        _ptr(err, torch.int32, "err", (1,), opt=True), _stream(stream)))
+
+
+def qb_radix_lo_select_noalloc(s, alpha, sel_hi, rank_lo, q_out, b, bounds, hist_lo=None, key_out=None,
+                               err=None, hist_hi=None, stream=None):
+    """qb_radix_hist_lo_ws + qb_select_lo_ws on the library's own device
+    scratch (QB_NOALLOC_SCRATCH_BYTES per GPU): nothing is allocated.  Calls
+    that overlap on one GPU race."""
+    L, N, E, lead = _lne(s)
+    _check(lib().qb_radix_lo_select_noalloc(
+        _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
+        _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)), _ptr(rank_lo, torch.int32, "rank_lo", lead + (E,)),
         _ptr(hist_lo, torch.int32, "hist_lo", lead + (E, 256), opt=True),
         _ptr(key_out, torch.uint16, "key_out", lead + (E,), opt=True),
         _ptr(q_out, torch.float32, "q_out", lead + (E,)), _ptr(b, torch.float32, "b", lead + (E,)),

@@ -203,6 +203,32 @@ QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_
                            int32_t* hist_hi, int32_t* err, qb_stream_t stream);
 
 /*
+ * qb_radix_hist_lo_ws followed by qb_select_lo_ws, with the workspace taken
+ * from a device array inside the library instead of the caller: for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+ * and outputs as that pair of calls (hist_lo, key_out, hist_hi and err
+ * nullable; hist_hi zeroed in place when given), bit for bit.
+ *   The array holds QB_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the
+ *   library runs on, from the first call on that GPU until the process
+ *   ends.  Layers are processed in groups whose partial histograms fit it
+ *   (one 1,048,576 x 256 layer needs 48 MiB; 48 layers of 262,144 x 256
+ *   go in two groups, of 32 and 16); a shape where a single layer does not fit
+ *   (qb_hist_lo_workspace_bytes(1, N, E) > QB_NOALLOC_SCRATCH_BYTES) is
+ *   rejected with QB_EINVAL.  The contents on entry do not matter (every
+ *   partial row is written before it is read), so nothing is cleared.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on
+ *   one GPU (on different streams, or from different threads) race and
+ *   give wrong results; order them on one stream.  Nothing is allocated:
+ *   no hipMalloc, no hipFree.
+ */
+#define QB_NOALLOC_SCRATCH_BYTES (64LL << 20)
+QB_API int qb_radix_lo_select_noalloc(const float* s, const float* alpha, int L, int64_t N, int E,
+                                      const int32_t* sel_hi, const int32_t* rank_lo, int32_t* hist_lo,
+                                      uint16_t* key_out, float* q_out, float* b, float* bounds, int32_t* hist_hi,
+                                      int32_t* err, qb_stream_t stream);
+
+/*
  * K3 mode binning ("[Dev] Add global-batch quantile balancing", sections
  * "Quantile estimator" and "Implementation"): for the fp32 margin r,
  * bin = clamp(floor(fl32(fl32(r - lo) * fl32(n_bins / fl32(hi - lo)))), 0,

@@ -135,3 +135,19 @@ def test_product_code_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not pat.search(text), f
+
+
+def test_noalloc_rejects_a_layer_beyond_its_scratch(libqb):
+    """qb_radix_lo_select_noalloc refuses a shape whose single layer needs
+    more than its 64 MiB scratch, before any launch or device lookup."""
+    from exact_quantile_selection_amd import qb
+
+    N, E = 30_000_000, 256
+    assert libqb.qb_hist_lo_workspace_bytes(1, N, E) > qb.QB_NOALLOC_SCRATCH_BYTES
+    fake = 0x1000  # never dereferenced: validation fails first
+    rc = libqb.qb_radix_lo_select_noalloc(fake, fake, 1, N, E, fake, fake, None, None, fake, fake, fake, None,
+                                          None, None)
+    assert rc == qb.QB_EINVAL and "scratch" in _last(libqb) and "qb_radix_hist_lo_ws" in _last(libqb)
+    rc = libqb.qb_radix_lo_select_noalloc(fake, None, 1, 1024, E, fake, fake, None, None, fake, fake, fake,
+                                          None, None, None)
+    assert rc == qb.QB_EINVAL and "required" in _last(libqb)
