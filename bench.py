@@ -121,12 +121,42 @@ def time_graph(step, torch, steps, warmup):
 
 
 def time_kernels(step, torch, reps):
-    """Average duration of each launch of the step: HIP events on the stream
-    the kernels run on, around `reps` back-to-back launches of that one call
-    (so launch gaps do not count, as in a kernel trace)."""
+    """Average duration of each launch of the step: `reps` steps launched
+    eagerly in step order, a HIP event recorded on the kernels' stream
+    right before and right after every launch, so each kernel runs in the
+    same context as in the graph (after the same predecessor).  Returns
+    seconds per launch by name."""
     stream = torch.cuda.current_stream()
-    out = {}
-    for n, f in step.launches():
+    names = [n for n, _ in step.launches()]
+    ev = []
+    for _ in range(reps):
+        for n, f in step.launches():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            ev.append((n, e0, e1))
+    torch.cuda.synchronize()
+    out = {n: 0.0 for n in names}
+    for n, e0, e1 in ev:
+        out[n] += e0.elapsed_time(e1) * 1e-3 / reps
+    return out
+
+
+def ceilings(torch, s, reps=10):
+    """The measured streaming ceiling over the same score tensor: the plain
+    read kernel of libstreamprobe (include/stream_probe.h) at every (grid,
+    unroll) of a small sweep, each timed with HIP events around `reps`
+    back-to-back launches; the fastest is the ceiling."""
+    from exact_quantile_selection_amd import stream_probe as sp
+
+    cus = torch.cuda.get_device_properties(s.device).multi_processor_count
+    nbytes = s.numel() * 4
+    sink = torch.zeros(16 * cus, dtype=torch.int32, device=s.device)
+    stream = torch.cuda.current_stream()
+
+    def timed(f):
         f()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -135,31 +165,16 @@ def time_kernels(step, torch, reps):
             f()
         e1.record(stream)
         torch.cuda.synchronize()
-        out[n] = e0.elapsed_time(e1) * 1e-3 / reps
-    return out
+        return e0.elapsed_time(e1) * 1e-3 / reps
 
-
-def ceilings(torch, s, reps=10):
-    """Plain streaming kernels over the same score tensor, for context: a
-    read-only reduction and an elementwise copy (read + write)."""
-    out = {}
-    dst = torch.empty_like(s)
-    nbytes = s.numel() * 4
-    for name, f, moved in (("read_sum", lambda: s.sum(), nbytes),
-                           ("copy_add0", lambda: torch.add(s, 0.0, out=dst), 2 * nbytes)):
-        f()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            f()
-        e1.record()
-        torch.cuda.synchronize()
-        sec = e0.elapsed_time(e1) * 1e-3 / reps
-        out[name] = dict(us=round(sec * 1e6, 2), GBps=round(moved / sec / 1e9, 1), bytes=moved)
-    del dst
-    return out
+    sweep = {}
+    for per_cu in (1, 2, 4, 8, 16):
+        for u in (2, 4, 8):
+            sec = timed(lambda: sp.read(s, sink, per_cu * cus, u))
+            sweep[f"grid={per_cu * cus},unroll={u}"] = round(nbytes / sec / 1e9, 1)
+    best = max(sweep, key=sweep.get)
+    return {"read": dict(GBps=sweep[best], us=round(nbytes / sweep[best] / 1e3, 2), bytes=nbytes, best=best,
+                         frac_of_peak=round(sweep[best] / PEAK_HBM_GBS, 4), sweep=sweep)}
 
 
 def cpu_baseline(s_np, b_np, K, rows):
@@ -224,6 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--suite", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--contrast", action="store_true",
+                    help="also time the step with pass 2 merged by global atomics")
     ap.add_argument("--cpu-rows", type=int, default=1048576)
     ap.add_argument("--router", action="store_true",
                     help="time only the fused-router workload and print its JSON line")
@@ -268,14 +285,19 @@ def main():
     sec, _graph = time_graph(step, torch, args.steps, args.warmup)
     assert int(step.buf.err.item()) == 0
     b_ws = step.b.clone()
-    per_k = time_kernels(step, torch, max(5, args.steps))
     del _graph
-    # The same step with pass 2 merged by global atomics, for contrast.
-    atomic = EqbStep(s, b0, K, qb, torch, ws=False)
-    sec_atomic, _graph = time_graph(atomic, torch, args.steps, args.warmup)
-    assert int(atomic.buf.err.item()) == 0 and torch.equal(atomic.b, b_ws)
-    per_k_atomic = time_kernels(atomic, torch, max(5, args.steps))
-    del _graph, atomic
+    per_k = time_kernels(step, torch, args.steps)
+    contrast = None
+    if args.contrast:
+        # The same step with pass 2 merged by global atomics, for contrast.
+        atomic = EqbStep(s, b0, K, qb, torch, ws=False)
+        sec_atomic, _graph = time_graph(atomic, torch, args.steps, args.warmup)
+        assert int(atomic.buf.err.item()) == 0 and torch.equal(atomic.b, b_ws)
+        per_k_atomic = time_kernels(atomic, torch, args.steps)
+        del _graph, atomic
+        contrast = {"step_us": round(sec_atomic * 1e6, 2),
+                    "pass2_us": round(per_k_atomic["pass2_hist_lo"] * 1e6, 2),
+                    "select_lo_us": round(per_k_atomic["select_lo"] * 1e6, 2), "same_b_next": True}
     ceil = ceilings(torch, s)
 
     bpt = bytes_per_token(E)
@@ -308,18 +330,20 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(dominant),
+                     "traffic_source": "profiles/traffic_skew_N1048576_E256.txt (rocprofv3 FETCH_SIZE + "
+                                       "WRITE_SIZE per dispatch, calibrated on a copy of known size; null "
+                                       "when the pass sources changed since)",
+                     "avg_launch_us": round(per_k[dominant] * 1e6, 2),
+                     "timing": f"HIP events around each launch on its stream, {args.steps} eager steps in "
+                               "step order after the timed graph replay",
+                     "frac_of_measured_read_ceiling": round(achieved / ceil["read"]["GBps"], 4),
                      "algorithmic_bytes_per_launch": dom_bytes},
         "kernels": kernels,
-        "pass2_merge": {"workspace": {"step_us": round(sec * 1e6, 2),
-                                      "pass2_us": kernels["pass2_hist_lo"]["us"],
-                                      "select_lo_us": kernels["select_lo"]["us"]},
-                        "global_atomics": {"step_us": round(sec_atomic * 1e6, 2),
-                                           "pass2_us": round(per_k_atomic["pass2_hist_lo"] * 1e6, 2),
-                                           "select_lo_us": round(per_k_atomic["select_lo"] * 1e6, 2)},
-                        "same_b_next": True},
         "stream_ceilings": ceil,
     }
 
+    if contrast:
+        out["pass2_global_atomics_step"] = contrast
     if args.suite:
         out["suite"] = suite(torch, qb, synth, dev, args)
 

@@ -18,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqb.so")
+# the diagnostic streaming kernels (the measured HBM ceiling), a separate library
+PROBE_LIB = os.path.join(PKG, "libstreamprobe.so")
 ARCH = os.environ.get("QB_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -72,7 +74,22 @@ def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str |
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, lib)
+    if not out:
+        build_probe(verbose)
     return lib
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile libstreamprobe.so (include/stream_probe.h)."""
+    os.makedirs(BUILD, exist_ok=True)
+    obj = _compile(("stream_probe.o", "stream_probe.hip", []), verbose, BUILD, [])
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -137,6 +137,34 @@ def test_product_code_never_touches_the_oracle():
                 assert not pat.search(text), f
 
 
+PROBE_HEADER = os.path.join(ROOT, "include", "stream_probe.h")
+PROBE_LIB = os.path.join(ROOT, "exact_quantile_selection_amd", "libstreamprobe.so")
+
+
+def test_stream_probe_exports_its_header():
+    """The diagnostic streaming library exports exactly what its header
+    declares and rejects bad arguments without a launch."""
+    if not os.path.exists(PROBE_LIB):
+        from exact_quantile_selection_amd import build
+
+        build.build_probe()
+    declared = sorted(set(re.findall(r"SP_API\s+[\w\s\*]+?\b(sp_\w+)\s*\(", open(PROBE_HEADER).read())))
+    assert declared == ["sp_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True).stdout
+    assert sorted(set(re.findall(r" T (sp_\w+)", out))) == declared
+    import torch  # noqa: F401
+
+    from exact_quantile_selection_amd import stream_probe
+
+    L = stream_probe.lib()
+    fake = 0x1000  # never dereferenced: validation fails first
+    assert L.sp_read(None, 1024, 1, 8, fake, None) == -1
+    assert L.sp_read(fake, 1000, 1, 8, fake, None) == -1    # not a multiple of 16
+    assert L.sp_read(fake + 4, 1024, 1, 8, fake, None) == -1  # misaligned
+    assert L.sp_read(fake, 1024, 1, 5, fake, None) == -1    # unroll
+    assert L.sp_read(fake, 1024, 0, 8, fake, None) == -1    # grid
+
+
 def test_noalloc_rejects_a_layer_beyond_its_scratch(libqb):
     """qb_radix_lo_select_noalloc refuses a shape whose single layer needs
     more than its 64 MiB scratch, before any launch or device lookup."""
