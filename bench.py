@@ -674,17 +674,32 @@ def router_suite(torch, qb, synth, dev, args):
         return e0.elapsed_time(e1) * 1e-3 / n
 
     n = max(3, args.steps // 2)
-    t_fused = reps(lambda: qb.qb_router_fused(hidden, w, b, K, s, alpha), n)
-    t_pass1 = reps(lambda: qb.qb_margins_topk(s, b, K, alpha), n)
-    t_gemm = t_fused - t_pass1
+    hist = buf.hist_hi
+    # pass 1 fused into the GEMM's epilogue, against the GEMM alone followed
+    # by the standalone pass 1 over the scores it wrote (same results)
+    t_fused = reps(lambda: qb.qb_router_fused(hidden, w, b, K, s, alpha, load=load, hist_hi=hist), n)
+    t_gemm = reps(lambda: qb.qb_router_scores(hidden, w, s), n)
+    t_pass1 = reps(lambda: qb.qb_margins_topk(s, b, K, alpha, load=load, hist_hi=hist), n)
+    qb.qb_fill_i32(hist, 0)
+    qb.qb_fill_i32(load, 0)
 
     ws = torch.empty(qb.qb_hist_lo_workspace_bytes(1, N, E), dtype=torch.uint8, device=dev)
 
     class Chain:
+        """Router forward, the EQB update and LEI; pass 1 either in the
+        GEMM's epilogue (fused) or as its own pass over the scores."""
+
+        def __init__(self_, fused):
+            self_.fused = fused
+
         def run(self_):
             b.copy_(b0)
             qb.qb_fill_i32(load, 0)
-            qb.qb_router_fused(hidden, w, b, K, s, alpha, load=load, hist_hi=buf.hist_hi)
+            if self_.fused:
+                qb.qb_router_fused(hidden, w, b, K, s, alpha, load=load, hist_hi=buf.hist_hi)
+            else:
+                qb.qb_router_scores(hidden, w, s)
+                qb.qb_margins_topk(s, b, K, alpha, load=load, hist_hi=buf.hist_hi)
             qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi,
                                 rank_lo=buf.rank_lo, err=buf.err)
             qb.qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws)
@@ -692,17 +707,27 @@ def router_suite(torch, qb, synth, dev, args):
                                err=buf.err, hist_hi=buf.hist_hi)  # clears hist_hi for the next run
             qb.qb_lei_grad(grad, load, K, 1e-5)
 
-    sec, _ = time_graph(Chain(), torch, n, 1)
+    sec, _ = time_graph(Chain(True), torch, n, 1)
+    b_fused = b.clone()
+    sec_unfused, _ = time_graph(Chain(False), torch, n, 1)
+    assert torch.equal(b, b_fused)
     flops = 2.0 * N * H * E
     gemm_bytes = N * H * 2 + N * E * 4 + E * H * 2
     out = dict(N=N, H=H, E=E, K=K,
+               fused_gemm_pass1_us=round(t_fused * 1e6, 2),
                gemm_sigmoid_us=round(t_gemm * 1e6, 2),
+               pass1_on_scores_us=round(t_pass1 * 1e6, 2),
+               unfused_gemm_plus_pass1_us=round((t_gemm + t_pass1) * 1e6, 2),
                gemm_mfma_TFLOPs=round(flops / t_gemm / 1e12, 1),
                gemm_mfma_frac_of_2500=round(flops / t_gemm / 2.5e15, 4),
                gemm_hbm_GBps=round(gemm_bytes / t_gemm / 1e9, 1),
-               pass1_on_scores_us=round(t_pass1 * 1e6, 2),
-               chain_us=round(sec * 1e6, 2), chain_tokens_per_s=N / sec,
-               chain="router GEMM + sigmoid + pass 1, select HI, pass 2, select LO, LEI")
+               fused_hbm_GBps=round(gemm_bytes / t_fused / 1e9, 1),
+               chain_fused_us=round(sec * 1e6, 2), chain_fused_tokens_per_s=N / sec,
+               chain_unfused_us=round(sec_unfused * 1e6, 2), chain_unfused_tokens_per_s=N / sec_unfused,
+               chain_same_b_next=True,
+               chain="router GEMM + sigmoid, pass 1 (in the GEMM's epilogue, or after it), select HI, "
+                     "pass 2, select LO, LEI; one graph of the steps",
+               timing="HIP events around back-to-back launches of each call")
     del hidden, w, grad, s
     torch.cuda.empty_cache()
     return out

@@ -525,9 +525,24 @@ QB_API int qb_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N,
   if ((logits_out && !aligned4(logits_out)) || !aligned4(b) || !aligned4(alpha) || (load && !aligned4(load)))
     return fail(QB_EINVAL, "%s: logits_out, b, alpha and load must be 4-byte aligned", fn);
   if (hist_hi && !aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
-  int rc = qbk::launch_router_gemm(hidden, w, N, H, E, s_out, logits_out, stream);
-  if (rc != int(hipSuccess)) return hip_status(rc, fn);
-  return hip_status(qbk::launch_margins_topk(s_out, b, 1, N, E, K, alpha, load, hist_hi, stream), fn);
+  return hip_status(
+      qbk::launch_router_fused(hidden, w, N, H, E, s_out, logits_out, b, K, alpha, load, hist_hi, stream), fn);
+}
+
+QB_API int qb_router_scores(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E, float* s_out,
+                            float* logits_out, qb_stream_t stream) {
+  const char* fn = "qb_router_scores";
+  if (!hidden || !w || !s_out)
+    return fail(QB_EINVAL, "%s: hidden (bf16 [N][H]), w (bf16 [E][H]) and s_out (float [N][E]) are required", fn);
+  if (N < 1 || N > INT32_MAX)
+    return fail(QB_EINVAL, "%s: N=%lld, expected 1 <= N < 2^31", fn, (long long)N);
+  if (H < 64 || H % 64 != 0) return fail(QB_EINVAL, "%s: H=%d, expected a positive multiple of 64", fn, H);
+  if (E != 32 && E != 64 && E != 128 && E != 256)
+    return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {32, 64, 128, 256}", fn, E);
+  if (!aligned16(hidden) || !aligned16(w) || !aligned16(s_out))
+    return fail(QB_EINVAL, "%s: hidden, w and s_out must be 16-byte aligned", fn);
+  if (logits_out && !aligned4(logits_out)) return fail(QB_EINVAL, "%s: logits_out must be 4-byte aligned", fn);
+  return hip_status(qbk::launch_router_gemm(hidden, w, N, H, E, s_out, logits_out, stream), fn);
 }
 
 QB_API int qb_lei_grad(float* g, const int32_t* load, int64_t N, int E, int K, float eta,

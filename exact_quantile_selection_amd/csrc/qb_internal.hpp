@@ -75,6 +75,9 @@ int launch_bias_bounds(const float* b, int L, int E, float* bounds, hipStream_t 
 int launch_fill_i32(int32_t* dst, int64_t count, int32_t value, hipStream_t st);
 int launch_router_gemm(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E,
                        float* s_out, float* logits_out, hipStream_t st);
+int launch_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E, float* s_out,
+                        float* logits_out, const float* b, int K, float* alpha, int32_t* load, int32_t* hist_hi,
+                        hipStream_t st);
 int launch_lei(float* g, const int32_t* load, int64_t N, int E, int K, float eta,
                hipStream_t st);
 

@@ -95,13 +95,193 @@ __device__ __forceinline__ float rg_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-template <int E, int BK, int S>
+// ---------------------------------------------------------------------------
+// Pass 1 in the GEMM epilogue ("[Dev] Add global-batch quantile balancing",
+// section "Implementation": the fused routing path adds bin classification
+// and histogram atomics in shared memory to the router kernel; section
+// "Quantile estimator": alpha, the margins; "Exact Quantile Balancing and
+// Load-Error Injection for Mixture-of-Experts", EQB paragraph: the
+// high-byte histogram of the bf16 margins).
+//
+// After the K loop a token's E scores sit in four places (two lanes of each
+// of two waves).  The workgroup has just stored its 256 rows of scores, so
+// once its waves meet at a barrier it reads them back, still in L2, row by
+// row: each row by LPR = E/32 lanes holding 32 scores each, in the layout of
+// the standalone pass 1 -- top-(K+1) of s + b by v_med3 insertion and DPP
+// merges (quad xor 1, quad xor 2, half-row mirror), alpha, the top-K loads
+// and the high-byte key histogram.  (Passing the scores through LDS instead
+// keeps the 128 accumulators live beside the row state and spills.)
+//
+// The high-byte histogram is counted in LDS with the standalone pass's packed
+// 16-bit counters (E x 512 bytes: 128 KiB at E = 256, in the LDS the operand
+// ring used) and flushed once per workgroup, one 64-bit device atomic per two
+// adjacent bins.  Each lane keeps the rows of two steps in flight.
+template <int E>
+struct RfShape {
+  static constexpr int LPR = E / 32;                       // lanes per row
+  static constexpr int F4 = 8;                             // float4 per lane (32 scores)
+  static constexpr int RPW = kWave / LPR;                  // rows per wave and step
+  static constexpr int R = kRgWaves * RPW < kRgBM ? kRgWaves * RPW : kRgBM;  // rows per step
+  static constexpr int WAVES_USED = R / RPW;
+  static constexpr int NP = kRgBM / R;                     // steps per workgroup
+  static constexpr int HIST_BYTES = E * 512;
+  static constexpr int BIAS_OFF = HIST_BYTES;
+  static constexpr int LOAD_OFF = BIAS_OFF + E * 4;
+  static constexpr int BYTES = LOAD_OFF + E * 4;
+  static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
+  static_assert(kRgBM % R == 0, "steps");
+};
+
+// DPP half-row mirror: lane i of each group of 8 reads lane 7 - i.
+constexpr int kHalfMirror = 0x141;
+
+template <int P, int LPR>
+__device__ __forceinline__ void rf_merge_rows(float (&t)[P]) {
+  if constexpr (LPR >= 2) top_merge<P, kQuadXor1>(t);
+  if constexpr (LPR >= 4) top_merge<P, kQuadXor2>(t);
+  if constexpr (LPR >= 8) top_merge<P, kHalfMirror>(t);
+}
+
+template <int LPR>
+__device__ __forceinline__ int rf_row_sum(int x) {
+  if constexpr (LPR >= 2) x += quad_mov_i<kQuadXor1>(x);
+  if constexpr (LPR >= 4) x += quad_mov_i<kQuadXor2>(x);
+  if constexpr (LPR >= 8) x += quad_mov_i<kHalfMirror>(x);
+  return x;
+}
+
+template <int E, int P>
+__device__ __forceinline__ void rf_epilogue(uint8_t* lds, int lane, int wave, int tid, int64_t m0, int64_t N,
+                                            const float* s_rows, const float* bias, int K, float* alpha,
+                                            int32_t* load, int32_t* hist_hi) {
+  using F = RfShape<E>;
+  constexpr int LPR = F::LPR;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(lds);
+  float* lds_b = reinterpret_cast<float*>(lds + F::BIAS_OFF);
+  int32_t* lds_load = reinterpret_cast<int32_t*>(lds + F::LOAD_OFF);
+  const bool want_hist = hist_hi != nullptr, want_load = load != nullptr;
+
+  if (want_hist) hist16_zero<E>(hist, tid, kRgThreads);
+  for (int j = tid; j < E; j += kRgThreads) {
+    lds_b[j] = bias[j];
+    lds_load[j] = 0;
+  }
+  // the barrier publishes the LDS set-up and this workgroup's score stores
+  __syncthreads();
+  const int rho = lane / LPR, ql = lane % LPR;
+  if (wave < F::WAVES_USED) {
+    // rows of up to two steps in flight: step p + 2 is loaded once step p
+    // has been ranked
+    constexpr int NB = F::NP < 2 ? F::NP : 2;
+    float4 xb[NB][F::F4];
+    auto fetch = [&](int p, float4(&x)[F::F4]) {
+      const int64_t row = m0 + int64_t(p) * F::R + wave * F::RPW + rho;
+      const float* src = s_rows + (row < N ? row : N - 1) * E;
+#pragma unroll
+      for (int t = 0; t < F::F4; ++t) x[t] = ld4(src + 4 * (LPR * ((t + rho) & (F::F4 - 1)) + ql));
+    };
+#pragma unroll
+    for (int p = 0; p < NB; ++p) fetch(p, xb[p]);
+#pragma unroll
+    for (int p = 0; p < F::NP; ++p) {
+      float4(&xp)[F::F4] = xb[p % NB];
+      const int64_t row = m0 + int64_t(p) * F::R + wave * F::RPW + rho;
+      const bool valid = row < N;
+      float top[P];
+#pragma unroll
+      for (int k = 0; k < P; ++k) top[k] = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < F::F4; ++t) {
+        const int Q = LPR * ((t + rho) & (F::F4 - 1)) + ql;
+        const float4 bb = *reinterpret_cast<const float4*>(lds_b + 4 * Q);
+        top_insert<P>(top, xp[t].x + bb.x);
+        top_insert<P>(top, xp[t].y + bb.y);
+        top_insert<P>(top, xp[t].z + bb.z);
+        top_insert<P>(top, xp[t].w + bb.w);
+      }
+      rf_merge_rows<P, LPR>(top);
+      float a = top[0];
+#pragma unroll
+      for (int k = 1; k < P; ++k) a = k == K ? top[k] : a;
+      if (valid && ql == 0) __builtin_nontemporal_store(a, alpha + row);
+      if (want_load) {
+        // members: v > alpha, plus the lowest-index elements equal to alpha
+        // up to K in all.  Bit 4u + c of a lane's masks is its element of
+        // expert 4 (LPR u + ql) + c, so bit order is expert order.
+        uint32_t gt = 0;
+#pragma unroll
+        for (int t = 0; t < F::F4; ++t) {
+          const int u = (t + rho) & (F::F4 - 1);
+          const float4 bb = *reinterpret_cast<const float4*>(lds_b + 4 * (LPR * u + ql));
+          gt |= (xp[t].x + bb.x > a ? 1u : 0u) << (4 * u);
+          gt |= (xp[t].y + bb.y > a ? 1u : 0u) << (4 * u + 1);
+          gt |= (xp[t].z + bb.z > a ? 1u : 0u) << (4 * u + 2);
+          gt |= (xp[t].w + bb.w > a ? 1u : 0u) << (4 * u + 3);
+        }
+        uint32_t mem = gt;
+        const int need = K - rf_row_sum<LPR>(__popc(gt));
+        if (__ballot(valid && need > 0) != 0) {  // a tie at alpha somewhere in the wave
+          uint32_t eq = 0;
+#pragma unroll
+          for (int t = 0; t < F::F4; ++t) {
+            const int u = (t + rho) & (F::F4 - 1);
+            const float4 bb = *reinterpret_cast<const float4*>(lds_b + 4 * (LPR * u + ql));
+            eq |= (xp[t].x + bb.x == a ? 1u : 0u) << (4 * u);
+            eq |= (xp[t].y + bb.y == a ? 1u : 0u) << (4 * u + 1);
+            eq |= (xp[t].z + bb.z == a ? 1u : 0u) << (4 * u + 2);
+            eq |= (xp[t].w + bb.w == a ? 1u : 0u) << (4 * u + 3);
+          }
+          uint32_t M[LPR];
+#pragma unroll
+          for (int q2 = 0; q2 < LPR; ++q2) M[q2] = __shfl(eq, rho * LPR + q2);
+          if (valid && need > 0) {
+            uint32_t e = eq;
+            while (e) {
+              const int bit = __builtin_ctz(e);
+              e &= e - 1;
+              const int u = bit >> 2, c = bit & 3;
+              int rank = 0;
+#pragma unroll
+              for (int q2 = 0; q2 < LPR; ++q2) {
+                const int nb = q2 < ql ? 4 * (u + 1) : (q2 > ql ? 4 * u : 4 * u + c);
+                rank += __popc(M[q2] & (nb >= 32 ? 0xFFFFFFFFu : ((1u << nb) - 1u)));
+              }
+              if (rank < need) mem |= 1u << bit;
+            }
+          }
+        }
+        if (valid) {
+          while (mem) {
+            const int bit = __builtin_ctz(mem);
+            mem &= mem - 1;
+            atomicAdd(&lds_load[4 * (LPR * (bit >> 2) + ql) + (bit & 3)], 1);
+          }
+        }
+      }
+      if (want_hist && valid) {
+#pragma unroll
+        for (int t = 0; t < F::F4; ++t) {
+          const int Q = LPR * ((t + rho) & (F::F4 - 1)) + ql;
+          const uint32_t swz = hist16_swizzle2(Q);
+          hist16_add_hi(hist, Q, 0, key2(bf16x2_rne(a - xp[t].x, a - xp[t].y)) ^ swz);
+          hist16_add_hi(hist, Q, 2, key2(bf16x2_rne(a - xp[t].z, a - xp[t].w)) ^ swz);
+        }
+      }
+      if (p + NB < F::NP) fetch(p + NB, xp);
+    }
+  }
+  __syncthreads();
+  if (want_hist) hist16_flush_pairs<E>(hist, hist_hi, tid, kRgThreads, int(blockIdx.x));
+  if (want_load)
+    for (int j = tid; j < E; j += kRgThreads)
+      if (lds_load[j]) atomicAdd(load + j, lds_load[j]);
+}
+
+template <int E, int BK, int S, int P>
 __global__ __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void k_router_gemm(const uint16_t* __restrict__ hidden,
-                                                            const uint16_t* __restrict__ w,
-                                                            int64_t N, int H,
-                                                            float* __restrict__ s_out,
-                                                            float* __restrict__ logits_out) {
+void k_router_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ w, int64_t N, int H,
+                   float* __restrict__ s_out, float* __restrict__ logits_out, const float* __restrict__ bias,
+                   int K, float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi) {
   using Sh = RgShape<E>;
   constexpr int TM = Sh::TM, TN = Sh::TN;
   constexpr int CPR = BK / 8;                        // 16-byte chunks per tile row
@@ -114,7 +294,10 @@ void k_router_gemm(const uint16_t* __restrict__ hidden,
   constexpr int PER_STAGE = A_PER_WAVE + B_PER_WAVE;  // loads per wave per stage
   static_assert(A_INSTR % kRgWaves == 0, "A tile split");
   static_assert(BK % 16 == 0 && CPR <= 16 && 16 % CPR == 0, "BK");
-  __shared__ __align__(1024) uint8_t lds[S * (A_BYTES + B_BYTES)];
+  constexpr int RING_BYTES = S * (A_BYTES + B_BYTES);
+  constexpr int LDS_BYTES = P == 0 ? RING_BYTES
+                                   : (RING_BYTES > RfShape<E>::BYTES ? RING_BYTES : RfShape<E>::BYTES);
+  __shared__ __align__(1024) uint8_t lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -235,46 +418,77 @@ void k_router_gemm(const uint16_t* __restrict__ hidden,
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int64_t row = m0 + (wm * TM + tm) * 32 + (lane % 32);
-    if (row >= N) continue;
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = (wn * TN + tn) * 32 + 8 * q + 4 * (lane / 32);
-        const float x0 = acc[tm][tn][4 * q], x1 = acc[tm][tn][4 * q + 1], x2 = acc[tm][tn][4 * q + 2],
-                    x3 = acc[tm][tn][4 * q + 3];
-        *reinterpret_cast<float4*>(s_out + row * E + col) =
-            make_float4(rg_sigmoid(x0), rg_sigmoid(x1), rg_sigmoid(x2), rg_sigmoid(x3));
-        if (logits_out) {  // 4-byte aligned only
+        if (logits_out && row < N) {  // 4-byte aligned only
           float* lo = logits_out + row * E + col;
-          lo[0] = x0;
-          lo[1] = x1;
-          lo[2] = x2;
-          lo[3] = x3;
+          lo[0] = acc[tm][tn][4 * q];
+          lo[1] = acc[tm][tn][4 * q + 1];
+          lo[2] = acc[tm][tn][4 * q + 2];
+          lo[3] = acc[tm][tn][4 * q + 3];
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[tm][tn][4 * q + c] = rg_sigmoid(acc[tm][tn][4 * q + c]);
+        if (row < N)
+          *reinterpret_cast<float4*>(s_out + row * E + col) =
+              make_float4(acc[tm][tn][4 * q], acc[tm][tn][4 * q + 1], acc[tm][tn][4 * q + 2],
+                          acc[tm][tn][4 * q + 3]);
       }
+  }
+  if constexpr (P > 0) {
+    // every wave is past its last LDS read of the ring
+    __syncthreads();
+    rf_epilogue<E, P>(lds, lane, wave, tid, m0, N, s_out, bias, K, alpha, load, hist_hi);
   }
 }
 
-template <int E>
+template <int E, int P>
 static int launch_rg(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, float* s_out,
-                     float* logits_out, hipStream_t st) {
+                     float* logits_out, const float* b, int K, float* alpha, int32_t* load, int32_t* hist_hi,
+                     hipStream_t st) {
   const dim3 grid{unsigned((N + kRgBM - 1) / kRgBM), 1u, 1u};
   const dim3 block{unsigned(kRgThreads), 1u, 1u};
-  hipLaunchKernelGGL((k_router_gemm<E, QB_RG_BK, QB_RG_STAGES>), grid, block, 0, st, hidden, w, N, H,
-                     s_out, logits_out);
+  hipLaunchKernelGGL((k_router_gemm<E, QB_RG_BK, QB_RG_STAGES, P>), grid, block, 0, st, hidden, w, N, H, s_out,
+                     logits_out, b, K, alpha, load, hist_hi);
   return int(hipGetLastError());
 }
 
 int launch_router_gemm(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E,
                        float* s_out, float* logits_out, hipStream_t st) {
   switch (E) {
-    case 32: return launch_rg<32>(hidden, w, N, H, s_out, logits_out, st);
-    case 64: return launch_rg<64>(hidden, w, N, H, s_out, logits_out, st);
-    case 128: return launch_rg<128>(hidden, w, N, H, s_out, logits_out, st);
-    case 256: return launch_rg<256>(hidden, w, N, H, s_out, logits_out, st);
+    case 32: return launch_rg<32, 0>(hidden, w, N, H, s_out, logits_out, nullptr, 0, nullptr, nullptr, nullptr, st);
+    case 64: return launch_rg<64, 0>(hidden, w, N, H, s_out, logits_out, nullptr, 0, nullptr, nullptr, nullptr, st);
+    case 128:
+      return launch_rg<128, 0>(hidden, w, N, H, s_out, logits_out, nullptr, 0, nullptr, nullptr, nullptr, st);
+    case 256:
+      return launch_rg<256, 0>(hidden, w, N, H, s_out, logits_out, nullptr, 0, nullptr, nullptr, nullptr, st);
     default: return int(hipErrorInvalidValue);
   }
+}
+
+template <int P>
+static int launch_rf_p(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E, float* s_out,
+                       float* logits_out, const float* b, int K, float* alpha, int32_t* load, int32_t* hist_hi,
+                       hipStream_t st) {
+  switch (E) {
+    case 32: return launch_rg<32, P>(hidden, w, N, H, s_out, logits_out, b, K, alpha, load, hist_hi, st);
+    case 64: return launch_rg<64, P>(hidden, w, N, H, s_out, logits_out, b, K, alpha, load, hist_hi, st);
+    case 128: return launch_rg<128, P>(hidden, w, N, H, s_out, logits_out, b, K, alpha, load, hist_hi, st);
+    case 256: return launch_rg<256, P>(hidden, w, N, H, s_out, logits_out, b, K, alpha, load, hist_hi, st);
+    default: return int(hipErrorInvalidValue);
+  }
+}
+
+// Router GEMM with pass 1 in its epilogue: lists of 8 for K <= 7, of 16 up
+// to K = 15.
+int launch_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E, float* s_out,
+                        float* logits_out, const float* b, int K, float* alpha, int32_t* load, int32_t* hist_hi,
+                        hipStream_t st) {
+  if (K + 1 <= 8) return launch_rf_p<8>(hidden, w, N, H, E, s_out, logits_out, b, K, alpha, load, hist_hi, st);
+  return launch_rf_p<16>(hidden, w, N, H, E, s_out, logits_out, b, K, alpha, load, hist_hi, st);
 }
 
 }  // namespace qbk

@@ -57,6 +57,7 @@ def lib() -> C.CDLL:
             "qb_fill_i32": [vp, i64, C.c_int32, vp],
             "qb_lei_grad": [vp, vp, i64, i32, i32, f32, vp],
             "qb_router_fused": [vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
+            "qb_router_scores": [vp, vp, i64, i32, i32, vp, vp, vp],
             "qb_microbatch_loads": [vp, vp, i32, i64, i32, i32, i64, vp, vp, vp],
             "qb_margins_topk_mb": [vp, vp, i32, i64, i32, i32, vp, vp, vp, i64, vp, vp],
             "qb_maxvio": [vp, i32, i32, i32, i32, i64, vp, vp, vp, vp],
@@ -193,7 +194,8 @@ def qb_fill_i32(t, value=0, stream=None):
 def qb_router_fused(hidden, w, b, K, s_out, alpha, logits_out=None, load=None, hist_hi=None,
                     stream=None):
     """hidden: bf16 [N, H]; w: bf16 [E, H] (nn.Linear layout).  Writes s_out
-    = sigmoid(hidden @ w.T) and runs pass 1 on it."""
+    = sigmoid(hidden @ w.T); the same kernel's epilogue computes alpha, the
+    top-K loads and the high-byte histogram (pass 1) of those scores."""
     N, H = hidden.shape
     E = w.shape[0]
     _check(lib().qb_router_fused(
@@ -203,6 +205,16 @@ def qb_router_fused(hidden, w, b, K, s_out, alpha, logits_out=None, load=None, h
         _ptr(alpha, torch.float32, "alpha", (N,)),
         _ptr(load, torch.int32, "load", (E,), opt=True),
         _ptr(hist_hi, torch.int32, "hist_hi", (E, 256), opt=True), _stream(stream)))
+
+
+def qb_router_scores(hidden, w, s_out, logits_out=None, stream=None):
+    """The router GEMM + sigmoid alone: s_out = sigmoid(hidden @ w.T)."""
+    N, H = hidden.shape
+    E = w.shape[0]
+    _check(lib().qb_router_scores(
+        _ptr(hidden, torch.bfloat16, "hidden"), _ptr(w, torch.bfloat16, "w", (E, H)), N, H, E,
+        _ptr(s_out, torch.float32, "s_out", (N, E)),
+        _ptr(logits_out, torch.float32, "logits_out", (N, E), opt=True), _stream(stream)))
 
 
 def qb_lei_grad(g, load, K, eta, stream=None):

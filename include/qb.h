@@ -251,16 +251,19 @@ QB_API int qb_bias_bounds(const float* b, int L, int E, float* bounds, qb_stream
 QB_API int qb_fill_i32(int32_t* dst, int64_t count, int32_t value, qb_stream_t stream);
 
 /*
- * Router forward fused with pass 1, for one layer: logits = hidden . w^T on
- * MFMA (bf16 inputs, fp32 accumulation), s = 1 / (1 + 2^(-x log2 e)) with
- * a two-constant (Cody-Waite) split of x log2 e, the hardware exp2 and
- * reciprocal (within a few ulp of the correctly rounded sigmoid; results
- * below 2^-126 flush to 0), written to s_out; then exactly qb_margins_topk
- * on s_out (alpha,
- * optional top-K loads, optional high-byte histogram).  The sigmoid scores
- * are those of "[Dev] Add global-batch quantile balancing", section
- * "Quantile estimator"; the router forward is the one its Validation section
- * exercises.
+ * Router forward with pass 1 fused into the GEMM's epilogue, for one layer
+ * ("[Dev] Add global-batch quantile balancing", section "Implementation":
+ * the fused routing path classifies bins and adds histogram atomics in the
+ * router kernel itself; its Validation section exercises the router
+ * forward).  logits = hidden . w^T on MFMA (bf16 inputs, fp32 accumulation);
+ * s = 1 / (1 + 2^(-x log2 e)) with a two-constant (Cody-Waite) split of
+ * x log2 e, the hardware exp2 and reciprocal (within a few ulp of the
+ * correctly rounded sigmoid; results below 2^-126 flush to 0), written to
+ * s_out.  Each workgroup then reads its just-written rows back (from L2)
+ * and computes, as qb_margins_topk does on s_out -- same results bit for
+ * bit: alpha, the top-K loads (load += ...) and the high-byte histogram of
+ * the bf16 margin keys (hist_hi += ...), counted in LDS and flushed with
+ * device atomics; no second pass over the scores.
  *   hidden  uint16 bf16 bit patterns [N][H], 16-byte aligned, H % 64 == 0
  *   w       uint16 bf16 bit patterns [E][H] (nn.Linear weight layout)
  *   b       float [E]; s_out float [N][E] (16-byte aligned);
@@ -271,6 +274,15 @@ QB_API int qb_fill_i32(int32_t* dst, int64_t count, int32_t value, qb_stream_t s
 QB_API int qb_router_fused(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E,
                            int K, const float* b, float* s_out, float* logits_out, float* alpha,
                            int32_t* load, int32_t* hist_hi, qb_stream_t stream);
+
+/*
+ * The router GEMM and sigmoid of qb_router_fused alone (s_out and the
+ * optional logits_out, same values bit for bit), without the pass-1
+ * epilogue: for callers that run pass 1 themselves (qb_margins_topk) or
+ * only need the scores.  Same layouts and limits.
+ */
+QB_API int qb_router_scores(const uint16_t* hidden, const uint16_t* w, int64_t N, int H, int E,
+                            float* s_out, float* logits_out, qb_stream_t stream);
 
 /*
  * Top-K expert loads per microbatch, for the local-balance metric

@@ -179,3 +179,21 @@ def test_noalloc_rejects_a_layer_beyond_its_scratch(libqb):
     rc = libqb.qb_radix_lo_select_noalloc(fake, None, 1, 1024, E, fake, fake, None, None, fake, fake, fake,
                                           None, None, None)
     assert rc == qb.QB_EINVAL and "required" in _last(libqb)
+
+
+def test_router_entry_points_reject_bad_shapes(libqb):
+    """qb_router_fused and qb_router_scores refuse unsupported shapes before
+    any launch."""
+    from exact_quantile_selection_amd import qb
+
+    fake = 0x1000  # never dereferenced: validation fails first
+    rc = libqb.qb_router_scores(fake, fake, 1024, 100, 256, fake, None, None)
+    assert rc == qb.QB_EINVAL and "H=100" in _last(libqb)
+    rc = libqb.qb_router_scores(fake, fake, 1024, 128, 48, fake, None, None)
+    assert rc == qb.QB_EUNSUPPORTED and "E=48" in _last(libqb)
+    rc = libqb.qb_router_scores(fake + 2, fake, 1024, 128, 256, fake, None, None)
+    assert rc == qb.QB_EINVAL and "aligned" in _last(libqb)
+    rc = libqb.qb_router_fused(fake, fake, 1024, 128, 256, 16, fake, fake, None, fake, None, None, None)
+    assert rc == qb.QB_EUNSUPPORTED and "K=16" in _last(libqb)
+    rc = libqb.qb_router_fused(fake, fake, 1024, 128, 256, 6, fake, fake, None, fake, None, fake + 4, None)
+    assert rc == qb.QB_EINVAL and "8-byte" in _last(libqb)

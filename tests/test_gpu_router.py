@@ -1,5 +1,6 @@
-"""GPU checks of the fused router path (MFMA GEMM + sigmoid + pass 1), and of
-the whole EQB + LEI chain on the scores it produces.
+"""GPU checks of the fused router path (MFMA GEMM + sigmoid, with pass 1 in
+the GEMM's epilogue), of the scores-only GEMM, and of the whole EQB + LEI
+chain on the scores they produce.
 
 Logits: within |d| <= 1e-2 * |ref| + 1e-4 * rms(ref) of a float64 host GEMM
 of the same bf16 inputs (bf16 x bf16 products are exact in fp32; the only
@@ -66,7 +67,8 @@ def run_router(hidden_np, w_np, b_np, K, with_logits=True):
 
 
 @pytest.mark.parametrize("N,H,E,K", [(1000, 256, 256, 6), (333, 128, 64, 4), (129, 64, 32, 2),
-                                     (4096, 512, 128, 7), (700, 128, 256, 8)])
+                                     (4096, 512, 128, 7), (700, 128, 256, 8), (300, 64, 32, 15),
+                                     (513, 128, 128, 15), (257, 64, 256, 1)])
 def test_router_small(O, N, H, E, K):
     hidden_np, w_np, b_np, _, _, _ = synth.router(seed=3, N=N, H=H, E=E)
     G.say(f"router N={N} H={H} E={E} K={K}")
@@ -134,3 +136,60 @@ def test_router_full_size_chain(O):
                err=0)
     G.compare_eqb(got, ref, tag="router ")
     G.assert_same("lei g", G.host(g), O.lei(g_np, ref["load"], K, eta))
+
+
+def _fused_and_unfused(hidden_np, w_np, b_np, K):
+    """qb_router_fused against qb_router_scores + qb_margins_topk on the same
+    inputs: scores, logits, alpha, loads and histogram bit for bit."""
+    N, H = hidden_np.shape
+    E = w_np.shape[0]
+    s, logits, alpha, load, buf, b = run_router(hidden_np, w_np, b_np, K)
+    hidden, w = bf16_dev(hidden_np), bf16_dev(w_np)
+    s2 = torch.empty((N, E), dtype=torch.float32, device=G.DEV)
+    lg2 = torch.empty((N, E), dtype=torch.float32, device=G.DEV)
+    qb.qb_router_scores(hidden, w, s2, logits_out=lg2)
+    alpha2 = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    load2 = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+    hist2 = torch.zeros((E, 256), dtype=torch.int32, device=G.DEV)
+    qb.qb_margins_topk(s2, b, K, alpha2, load=load2, hist_hi=hist2)
+    torch.cuda.synchronize()
+    for name, x, y in (("s", s, s2), ("logits", logits, lg2), ("alpha", alpha, alpha2), ("load", load, load2),
+                       ("hist_hi", buf.hist_hi, hist2)):
+        G.assert_same(f"fused vs unfused {name}", G.host(x), G.host(y))
+    return G.host(s), G.host(alpha), G.host(load), G.host(buf.hist_hi)
+
+
+@pytest.mark.parametrize("E,K", [(256, 6), (128, 7), (64, 8), (32, 3)])
+def test_fused_epilogue_bias_and_ties(O, E, K):
+    """A non-zero bias, a ragged last workgroup, and forced exact ties: expert
+    rows of the weight repeated (equal logits, equal scores) with equal
+    biases, and token rows repeated, so alpha is tied across experts in many
+    rows and the loads depend on the lower-index rule."""
+    N, H = 1000, 128
+    hidden_np, w_np, _, _, _, _ = synth.router(seed=7, N=N, H=H, E=E)
+    w_np = w_np.copy()
+    w_np[1::2] = w_np[0::2]                  # experts 2i and 2i+1 share their weights
+    hidden_np = hidden_np.copy()
+    hidden_np[500:] = hidden_np[:500]        # repeated tokens
+    b_np = np.random.default_rng(8).uniform(-0.1, 0.1, E).astype(np.float32)
+    b_np[1::2] = b_np[0::2]
+    G.say(f"fused epilogue E={E} K={K} with ties")
+    s_np, a_np, load_np, hist_np = _fused_and_unfused(hidden_np, w_np, b_np, K)
+    ref_a, ref_load = O.alpha(s_np, b_np, K)
+    G.assert_same("alpha", a_np, ref_a)
+    G.assert_same("load", load_np, ref_load)
+    G.assert_same("hist_hi", hist_np, O.eqb_layer(s_np, b_np, K)["hist_hi"])
+
+
+def test_fused_epilogue_saturated_equals_unfused(O):
+    """Saturated scores (exact 0 and 1 in most rows: massive ties) through
+    both paths at E = 256."""
+    N, H, E, K = 777, 1024, 256, 6
+    hidden_np, _, b_np, _, _, _ = synth.router(seed=9, N=N, H=H, E=E)
+    w32 = np.random.default_rng(10).standard_normal((E, H), dtype=np.float32)
+    w_np = torch.from_numpy(w32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    G.say("fused epilogue saturated E=256")
+    s_np, a_np, load_np, hist_np = _fused_and_unfused(hidden_np, w_np, b_np, K)
+    ref_a, ref_load = O.alpha(s_np, b_np, K)
+    G.assert_same("load", load_np, ref_load)
+    G.assert_same("hist_hi", hist_np, O.eqb_layer(s_np, b_np, K)["hist_hi"])
