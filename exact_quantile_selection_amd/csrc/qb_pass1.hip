@@ -44,11 +44,15 @@ namespace qbk {
 #ifndef QB_P1_WAVES
 #define QB_P1_WAVES 16
 #endif
-// QB_P1_WAVES waves per workgroup (<= 128 VGPRs each); the load-counting
-// variant and lists longer than 8 keep more state per lane and run 8 waves
-// (<= 256 VGPRs each).
-template <bool LOAD, int P>
-constexpr int p1_waves() { return (LOAD || P > 8) ? 8 : QB_P1_WAVES; }
+// QB_P1_WAVES waves per workgroup (<= 128 VGPRs each) for lists of up to 8,
+// also with load counting (the count runs after the histogram, from the raw
+// scores and bias values re-read from LDS, so it fits); lists longer than 8
+// keep more state per lane and run 8 waves (<= 256 VGPRs each), and the
+// per-microbatch count 12 (<= 168).  Measured on one MI355X, alpha + loads +
+// high-byte histogram at 1,048,576 x 256: 245 us with 8 waves, 229 with 12,
+// 224 with 16; with microbatch loads 222, 216 and 225 us.
+template <bool LOAD, int P, bool MB = false>
+constexpr int p1_waves() { return P > 8 ? 8 : (MB ? 12 : QB_P1_WAVES); }
 
 template <int E>
 struct P1Shape {
@@ -91,6 +95,10 @@ __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], c
                                             int rho, int ql, float a, int K, bool valid,
                                             int32_t* lds_load) {
   using S = P1Shape<E>;
+  // An opaque copy of the rotation: the compiler cannot tell that these bias
+  // reads repeat the top-(K+1) loop's, so it re-reads them from LDS instead
+  // of keeping that loop's bias values live until here.
+  asm volatile("" : "+v"(rho));
   uint64_t gt_t = 0;
 #pragma unroll
   for (int t = 0; t < S::F4; ++t) {
@@ -221,7 +229,6 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
   // alpha is read again only by the next pass: a non-temporal store keeps
   // it from sitting dirty in L2 until the end of the kernel
   if (valid && ql == 0) __builtin_nontemporal_store(a, alpha + row);
-  if constexpr (LOAD) count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load);
   if constexpr (HM == 2) {
     // full 16-bit key histogram, [E][65536] int32 in global memory
     if (valid) {
@@ -249,6 +256,12 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
       }
     }
   }
+  // The loads last, after the histogram's key arithmetic, with a scheduling
+  // fence between: only the raw scores stay live into the count.
+  if constexpr (LOAD) {
+    __builtin_amdgcn_sched_barrier(0);
+    count_loads<E, P>(x, lds_b, rot, ql, a, K, valid, lds_load);
+  }
 }
 
 // MB (with LOAD): per-microbatch loads as well.  Each workgroup then takes
@@ -257,13 +270,13 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
 // load_mb and load at each microbatch boundary (one atomic per non-zero
 // counter instead of one device atomic per member).
 template <int E, int P, int HM, bool LOAD, bool MB>
-__global__ __launch_bounds__((p1_waves<LOAD, P>() * kWave)) void k_margins_topk(
+__global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_topk(
     const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int bdiv, int K,
     float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi,
     int32_t* __restrict__ load_mb, int64_t n_mb) {
   using S = P1Shape<E>;
   static_assert(!MB || LOAD, "microbatch loads need load counting");
-  constexpr int kWaves = p1_waves<LOAD, P>();
+  constexpr int kWaves = p1_waves<LOAD, P, MB>();
   constexpr int kThreads = kWaves * kWave;
   __shared__ uint32_t lds_hist[HM == 1 ? S::HDW : 4];
   __shared__ float lds_b[E];
@@ -359,8 +372,8 @@ template <int E, int P, int HM, bool LOAD, bool MB = false>
 static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb = nullptr,
                        int64_t n_mb = 1) {
-  constexpr int kThreads = p1_waves<LOAD, P>() * kWave;
-  const RowSplit sp = split_rows(L, N, p1_waves<LOAD, P>() * P1Shape<E>::RPW, QB_P1_MAXROWS);
+  constexpr int kThreads = p1_waves<LOAD, P, MB>() * kWave;
+  const RowSplit sp = split_rows(L, N, p1_waves<LOAD, P, MB>() * P1Shape<E>::RPW, QB_P1_MAXROWS);
   hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD, MB>), dim3(unsigned(sp.blocks)), dim3(kThreads),
                      0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi, load_mb, n_mb);
   return int(hipGetLastError());
