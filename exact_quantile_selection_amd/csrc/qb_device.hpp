@@ -210,47 +210,6 @@ __device__ __forceinline__ void hist16_flush_pairs(const uint32_t* lds, int32_t*
   }
 }
 
-// Transposed packed high-byte histogram for 256 experts (64 quads): the
-// dword of expert pair (4*quad + 2*cp, 4*quad + 2*cp + 1) and bin h sits at
-// (cp * 256 + h) * 64 + quad, so its bank is the quad alone.  The 64 lanes
-// of an instruction hold 64 distinct quads, so they hit 64 distinct banks
-// whatever their bins: with the XOR swizzle above, a lane and the lane whose
-// quad differs by the difference of two hot bins collide whenever each holds
-// the other's bin, which a skewed layer's two or three crowded bins make
-// common.
-__device__ __forceinline__ void hist16t_add_hi(uint32_t* lds, int quad, int c0, uint32_t kp) {
-  uint32_t* base = lds + (c0 >> 1) * (256 * 64) + quad;
-  atomicAdd(base + ((kp >> 8) & 0xFFu) * 64, 1u);
-  atomicAdd(base + (kp >> 24) * 64, 0x10000u);
-}
-
-// Adds the transposed table into the global int32 histogram out[256][256]
-// (8-byte aligned), one 64-bit atomic per two adjacent bins of an expert
-// with a non-zero count; consecutive threads take consecutive quads, so the
-// table reads are free of bank conflicts.  `start` staggers the walk as in
-// hist16_flush.
-__device__ __forceinline__ void hist16t_flush_pairs(const uint32_t* lds, int32_t* out, int tid, int nthreads,
-                                                    int start) {
-  constexpr int ITEMS = 2 * 128 * 64;  // (cp, bin pair, quad)
-  const int nblk = (ITEMS + nthreads - 1) / nthreads;
-  const int b0 = start % nblk;
-  for (int k = 0; k < nblk; ++k) {
-    int blk = b0 + k;
-    blk = blk >= nblk ? blk - nblk : blk;
-    const int i = blk * nthreads + tid;
-    if (i >= ITEMS) continue;
-    const int quad = i & 63, m = (i >> 6) & 127, cp = i >> 13;
-    const int d0 = (cp * 256 + 2 * m) * 64 + quad;
-    const uint32_t a = lds[d0], c = lds[d0 + 64];  // bins 2m and 2m + 1
-    if ((a | c) == 0u) continue;
-    const uint64_t lo = uint64_t(a & 0xFFFFu) | (uint64_t(c & 0xFFFFu) << 32);
-    const uint64_t hi = uint64_t(a >> 16) | (uint64_t(c >> 16) << 32);
-    const int j0 = 4 * quad + 2 * cp;
-    if (lo) atomicAdd(reinterpret_cast<unsigned long long*>(out + j0 * 256 + 2 * m), (unsigned long long)lo);
-    if (hi) atomicAdd(reinterpret_cast<unsigned long long*>(out + (j0 + 1) * 256 + 2 * m), (unsigned long long)hi);
-  }
-}
-
 template <int E>
 __device__ __forceinline__ void hist16_zero(uint32_t* lds, int tid, int nthreads) {
   constexpr int HDW = (E / 2) * 256;

@@ -250,14 +250,9 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
 #pragma unroll
       for (int t = 0; t < S::F4; ++t) {
         const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
-        if constexpr (E == 256) {
-          hist16t_add_hi(lds_hist, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)));
-          hist16t_add_hi(lds_hist, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)));
-        } else {
-          const uint32_t swz = hist16_swizzle2(quad);
-          hist16_add_hi(lds_hist, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
-          hist16_add_hi(lds_hist, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
-        }
+        const uint32_t swz = hist16_swizzle2(quad);
+        hist16_add_hi(lds_hist, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
+        hist16_add_hi(lds_hist, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
       }
     }
   }
@@ -366,12 +361,7 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   // The high-byte counts crowd into a few adjacent bins per expert, so a
   // 64-bit atomic per bin pair halves the flush's atomics (190 -> 188 us
   // at 1M x 256).
-  if constexpr (HM == 1) {
-    if constexpr (E == 256)
-      hist16t_flush_pairs(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
-    else
-      hist16_flush_pairs<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
-  }
+  if constexpr (HM == 1) hist16_flush_pairs<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
   if constexpr (LOAD && !MB) {
     for (int j = tid; j < E; j += kThreads)
       if (lds_load[j]) atomicAdd(load + j, lds_load[j]);

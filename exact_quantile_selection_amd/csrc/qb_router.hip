@@ -262,26 +262,16 @@ __device__ __forceinline__ void rf_epilogue(uint8_t* lds, int lane, int wave, in
 #pragma unroll
         for (int t = 0; t < F::F4; ++t) {
           const int Q = LPR * ((t + rho) & (F::F4 - 1)) + ql;
-          if constexpr (E == 256) {
-            hist16t_add_hi(hist, Q, 0, key2(bf16x2_rne(a - xp[t].x, a - xp[t].y)));
-            hist16t_add_hi(hist, Q, 2, key2(bf16x2_rne(a - xp[t].z, a - xp[t].w)));
-          } else {
-            const uint32_t swz = hist16_swizzle2(Q);
-            hist16_add_hi(hist, Q, 0, key2(bf16x2_rne(a - xp[t].x, a - xp[t].y)) ^ swz);
-            hist16_add_hi(hist, Q, 2, key2(bf16x2_rne(a - xp[t].z, a - xp[t].w)) ^ swz);
-          }
+          const uint32_t swz = hist16_swizzle2(Q);
+          hist16_add_hi(hist, Q, 0, key2(bf16x2_rne(a - xp[t].x, a - xp[t].y)) ^ swz);
+          hist16_add_hi(hist, Q, 2, key2(bf16x2_rne(a - xp[t].z, a - xp[t].w)) ^ swz);
         }
       }
       if (p + NB < F::NP) fetch(p + NB, xp);
     }
   }
   __syncthreads();
-  if (want_hist) {
-    if constexpr (E == 256)
-      hist16t_flush_pairs(hist, hist_hi, tid, kRgThreads, int(blockIdx.x));
-    else
-      hist16_flush_pairs<E>(hist, hist_hi, tid, kRgThreads, int(blockIdx.x));
-  }
+  if (want_hist) hist16_flush_pairs<E>(hist, hist_hi, tid, kRgThreads, int(blockIdx.x));
   if (want_load)
     for (int j = tid; j < E; j += kRgThreads)
       if (lds_load[j]) atomicAdd(load + j, lds_load[j]);
