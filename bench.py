@@ -247,7 +247,7 @@ def main():
     ap.add_argument("--only", default=None,
                     help="time only this workload of the suite and print its JSON line "
                          "(single, step_48_layers, router, controller, sharding, "
-                         "one_pass_full_hist, k3_skew, lei_backward)")
+                         "one_pass_full_hist, k3_skew, lei_backward, calibration)")
     args = ap.parse_args()
     if args.only and args.only not in SUITES:
         print(f"unknown workload {args.only!r}; one of {', '.join(SUITES)}", file=sys.stderr)
@@ -413,7 +413,7 @@ def step48_suite(torch, qb, synth, dev, args):
 def suite(torch, qb, synth, dev, args):
     res = single_suite(torch, qb, synth, dev, args)
     for name, f in SUITES.items():
-        if name != "single":
+        if name not in ("single", "calibration"):
             res[name] = f(torch, qb, synth, dev, args)
     return res
 
@@ -733,6 +733,26 @@ def router_suite(torch, qb, synth, dev, args):
     return out
 
 
+def calibration_suite(torch, qb, synth, dev, args):
+    """Kernels of known traffic for calibrating the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE counters: a plain torch copy of 1 GiB (1 GiB read, 1 GiB
+    written) and the stream probe's read of 1 GiB (1 GiB read)."""
+    from exact_quantile_selection_amd import stream_probe as sp
+
+    n = 1 << 28  # floats: 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    for _ in range(3):
+        dst.copy_(src)
+        sp.read(src, sink, 2 * cus, 4)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(copy_bytes_read=4 * n, copy_bytes_written=4 * n, read_bytes=4 * n, launches_each=3)
+
+
 SUITES = {
     "single": single_suite,
     "step_48_layers": step48_suite,
@@ -742,6 +762,7 @@ SUITES = {
     "one_pass_full_hist": full_hist_suite,
     "k3_skew": k3_skew_suite,
     "lei_backward": lei_backward_suite,
+    "calibration": calibration_suite,
 }
 
 
