@@ -636,8 +636,10 @@ def controller_suite(torch, qb, synth, dev, args, T=8):
                global_maxvio=[round(float(a[0]), 4) for a, _ in traj],
                local_maxvio_mean=[round(float(b[1]), 4) for _, b in traj],
                local_maxvio_max=[round(float(b[0]), 4) for _, b in traj],
-               step="pass 1 (alpha, loads, microbatch loads, hist_hi), 2 x MaxVio, select HI, "
-                    "pass 2, select LO (b updated in place)")
+               step=("pass 1 (alpha, hist_hi), select HI, pass 2 (hist_lo partials, loads, microbatch "
+                     "loads), 2 x MaxVio, select LO (b updated in place)" if ctl.loads_in_pass2 else
+                     "pass 1 (alpha, loads, microbatch loads, hist_hi), select HI, pass 2, 2 x MaxVio, "
+                     "select LO (b updated in place)"))
     del batches
     torch.cuda.empty_cache()
     return out
@@ -653,7 +655,8 @@ def router_suite(torch, qb, synth, dev, args):
     g.manual_seed(0)
     hidden = torch.randn((N, H), generator=g, device=dev).to(torch.bfloat16)
     w = (torch.randn((E, H), generator=g, device=dev) * 0.02).to(torch.bfloat16)
-    grad = torch.randn((N, E), generator=g, device=dev)
+    grad0 = torch.randn((N, E), generator=g, device=dev)
+    grad = grad0.clone()
     b0 = torch.zeros(E, dtype=torch.float32, device=dev)
     b = b0.clone()
     s = torch.empty((N, E), dtype=torch.float32, device=dev)
@@ -687,30 +690,43 @@ def router_suite(torch, qb, synth, dev, args):
 
     class Chain:
         """Router forward, the EQB update and LEI; pass 1 either in the
-        GEMM's epilogue (fused) or as its own pass over the scores."""
+        GEMM's epilogue (fused) or as its own pass over the scores, and the
+        top-K loads counted in pass 1 or in the low-byte pass."""
 
-        def __init__(self_, fused):
+        def __init__(self_, fused, loads_in_pass2=False):
             self_.fused = fused
+            self_.p2 = loads_in_pass2
 
         def run(self_):
             b.copy_(b0)
             qb.qb_fill_i32(load, 0)
+            l1 = None if self_.p2 else load
             if self_.fused:
-                qb.qb_router_fused(hidden, w, b, K, s, alpha, load=load, hist_hi=buf.hist_hi)
+                qb.qb_router_fused(hidden, w, b, K, s, alpha, load=l1, hist_hi=buf.hist_hi)
             else:
                 qb.qb_router_scores(hidden, w, s)
-                qb.qb_margins_topk(s, b, K, alpha, load=load, hist_hi=buf.hist_hi)
+                qb.qb_margins_topk(s, b, K, alpha, load=l1, hist_hi=buf.hist_hi)
             qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi,
                                 rank_lo=buf.rank_lo, err=buf.err)
-            qb.qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws)
+            if self_.p2:
+                qb.qb_radix_hist_lo_ws_loads(s, alpha, buf.sel_hi, ws, b, K, load)
+            else:
+                qb.qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws)
             qb.qb_select_lo_ws(N, ws, buf.sel_hi, buf.rank_lo, buf.q, b, buf.bounds, key_out=buf.key,
                                err=buf.err, hist_hi=buf.hist_hi)  # clears hist_hi for the next run
             qb.qb_lei_grad(grad, load, K, 1e-5)
 
-    sec, _ = time_graph(Chain(True), torch, n, 1)
-    b_fused = b.clone()
-    sec_unfused, _ = time_graph(Chain(False), torch, n, 1)
-    assert torch.equal(b, b_fused)
+    chains = {}
+    b_ref = g_ref = None
+    for name, fused, p2 in (("fused", True, False), ("unfused", False, False),
+                            ("fused_loads_in_pass2", True, True), ("unfused_loads_in_pass2", False, True)):
+        grad.copy_(grad0)
+        chains[name], _ = time_graph(Chain(fused, p2), torch, n, 1)
+        if b_ref is None:
+            b_ref, g_ref = b.clone(), grad.clone()
+        assert torch.equal(b, b_ref), name
+        assert torch.equal(grad, g_ref), name
+    sec, sec_unfused = chains["fused"], chains["unfused"]
     flops = 2.0 * N * H * E
     gemm_bytes = N * H * 2 + N * E * 4 + E * H * 2
     out = dict(N=N, H=H, E=E, K=K,
@@ -724,11 +740,13 @@ def router_suite(torch, qb, synth, dev, args):
                fused_hbm_GBps=round(gemm_bytes / t_fused / 1e9, 1),
                chain_fused_us=round(sec * 1e6, 2), chain_fused_tokens_per_s=N / sec,
                chain_unfused_us=round(sec_unfused * 1e6, 2), chain_unfused_tokens_per_s=N / sec_unfused,
-               chain_same_b_next=True,
+               chain_fused_loads_in_pass2_us=round(chains["fused_loads_in_pass2"] * 1e6, 2),
+               chain_unfused_loads_in_pass2_us=round(chains["unfused_loads_in_pass2"] * 1e6, 2),
+               chain_same_b_next_and_lei=True,
                chain="router GEMM + sigmoid, pass 1 (in the GEMM's epilogue, or after it), select HI, "
                      "pass 2, select LO, LEI; one graph of the steps",
                timing="HIP events around back-to-back launches of each call")
-    del hidden, w, grad, s
+    del hidden, w, grad, grad0, s
     torch.cuda.empty_cache()
     return out
 

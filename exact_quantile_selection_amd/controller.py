@@ -28,6 +28,11 @@ class BiasController:
             raise ValueError(f"n_mb={n_mb} must divide N={N}")
         self.L, self.N, self.E, self.K, self.n_mb = L, N, E, K, n_mb
         self.C = N // n_mb
+        # The low-byte pass counts the loads when its microbatches are whole
+        # row trips of that pass (every multiple of 2048 tokens is); it then
+        # costs 2-3 us at 262144 x 256 against 13 us for counting them in
+        # pass 1.  Other microbatch sizes count them in pass 1.
+        self.loads_in_pass2 = n_mb % 2048 == 0
         kw = dict(device=device)
         self.b = (torch.zeros((L, E), dtype=torch.float32, **kw) if b0 is None
                   else b0.to(device=device, dtype=torch.float32).reshape(L, E).clone())
@@ -57,18 +62,28 @@ class BiasController:
         s3 = s.view(L, N, E)
         buf = self.buf
         qb.qb_fill_i32(self.loads, 0, stream)
-        # pass 1 with the bias in force: alpha, loads, per-microbatch loads
-        # and the high-byte histogram in one read of the scores
-        qb.qb_margins_topk_mb(s3, self.b, K, self.alpha, self.load, self.n_mb, self.load_mb,
-                              hist_hi=buf.hist_hi, stream=stream)
+        if self.loads_in_pass2:
+            # pass 1 with the bias in force: alpha and the high-byte
+            # histogram; pass 2 counts the loads and per-microbatch loads on
+            # its own read of the scores (b is still the bias in force there)
+            qb.qb_margins_topk(s3, self.b, K, self.alpha, hist_hi=buf.hist_hi, stream=stream)
+            qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                                err=buf.err, stream=stream)
+            qb.qb_radix_hist_lo_ws_loads(s3, self.alpha, buf.sel_hi, self.ws, self.b, K, self.load,
+                                         n_mb=self.n_mb, load_mb=self.load_mb, stream=stream)
+        else:
+            # pass 1 with the bias in force: alpha, loads, per-microbatch
+            # loads and the high-byte histogram in one read of the scores
+            qb.qb_margins_topk_mb(s3, self.b, K, self.alpha, self.load, self.n_mb, self.load_mb,
+                                  hist_hi=buf.hist_hi, stream=stream)
+            qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                                err=buf.err, stream=stream)
+            qb.qb_radix_hist_lo_ws(s3, self.alpha, buf.sel_hi, self.ws, stream=stream)
         qb.qb_maxvio(self.load.view(L, 1, E), K, N, self.mv_global, self.summary_global,
                      self.worst_global, stream=stream)
         qb.qb_maxvio(self.load_mb, K, self.n_mb, self.mv_local, self.summary_local, self.worst_local,
                      stream=stream)
         # EQB update of this batch, written over b
-        qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
-                            err=buf.err, stream=stream)
-        qb.qb_radix_hist_lo_ws(s3, self.alpha, buf.sel_hi, self.ws, stream=stream)
         qb.qb_select_lo_ws(N, self.ws, buf.sel_hi, buf.rank_lo, buf.q, self.b, buf.bounds,
                            hist_lo=buf.hist_lo, key_out=buf.key, err=buf.err, hist_hi=buf.hist_hi,
                            stream=stream)

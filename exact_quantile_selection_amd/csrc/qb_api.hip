@@ -287,6 +287,34 @@ QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_
   return hip_status(qbk::launch_radix_hist_lo_ws(s, alpha, L, N, E, sel_hi, static_cast<uint8_t*>(ws), stream), fn);
 }
 
+QB_API int qb_radix_hist_lo_ws_loads(const float* s, const float* alpha, int L, int64_t N, int E,
+                                     const int32_t* sel_hi, void* ws, int64_t ws_bytes, const float* b, int K,
+                                     int32_t* load, int64_t n_mb, int32_t* load_mb, qb_stream_t stream) {
+  const char* fn = "qb_radix_hist_lo_ws_loads";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!alpha || !sel_hi || !ws || !b || !load)
+    return fail(QB_EINVAL,
+                "%s: alpha (float [L][N]), sel_hi (int32 [L=%d][E=%d]), ws, b (float [L][E]) and load (int32 [L][E]) are required",
+                fn, L, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  const int64_t need = qb_hist_lo_workspace_bytes(L, N, E);
+  if (ws_bytes < need)
+    return fail(QB_EINVAL, "%s: ws_bytes=%lld, this shape needs %lld (qb_hist_lo_workspace_bytes)", fn,
+                (long long)ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(QB_EINVAL, "%s: ws must be 16-byte aligned", fn);
+  if (!aligned4(b) || !aligned4(load) || (load_mb && !aligned4(load_mb)))
+    return fail(QB_EINVAL, "%s: b, load and load_mb must be 4-byte aligned", fn);
+  if (load_mb) {
+    const int trip = qbk::radix_lo_trip_rows(E);
+    if (n_mb < 1 || N % n_mb != 0 || n_mb % trip != 0)
+      return fail(QB_EINVAL, "%s: n_mb=%lld must divide N=%lld and be a multiple of %d rows at E=%d", fn,
+                  (long long)n_mb, (long long)N, trip, E);
+  }
+  return hip_status(qbk::launch_radix_hist_lo_ws_loads(s, alpha, L, N, E, sel_hi, static_cast<uint8_t*>(ws), b, K,
+                                                       load, load_mb ? n_mb : 1, load_mb, stream),
+                    fn);
+}
+
 QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_t* sel_hi, const int32_t* rank_lo,
                            int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
                            int32_t* hist_hi, int32_t* err, qb_stream_t stream) {

@@ -53,6 +53,10 @@ inline LoWs lo_ws_layout(int L, int E, int G) {
 }
 int launch_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E,
                             const int32_t* sel_hi, uint8_t* ws, hipStream_t st);
+int launch_radix_hist_lo_ws_loads(const float* s, const float* alpha, int L, int64_t N, int E,
+                                  const int32_t* sel_hi, uint8_t* ws, const float* b, int K, int32_t* load,
+                                  int64_t n_mb, int32_t* load_mb, hipStream_t st);
+int radix_lo_trip_rows(int E);
 int launch_select_lo_ws(int L, int E, int G, const uint8_t* ws, const int32_t* sel_hi, const int32_t* rank_lo,
                         int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
                         int32_t* hist_hi, int32_t* err, hipStream_t st);

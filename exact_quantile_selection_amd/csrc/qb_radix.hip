@@ -57,13 +57,34 @@ struct RHShape {
 // expert in the workspace (LoWs in qb_internal.hpp: bytes when all 256
 // counts of the row are <= 255, uint16 otherwise, and a flag saying which),
 // for a select that sums the partials (no atomics, no zeroing).
-template <int E, bool LO, bool WS>
+//
+// LD (low-byte pass only): the top-K loads of s + b are counted on the way
+// ("[Dev] Add global-batch quantile balancing", section "Quantile
+// estimator": the K largest of s + b route a token; "Exact Quantile
+// Balancing and Load-Error Injection for Mixture-of-Experts", LEI
+// paragraph: the per-expert loads behind the relative load errors), with
+// alpha from pass 1: a token's members are its v = s + b > alpha plus, when
+// alpha's value is tied, the lowest-index elements equal to alpha up to K.
+// Here a lane's four experts are fixed for the whole kernel, so their bias
+// sits in four registers and the lane counts their members in four register
+// counters; a row's count above alpha and its tie ranks come from ballots
+// over the lanes holding the row.  LD = 1: load[l][e] += counts, added once
+// per workgroup; LD = 2: also load_mb[l][c][e] for each n_mb-row
+// microbatch c (n_mb a multiple of the trip), the counts of each trip summed
+// in LDS and added to its microbatch's row.  No LDS atomic per element and
+// no bias reads from LDS: the standalone pass 1 pays for both.
+template <int E, bool LO, bool WS, int LD = 0>
 __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int wg_per_layer,
     const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist, uint8_t* __restrict__ ws,
-    int64_t ws_flag, int64_t ws_p16) {
+    int64_t ws_flag, int64_t ws_p16, const float* __restrict__ bias, int K, int32_t* __restrict__ load,
+    int32_t* __restrict__ load_mb, int64_t n_mb) {
   using S = RHShape<E>;
+  static_assert(LD == 0 || LO, "loads are counted in the low-byte pass");
   __shared__ uint32_t lds_hist[(E / 2) * 256];
+  // LD == 1: the workgroup's totals; LD == 2: two trip buffers, then the totals
+  constexpr int kLdsLoad = LD == 2 ? 3 * E : (LD == 1 ? E : 1);
+  __shared__ int32_t lds_load[kLdsLoad];
   const int tid = threadIdx.x;
   const int layer = blockIdx.x / wg_per_layer;
   const int g = blockIdx.x - layer * wg_per_layer;
@@ -93,6 +114,23 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
       asm volatile("" : "+v"(sel[c]));
     }
   }
+  // load counting: the bias of the lane's four experts and its counters
+  float bq[4] = {0.f, 0.f, 0.f, 0.f};
+  int cnt[4] = {0, 0, 0, 0};  // this trip's (LD == 2) or all trips' (LD == 1) members
+  int tot[4] = {0, 0, 0, 0};  // LD == 2: all trips' members
+  if constexpr (LD > 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bq[c] = bias[int64_t(layer) * E + 4 * quad + c];
+      asm volatile("" : "+v"(bq[c]));
+    }
+    for (int j = tid; j < kLdsLoad; j += kRHThreads) lds_load[j] = 0;
+    if constexpr (LD == 2) load_mb += int64_t(layer) * (N / n_mb) * E;
+    load += int64_t(layer) * E;
+  }
+  // lanes of this lane's row (QPR lanes) and those of them below this lane
+  const uint64_t seg = S::QPR >= 64 ? ~0ull : (((1ull << S::QPR) - 1ull) << (rsub * S::QPR));
+  const uint64_t below = seg & ((1ull << lane) - 1ull);
   __syncthreads();
 
   // Full trips (every row < N): addresses from the wave-uniform row base
@@ -106,6 +144,27 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
       x[u] = ld4(sw + uint32_t((u * S::RPI + rsub) * E + 4 * quad));
       a[u] = aw[u * S::RPI + rsub];
     }
+  };
+  auto count_load = [&](const float4& x, float a, bool valid) {
+    const float v0 = x.x + bq[0], v1 = x.y + bq[1], v2 = x.z + bq[2], v3 = x.w + bq[3];
+    const bool g0 = valid && v0 > a, g1 = valid && v1 > a, g2 = valid && v2 > a, g3 = valid && v3 > a;
+    const uint64_t b0 = __ballot(g0), b1 = __ballot(g1), b2 = __ballot(g2), b3 = __ballot(g3);
+    const int need = K - (__popcll(b0 & seg) + __popcll(b1 & seg) + __popcll(b2 & seg) + __popcll(b3 & seg));
+    int m0 = g0, m1 = g1, m2 = g2, m3 = g3;
+    if (__ballot(valid && need > 0) != 0) {  // a tie at alpha in some row of this instruction
+      const bool e0 = valid && v0 == a, e1 = valid && v1 == a, e2 = valid && v2 == a, e3 = valid && v3 == a;
+      const uint64_t q0 = __ballot(e0), q1 = __ballot(e1), q2 = __ballot(e2), q3 = __ballot(e3);
+      // equal elements of the row with a lower expert index (4 quad + c)
+      const int r0 = __popcll(q0 & below) + __popcll(q1 & below) + __popcll(q2 & below) + __popcll(q3 & below);
+      m0 |= e0 && r0 < need;
+      m1 |= e1 && r0 + e0 < need;
+      m2 |= e2 && r0 + e0 + e1 < need;
+      m3 |= e3 && r0 + e0 + e1 + e2 < need;
+    }
+    cnt[0] += m0;
+    cnt[1] += m1;
+    cnt[2] += m2;
+    cnt[3] += m3;
   };
   auto count1 = [&](const float4& x, float a) {
     const uint32_t k01 = key2(bf16x2_rne(a - x.x, a - x.y));
@@ -138,21 +197,68 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
   const int64_t nF = full_trips > g ? (full_trips - 1 - g) / wg_per_layer + 1 : 0;
   auto trip_base = [&](int64_t k) { return (int64_t(g) + k * wg_per_layer) * S::STEP + int64_t(wave) * S::RPW; };
   const bool early = wave >= kRHWaves / 2;
+  // LD == 2: each lane adds its counts of trip k into LDS buffer k & 1 at
+  // the end of the trip; wave 0 adds that buffer to trip k's microbatch row
+  // and clears it after the barrier that opens trip k + 1, which every wave
+  // reaches after its adds, and before the barrier that opens trip k + 2,
+  // after which the waves add into it again.  The bare barriers order no
+  // LDS access by themselves: each wave first waits for its own LDS
+  // operations (lgkmcnt 0; the row loads stay in flight).
+  auto mb_flush = [&](int64_t kt) {  // wave 0: trip number kt of this workgroup
+    const int64_t mb = ((int64_t(g) + kt * wg_per_layer) * S::STEP) / n_mb;
+    int32_t* buf = lds_load + (kt & 1) * E;
+    for (int j = lane; j < E; j += kWave) {
+      const int32_t v = buf[j];
+      if (v) {
+        atomicAdd(load_mb + mb * E + j, v);
+        buf[j] = 0;
+      }
+    }
+  };
+  auto trip_loads_done = [&](int64_t kt) {
+    if constexpr (LD == 2) {
+      int32_t* buf = lds_load + (kt & 1) * E;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (cnt[c]) atomicAdd(&buf[4 * quad + c], cnt[c]);
+        tot[c] += cnt[c];
+        cnt[c] = 0;
+      }
+    }
+  };
+  auto lds_wait_barrier = [&]() {
+    if constexpr (LD == 2) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+  };
   float4 x[S::U];
   float a[S::U];
   for (int64_t k = 0; k < nF; ++k) {
     if (early) {
       load_full(trip_base(k), x, a);
-      __builtin_amdgcn_s_barrier();
+      lds_wait_barrier();
     } else {
-      __builtin_amdgcn_s_barrier();
+      lds_wait_barrier();
       load_full(trip_base(k), x, a);
     }
+    if constexpr (LD == 2) {
+      if (k > 0 && wave == 0) mb_flush(k - 1);
+    }
 #pragma unroll
-    for (int u = 0; u < S::U; ++u) count1(x[u], a[u]);
+    for (int u = 0; u < S::U; ++u) {
+      count1(x[u], a[u]);
+      if constexpr (LD > 0) count_load(x[u], a[u], true);
+    }
+    trip_loads_done(k);
+  }
+  if constexpr (LD == 2) {
+    // every wave's adds of trip nF - 1 are done, and wave 0's clearing of
+    // buffer nF & 1 (trip nF - 2) before the partial trip adds into it
+    lds_wait_barrier();
+    if (nF > 0 && wave == 0) mb_flush(nF - 1);
   }
   const int64_t base = trip_base(nF);
-  if (base < N) {
+  const bool partial = base < N;  // wave 0 has a partial trip if any wave has
+  if (partial) {
     // the partial trip: rows clamped to N - 1 for the loads, not counted
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
@@ -165,7 +271,35 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     for (int u = 0; u < S::U; ++u)
       if (base + u * S::RPI + rsub < N) count1(x[u], a[u]);
   }
+  if constexpr (LD > 0) {
+    // rows past N count nothing (valid = false), and the ballots see every
+    // lane of the wave
+    if (__builtin_amdgcn_readfirstlane(int(partial))) {
+#pragma unroll
+      for (int u = 0; u < S::U; ++u) count_load(x[u], a[u], base + u * S::RPI + rsub < N);
+    }
+    if constexpr (LD == 2) {
+      if (partial) trip_loads_done(nF);
+    }
+  }
+  if constexpr (LD > 0) {
+    // the workgroup's totals, through LDS, then one atomic per expert
+    int32_t* lt = lds_load + (LD == 2 ? 2 * E : 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int v = LD == 2 ? tot[c] : cnt[c];
+      if (v) atomicAdd(&lt[4 * quad + c], v);
+    }
+  }
   __syncthreads();
+  if constexpr (LD > 0) {
+    if constexpr (LD == 2) {
+      if (partial && wave == 0) mb_flush(nF);
+    }
+    const int32_t* lt = lds_load + (LD == 2 ? 2 * E : 0);
+    for (int j = tid; j < E; j += kRHThreads)
+      if (lt[j]) atomicAdd(load + j, lt[j]);
+  }
   if constexpr (WS) {
     // Item i covers bins 8k .. 8k+7 (k = i & 31) of dword row pair = i >> 5
     // (experts 2 pair and 2 pair + 1).  Its eight counters are one aligned
@@ -260,21 +394,58 @@ static int launch_rh(bool lo, const float* s, const float* alpha, int L, int64_t
   const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, QB_RH_MAXROWS);
   if (lo)
     hipLaunchKernelGGL((k_radix_hist<E, true, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
-                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr, int64_t(0), int64_t(0));
+                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr, int64_t(0), int64_t(0), nullptr, 0,
+                       nullptr, nullptr, int64_t(1));
   else
     hipLaunchKernelGGL((k_radix_hist<E, false, false>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st,
-                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr, int64_t(0), int64_t(0));
+                       s, alpha, N, sp.wg_per_layer, sel_hi, hist, nullptr, int64_t(0), int64_t(0), nullptr, 0,
+                       nullptr, nullptr, int64_t(1));
   return int(hipGetLastError());
 }
 
 template <int E>
 static int launch_rh_ws(const float* s, const float* alpha, int L, int64_t N, const int32_t* sel_hi,
-                        uint8_t* ws, hipStream_t st) {
+                        uint8_t* ws, hipStream_t st, const float* b = nullptr, int K = 0, int32_t* load = nullptr,
+                        int64_t n_mb = 1, int32_t* load_mb = nullptr) {
   const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, QB_RH_MAXROWS);
   const LoWs lay = lo_ws_layout(L, E, sp.wg_per_layer);
-  hipLaunchKernelGGL((k_radix_hist<E, true, true>), dim3(unsigned(sp.blocks)), dim3(kRHThreads), 0, st, s,
-                     alpha, N, sp.wg_per_layer, sel_hi, nullptr, ws, lay.flag, lay.p16);
+  const dim3 grid(unsigned(sp.blocks)), block(kRHThreads);
+  if (load && load_mb)
+    hipLaunchKernelGGL((k_radix_hist<E, true, true, 2>), grid, block, 0, st, s, alpha, N, sp.wg_per_layer, sel_hi,
+                       nullptr, ws, lay.flag, lay.p16, b, K, load, load_mb, n_mb);
+  else if (load)
+    hipLaunchKernelGGL((k_radix_hist<E, true, true, 1>), grid, block, 0, st, s, alpha, N, sp.wg_per_layer, sel_hi,
+                       nullptr, ws, lay.flag, lay.p16, b, K, load, nullptr, int64_t(1));
+  else
+    hipLaunchKernelGGL((k_radix_hist<E, true, true, 0>), grid, block, 0, st, s, alpha, N, sp.wg_per_layer, sel_hi,
+                       nullptr, ws, lay.flag, lay.p16, nullptr, 0, nullptr, nullptr, int64_t(1));
   return int(hipGetLastError());
+}
+
+// Trip size of the low-byte pass, rows: microbatches of the load counting
+// must be a multiple of it.
+int radix_lo_trip_rows(int E) {
+  switch (E) {
+    case 16: return RHShape<16>::STEP;
+    case 32: return RHShape<32>::STEP;
+    case 64: return RHShape<64>::STEP;
+    case 128: return RHShape<128>::STEP;
+    case 256: return RHShape<256>::STEP;
+  }
+  return 0;
+}
+
+int launch_radix_hist_lo_ws_loads(const float* s, const float* alpha, int L, int64_t N, int E,
+                                  const int32_t* sel_hi, uint8_t* ws, const float* b, int K, int32_t* load,
+                                  int64_t n_mb, int32_t* load_mb, hipStream_t st) {
+  switch (E) {
+    case 16: return launch_rh_ws<16>(s, alpha, L, N, sel_hi, ws, st, b, K, load, n_mb, load_mb);
+    case 32: return launch_rh_ws<32>(s, alpha, L, N, sel_hi, ws, st, b, K, load, n_mb, load_mb);
+    case 64: return launch_rh_ws<64>(s, alpha, L, N, sel_hi, ws, st, b, K, load, n_mb, load_mb);
+    case 128: return launch_rh_ws<128>(s, alpha, L, N, sel_hi, ws, st, b, K, load, n_mb, load_mb);
+    case 256: return launch_rh_ws<256>(s, alpha, L, N, sel_hi, ws, st, b, K, load, n_mb, load_mb);
+  }
+  return int(hipErrorInvalidValue);
 }
 
 int radix_wg_per_layer(int L, int64_t N, int E) {

@@ -65,6 +65,7 @@ def lib() -> C.CDLL:
             "qb_margins_full_hist": [vp, vp, i32, i64, i32, i32, vp, vp, vp],
             "qb_lei_backward": [vp, vp, vp, i64, i32, i32, i64, f32, i32, vp, vp, vp],
             "qb_radix_hist_lo_ws": [vp, vp, i32, i64, i32, vp, vp, i64, vp],
+            "qb_radix_hist_lo_ws_loads": [vp, vp, i32, i64, i32, vp, vp, i64, vp, i32, vp, i64, vp, vp],
             "qb_select_lo_ws": [i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "qb_rank_average": [vp, i32, i32, vp, vp, vp],
             "qb_radix_lo_select_noalloc": [vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
@@ -296,6 +297,25 @@ def qb_radix_hist_lo_ws(s, alpha, sel_hi, ws, stream=None):
     _check(lib().qb_radix_hist_lo_ws(
         _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
         _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)), ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def qb_radix_hist_lo_ws_loads(s, alpha, sel_hi, ws, b, K, load, n_mb=None, load_mb=None, stream=None):
+    """qb_radix_hist_lo_ws that also adds the top-K loads of s + b (alpha from
+    pass 1 with the same b and K) into load [E] (or [L, E]) and, with
+    load_mb [N // n_mb, E] (or [L, N // n_mb, E]), the per-microbatch loads;
+    n_mb must divide N and be a multiple of the pass's row trip (2048 always
+    is)."""
+    L, N, E, lead = _lne(s)
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device.type != "cuda":
+        raise ValueError("ws must be a contiguous uint8 GPU tensor")
+    if load_mb is not None and (n_mb is None or n_mb < 1 or N % n_mb):
+        raise ValueError(f"n_mb={n_mb} must divide N={N}")
+    C = N // n_mb if load_mb is not None else 0
+    _check(lib().qb_radix_hist_lo_ws_loads(
+        _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
+        _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)), ws.data_ptr(), ws.numel(),
+        _ptr(b, torch.float32, "b", lead + (E,)), K, _ptr(load, torch.int32, "load", lead + (E,)),
+        int(n_mb or 1), _ptr(load_mb, torch.int32, "load_mb", lead + (C, E), opt=True), _stream(stream)))
 
 
 def qb_select_lo_ws(N, ws, sel_hi, rank_lo, q_out, b, bounds, hist_lo=None, key_out=None, err=None,

@@ -203,6 +203,29 @@ QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_
                            int32_t* hist_hi, int32_t* err, qb_stream_t stream);
 
 /*
+ * qb_radix_hist_lo_ws that also counts the top-K loads on its read of the
+ * scores, so that pass 1 can run without them (the loads the LEI paragraph
+ * of the EQB summary page turns into relative load errors; membership as in
+ * qb_margins_topk: v = fl32(s_ij + b_j) above alpha_i, then the values equal
+ * to alpha_i by lower expert index up to K).
+ *   b float [L][E]: the bias pass 1 computed alpha with (read before the
+ *   low-byte select updates it), K that pass's K (1 <= K < E).
+ *   load int32 [L][E], required, accumulated (+=).
+ *   load_mb nullable, int32 [L][N / n_mb][E], accumulated (+=): the loads of
+ *   each microbatch of n_mb consecutive tokens, as qb_microbatch_loads.  n_mb
+ *   must divide N and be a multiple of the pass's row trip, max(256,
+ *   32768 / E) rows (every multiple of 2048 is); ignored when load_mb is
+ *   NULL.
+ * Results equal qb_margins_topk's and qb_microbatch_loads' for the same s,
+ * b, K and alpha, bit for bit.  QB_EINVAL for a NULL b or load, K out of
+ * range, an n_mb that breaks the rules above or unaligned (4-byte) b, load
+ * or load_mb; the workspace rules of qb_radix_hist_lo_ws apply.
+ */
+QB_API int qb_radix_hist_lo_ws_loads(const float* s, const float* alpha, int L, int64_t N, int E,
+                                     const int32_t* sel_hi, void* ws, int64_t ws_bytes, const float* b, int K,
+                                     int32_t* load, int64_t n_mb, int32_t* load_mb, qb_stream_t stream);
+
+/*
  * qb_radix_hist_lo_ws followed by qb_select_lo_ws, with the workspace taken
  * from a device array inside the library instead of the caller: for callers
  * that cannot allocate device memory (code under HIP graph capture, tight

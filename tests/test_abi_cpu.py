@@ -197,3 +197,25 @@ def test_router_entry_points_reject_bad_shapes(libqb):
     assert rc == qb.QB_EUNSUPPORTED and "K=16" in _last(libqb)
     rc = libqb.qb_router_fused(fake, fake, 1024, 128, 256, 6, fake, fake, None, fake, None, fake + 4, None)
     assert rc == qb.QB_EINVAL and "8-byte" in _last(libqb)
+
+
+def test_pass2_loads_rejects_bad_arguments(libqb):
+    """qb_radix_hist_lo_ws_loads refuses a missing load, K out of range and
+    microbatches that are not whole trips, before any launch."""
+    from exact_quantile_selection_amd import qb
+
+    fake = 0x1000  # never dereferenced: validation fails first
+    N, E = 8192, 16
+    wsb = libqb.qb_hist_lo_workspace_bytes(1, N, E)
+    rc = libqb.qb_radix_hist_lo_ws_loads(fake, fake, 1, N, E, fake, fake, wsb, fake, 2, None, 1, None, None)
+    assert rc == qb.QB_EINVAL and "load" in _last(libqb)
+    rc = libqb.qb_radix_hist_lo_ws_loads(fake, fake, 1, N, E, fake, fake, wsb, fake, 16, fake, 1, None, None)
+    assert rc == qb.QB_EINVAL and "K=16" in _last(libqb)
+    rc = libqb.qb_radix_hist_lo_ws_loads(fake, fake, 1, N, E, fake, fake, wsb, fake, 2, fake, 1024, fake, None)
+    assert rc == qb.QB_EINVAL and "multiple of 2048" in _last(libqb)
+    rc = libqb.qb_radix_hist_lo_ws_loads(fake, fake, 1, N, 256, fake, fake,
+                                         libqb.qb_hist_lo_workspace_bytes(1, N, 256), fake, 6, fake, 3000, fake,
+                                         None)
+    assert rc == qb.QB_EINVAL and "n_mb=3000" in _last(libqb)
+    rc = libqb.qb_radix_hist_lo_ws_loads(fake, fake, 1, N, E, fake, fake, wsb - 1, fake, 2, fake, 1, None, None)
+    assert rc == qb.QB_EINVAL and "ws_bytes" in _last(libqb)

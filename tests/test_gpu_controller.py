@@ -113,8 +113,12 @@ def compare_loop(got, want):
         G.assert_same(f"step {t} local worst", g["wl"], w["local"][2])
 
 
-def test_closed_loop_two_layers(O):
-    L, N, E, K, n_mb, T = 2, 8192, 64, 4, 1024, 5
+@pytest.mark.parametrize("n_mb", [1024, 2048])
+def test_closed_loop_two_layers(O, n_mb):
+    """n_mb = 1024: the loads are counted in pass 1; 2048: in the low-byte
+    pass."""
+    L, N, E, K, T = 2, 8192, 64, 4, 5
+    assert BiasController(L, N, E, K, n_mb, device=G.DEV).loads_in_pass2 == (n_mb == 2048)
     batches = [synth.stream_batch(t, N, E, L=L) for t in range(T)]
     got = run_controller(batches, K, n_mb)
     want = oracle_loop(O, batches, np.zeros((L, E), np.float32), K, n_mb)
