@@ -31,6 +31,9 @@ namespace qbk {
 
 constexpr int kUHWaves = 16;
 constexpr int kUHThreads = kUHWaves * kWave;
+#ifndef QB_UH_REVERSE
+#define QB_UH_REVERSE 1
+#endif
 #ifndef QB_UH_UNROLL
 #define QB_UH_UNROLL 8
 #endif
@@ -103,7 +106,10 @@ __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
   const int64_t nT = trips > g ? (trips - 1 - g) / wg_per_slice + 1 : 0;
   const bool early = wave >= kUHWaves / 2;
   for (int64_t k = 0; k < nT; ++k) {
-    const int64_t base = (int64_t(g) + k * wg_per_slice) * U::STEP + int64_t(wave) * U::RPW;
+    // QB_UH_REVERSE: trips from the last to the first, so the rows pass 1
+    // read last (still in the memory-side cache) are binned first
+    const int64_t kt = QB_UH_REVERSE ? nT - 1 - k : k;
+    const int64_t base = (int64_t(g) + kt * wg_per_slice) * U::STEP + int64_t(wave) * U::RPW;
     float4 x[kUHUnroll];
     float a[kUHUnroll];
     if (early) {

@@ -34,6 +34,15 @@ namespace qbk {
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// 1: each workgroup walks its trips from the last to the first.  Pass 1
+// reads the scores in ascending row order, so the rows it read last (still
+// in the 256 MB memory-side Infinity Cache) are the ones this pass reads
+// first, and the next pass 1 starts on the rows this pass read last.  EQB
+// step at E = 256 (graph of 20 steps): 381-386 -> 371-375 us at 1M rows,
+// 216-217 -> 204 us at 512K; no change at 256K rows or 48 x 256K.
+#ifndef QB_RH_REVERSE
+#define QB_RH_REVERSE 1
+#endif
 #ifndef QB_RH_WAVES
 #define QB_RH_WAVES 16
 #endif
@@ -195,7 +204,10 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
   // runs after the loop.
   const int64_t full_trips = N / S::STEP;
   const int64_t nF = full_trips > g ? (full_trips - 1 - g) / wg_per_layer + 1 : 0;
-  auto trip_base = [&](int64_t k) { return (int64_t(g) + k * wg_per_layer) * S::STEP + int64_t(wave) * S::RPW; };
+  auto trip_of = [&](int64_t k) -> int64_t { return QB_RH_REVERSE && k < nF ? nF - 1 - k : k; };
+  auto trip_base = [&](int64_t k) {
+    return (int64_t(g) + trip_of(k) * wg_per_layer) * S::STEP + int64_t(wave) * S::RPW;
+  };
   const bool early = wave >= kRHWaves / 2;
   // LD == 2: each lane adds its counts of trip k into LDS buffer k & 1 at
   // the end of the trip; wave 0 adds that buffer to trip k's microbatch row
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
   // LDS access by themselves: each wave first waits for its own LDS
   // operations (lgkmcnt 0; the row loads stay in flight).
   auto mb_flush = [&](int64_t kt) {  // wave 0: trip number kt of this workgroup
-    const int64_t mb = ((int64_t(g) + kt * wg_per_layer) * S::STEP) / n_mb;
+    const int64_t mb = ((int64_t(g) + trip_of(kt) * wg_per_layer) * S::STEP) / n_mb;
     int32_t* buf = lds_load + (kt & 1) * E;
     for (int j = lane; j < E; j += kWave) {
       const int32_t v = buf[j];
