@@ -102,8 +102,11 @@ def time_graph(step, torch, steps, warmup):
     """Run `warmup` steps eagerly, capture `steps` consecutive steps in one
     HIP graph (as a training step's graph holds its layers' updates back to
     back), replay it once untimed, then time one replay: exactly `steps`
-    steps between two device synchronizations.  Returns seconds per step."""
+    steps between two device synchronizations.  Returns seconds per step.
+    The side stream first waits for the current one, where the step's
+    inputs and buffers were written (generation, zero-filled histograms)."""
     stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         for _ in range(max(1, warmup)):
             step.run()
