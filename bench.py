@@ -375,17 +375,33 @@ def single_suite(torch, qb, synth, dev, args):
     alpha = torch.empty(N, dtype=torch.float32, device=dev)
     hist_u = torch.zeros((E, 1000), dtype=torch.int32, device=dev)
     q_u = torch.zeros(E, dtype=torch.float32, device=dev)
+    ws_u = torch.empty(qb.qb_uniform_hist_workspace_bytes(1, N, E, 1000), dtype=torch.uint8, device=dev)
 
     class K3Step:
+        """K3 through the workspace merge (at this size the atomic flush of
+        256 small tables is a larger tail than storing them); `atomic`
+        selects the histogram merged with global atomics instead."""
+
+        def __init__(self_, atomic=False):
+            self_.atomic = atomic
+
         def run(self_):
             b.copy_(b0)
             bounds.copy_(bounds0)
-            qb.qb_fill_i32(hist_u, 0)
-            qb.k3_update(s, b, K, alpha, bounds, hist_u, q_u)
+            if self_.atomic:
+                qb.qb_fill_i32(hist_u, 0)
+                qb.k3_update(s, b, K, alpha, bounds, hist_u, q_u)
+            else:
+                qb.k3_update_ws(s, b, K, alpha, bounds, ws_u, q_u)
 
     sec, _ = time_graph(K3Step(), torch, args.steps, args.warmup)
+    b_ws = b.clone()
+    sec_atomic, _ = time_graph(K3Step(atomic=True), torch, args.steps, args.warmup)
+    assert torch.equal(b, b_ws)
     res["single_k3"] = dict(N=N, n_bins=1000, us_per_step=round(sec * 1e6, 2), tokens_per_s=N / sec,
-                            effective_GBps=round(N * (8 * E + 8) / sec / 1e9, 1))
+                            effective_GBps=round(N * (8 * E + 8) / sec / 1e9, 1),
+                            merge="workspace", us_per_step_atomic_merge=round(sec_atomic * 1e6, 2),
+                            same_b_next=True)
     del s, st
     torch.cuda.empty_cache()
     return res
@@ -507,15 +523,30 @@ def k3_skew_suite(torch, qb, synth, dev, args):
     q = torch.zeros(E, dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
 
+    ws_u = torch.empty(qb.qb_uniform_hist_workspace_bytes(1, N, E, 1000), dtype=torch.uint8, device=dev)
+
     class K3Step:
+        """K3 with the histogram merged by global atomics (at this size the
+        workspace merge stores more than the atomics flush; `ws` selects it)."""
+
+        def __init__(self_, ws=False):
+            self_.ws = ws
+
         def run(self_, i=0):
             b.copy_(b0)
             bounds.copy_(bounds0)
-            qb.qb_fill_i32(hist_u, 0)
-            qb.k3_update(s, b, K, alpha, bounds, hist_u, q, err=err)
+            if self_.ws:
+                qb.k3_update_ws(s, b, K, alpha, bounds, ws_u, q, err=err)
+            else:
+                qb.qb_fill_i32(hist_u, 0)
+                qb.k3_update(s, b, K, alpha, bounds, hist_u, q, err=err)
 
     sec, _ = time_graph(K3Step(), torch, max(5, args.steps // 2), 2)
     assert int(err.item()) == 0
+    b_atomic = b.clone()
+    sec_ws, _ = time_graph(K3Step(ws=True), torch, max(5, args.steps // 2), 2)
+    assert int(err.item()) == 0 and torch.equal(b, b_atomic)
+    del ws_u
     f = lambda: qb.qb_uniform_hist(s, alpha, bounds, hist_u)
     f()
     torch.cuda.synchronize()
@@ -527,6 +558,7 @@ def k3_skew_suite(torch, qb, synth, dev, args):
     torch.cuda.synchronize()
     bin_us = e0.elapsed_time(e1) * 1e3 / 10
     out = dict(N=N, E=E, K=K, n_bins=1000, us_per_step=round(sec * 1e6, 2), tokens_per_s=N / sec,
+               merge="global atomics", us_per_step_workspace_merge=round(sec_ws * 1e6, 2),
                step_GBps=round(N * (8 * E + 8) / sec / 1e9, 1), binning_pass_us=round(bin_us, 2),
                binning_pass_GBps=round(N * (4 * E + 4) / bin_us / 1e3, 1))
     del s, hist_u

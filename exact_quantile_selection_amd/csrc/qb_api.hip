@@ -517,6 +517,47 @@ QB_API int qb_uniform_hist(const float* s, const float* alpha, int L, int64_t N,
   return hip_status(qbk::launch_uniform_hist(s, alpha, L, N, E, bounds, n_bins, hist_u, stream), fn);
 }
 
+QB_API int64_t qb_uniform_hist_workspace_bytes(int L, int64_t N, int E, int n_bins) {
+  if (L < 1 || N < 1 || !qbk::supported_E(E) || n_bins < 1 || n_bins > 2048) return QB_EINVAL;
+  return qbk::uh_ws_layout(L, E, qbk::uniform_hist_groups(L, N, E, n_bins), n_bins).bytes;
+}
+
+QB_API int qb_uniform_hist_ws(const float* s, const float* alpha, int L, int64_t N, int E, const float* bounds,
+                              int n_bins, void* ws, int64_t ws_bytes, qb_stream_t stream) {
+  const char* fn = "qb_uniform_hist_ws";
+  if (int rc = check_pass(fn, s, L, N, E)) return rc;
+  if (!alpha || !bounds || !ws)
+    return fail(QB_EINVAL, "%s: alpha (float [L][N]), bounds (float [L=%d][2]) and ws are required", fn, L);
+  if (n_bins < 1 || n_bins > 2048)
+    return fail(QB_EINVAL, "%s: n_bins=%d, expected 1 <= n_bins <= 2048", fn, n_bins);
+  const int64_t need = qb_uniform_hist_workspace_bytes(L, N, E, n_bins);
+  if (ws_bytes < need)
+    return fail(QB_EINVAL, "%s: ws_bytes=%lld, this shape needs %lld (qb_uniform_hist_workspace_bytes)", fn,
+                (long long)ws_bytes, (long long)need);
+  if (!aligned16(ws)) return fail(QB_EINVAL, "%s: ws must be 16-byte aligned", fn);
+  return hip_status(qbk::launch_uniform_hist_ws(s, alpha, L, N, E, bounds, n_bins, static_cast<uint8_t*>(ws), stream),
+                    fn);
+}
+
+QB_API int qb_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, const void* ws, int32_t* hist_u,
+                                float* q_out, float* b, float* bounds, int32_t* err, qb_stream_t stream) {
+  const char* fn = "qb_select_uniform_ws";
+  if (L < 1 || N < 1) return fail(QB_EINVAL, "%s: L=%d, N=%lld, expected both >= 1", fn, L, (long long)N);
+  if (!qbk::supported_E(E))
+    return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {16, 32, 64, 128, 256}", fn, E);
+  if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (n_bins < 1 || n_bins > 2048)
+    return fail(QB_EINVAL, "%s: n_bins=%d, expected 1 <= n_bins <= 2048", fn, n_bins);
+  if (!ws || !q_out || !b || !bounds)
+    return fail(QB_EINVAL, "%s: ws, q_out, b (float [L=%d][E=%d]) and bounds (float [L][2]) are required", fn, L, E);
+  if (!aligned16(ws) || (hist_u && !aligned4(hist_u)) || (err && !aligned4(err)))
+    return fail(QB_EINVAL, "%s: ws must be 16-byte aligned, hist_u and err 4-byte aligned", fn);
+  return hip_status(qbk::launch_select_uniform_ws(L, N, E, K, n_bins, qbk::uniform_hist_groups(L, N, E, n_bins),
+                                                  static_cast<const uint8_t*>(ws), hist_u, q_out, b, bounds, err,
+                                                  stream),
+                    fn);
+}
+
 QB_API int qb_bias_bounds(const float* b, int L, int E, float* bounds, qb_stream_t stream) {
   const char* fn = "qb_bias_bounds";
   if (!b || !bounds) return fail(QB_EINVAL, "%s: b (float [L][E]) and bounds (float [L][2]) are required", fn);

@@ -73,6 +73,33 @@ int launch_margin_keys(const float* s, const float* alpha, int L, int64_t N, int
 int launch_select(int phase, int L, int E, int K, const int32_t* hist, int n_bins,
                   int32_t* sel_hi, int32_t* rank_lo, uint16_t* key_out, float* q_out, float* b,
                   float* bounds, int32_t* err, hipStream_t st);
+// Workspace of the K3 binning pass: one partial row of n_bins counts per
+// (layer, expert j, workgroup g of j's slice), row r = (layer * E + j) * G +
+// g, G = uniform_hist_groups(...).  A row whose counts are all <= 255 is
+// stored as bytes (p8: rows of b8 bytes), any other as uint16 (p16: rows of
+// b16 bytes); flag[r] says which.  Every row's flag is written on every
+// pass, so the contents on entry do not matter.
+struct UhWs {
+  int64_t rows, b8, b16;  // row count, byte stride of the byte / uint16 rows
+  int64_t flag, p8, p16;  // byte offsets (256-aligned)
+  int64_t bytes;          // total
+};
+inline UhWs uh_ws_layout(int L, int E, int64_t G, int n_bins) {
+  UhWs w;
+  w.rows = int64_t(L) * E * G;
+  w.b8 = (int64_t(n_bins) + 15) / 16 * 16;
+  w.b16 = (2 * int64_t(n_bins) + 15) / 16 * 16;
+  w.flag = 0;
+  w.p8 = (w.rows + 255) / 256 * 256;
+  w.p16 = w.p8 + (w.rows * w.b8 + 255) / 256 * 256;
+  w.bytes = w.p16 + w.rows * w.b16;
+  return w;
+}
+int64_t uniform_hist_groups(int L, int64_t N, int E, int n_bins);
+int launch_uniform_hist_ws(const float* s, const float* alpha, int L, int64_t N, int E, const float* bounds,
+                           int n_bins, uint8_t* ws, hipStream_t st);
+int launch_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, int64_t G, const uint8_t* ws,
+                             int32_t* hist_u, float* q_out, float* b, float* bounds, int32_t* err, hipStream_t st);
 int launch_uniform_hist(const float* s, const float* alpha, int L, int64_t N, int E,
                         const float* bounds, int n_bins, int32_t* hist_u, hipStream_t st);
 int launch_bias_bounds(const float* b, int L, int E, float* bounds, hipStream_t st);

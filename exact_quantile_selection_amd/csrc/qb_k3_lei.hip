@@ -54,10 +54,14 @@ struct UHShape {
 // Row stride (dwords) of the packed counter table for n_bins bins.
 inline int uh_stride(int n_bins) { return (n_bins + 63) / 64 * 64 + 1; }
 
+// hist_u == nullptr: instead of the atomic flush, the workgroup stores each
+// expert's counts as its own partial row in the workspace ws (UhWs in
+// qb_internal.hpp) for a select that sums them.
 template <int S>
 __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
     const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int E,
-    const float* __restrict__ bounds, int n_bins, int stride, int wg_per_slice, int32_t* __restrict__ hist_u) {
+    const float* __restrict__ bounds, int n_bins, int stride, int wg_per_slice, int32_t* __restrict__ hist_u,
+    uint8_t* __restrict__ ws, UhWs wl) {
   using U = UHShape<S>;
   extern __shared__ uint32_t lds_u[];  // [S / 2][stride] packed pairs
   const int n_slices = E / S;
@@ -133,6 +137,51 @@ __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
     }
   }
   __syncthreads();
+  if (hist_u == nullptr) {
+    // Partial rows, one wave per dword row of the table (experts 2p and
+    // 2p + 1 of the slice): a ballot over the row decides bytes or uint16
+    // for each expert, then each lane stores 4 bins of each expert per step
+    // (non-temporal: read once, by the select).
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    for (int p = wave; p < S / 2; p += kUHWaves) {
+      const uint32_t* row = lds_u + p * stride;
+      bool big0 = false, big1 = false;
+      for (int b = lane; b < n_bins; b += kWave) {
+        const uint32_t v = row[b];
+        big0 |= (v & 0xFFFFu) > 255u;
+        big1 |= (v >> 16) > 255u;
+      }
+      const bool w0 = __ballot(big0) != 0, w1 = __ballot(big1) != 0;
+      const int64_t r0 = (int64_t(layer) * E + slice * S + 2 * p) * wg_per_slice + g;
+      const int64_t r1 = r0 + wg_per_slice;  // expert 2p + 1
+      if (lane == 0) {
+        ws[wl.flag + r0] = w0 ? 1 : 0;
+        ws[wl.flag + r1] = w1 ? 1 : 0;
+      }
+      for (int b = 4 * lane; b < n_bins; b += 4 * kWave) {
+        uint32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = b + k < n_bins ? row[b + k] : 0u;
+        const bool ws0[2] = {w0, w1};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t r = h ? r1 : r0;
+          uint32_t c[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) c[k] = h ? (v[k] >> 16) : (v[k] & 0xFFFFu);
+          if (ws0[h]) {
+            uint2* dst = reinterpret_cast<uint2*>(ws + wl.p16 + r * wl.b16 + 2 * b);
+            __builtin_nontemporal_store(c[0] | (c[1] << 16), &dst->x);
+            __builtin_nontemporal_store(c[2] | (c[3] << 16), &dst->y);
+          } else {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(ws + wl.p8 + r * wl.b8 + b);
+            __builtin_nontemporal_store(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), dst);
+          }
+        }
+      }
+    }
+    return;
+  }
   // Flush: the G workgroups of a slice add into the same counters, so each
   // starts its walk at a different block of the table (by its index g).
   // A thread takes two adjacent bins of one dword row (two experts), and
@@ -213,20 +262,25 @@ static int uh_allow_lds() {
   return int(hipSuccess);
 }
 
+// workgroups per CU that the table of S experts leaves room for (up to 4)
+template <int S>
+static int uh_per_cu(int n_bins) {
+  const size_t lds = size_t(S / 2) * size_t(uh_stride(n_bins)) * sizeof(uint32_t);
+  return lds > 80 * 1024 ? 1 : (lds > 40 * 1024 ? 2 : QB_UH_SMALL_PER_CU);
+}
+
 template <int S>
 static int launch_uh(const float* s, const float* alpha, int L, int64_t N, int E, const float* bounds,
-                     int n_bins, int32_t* hist_u, hipStream_t st) {
+                     int n_bins, int32_t* hist_u, uint8_t* ws, hipStream_t st) {
   const int stride = uh_stride(n_bins);
   const size_t lds = size_t(S / 2) * size_t(stride) * sizeof(uint32_t);
-  // workgroups per CU that the table leaves room for (up to 4)
-  const int per_cu = lds > 80 * 1024 ? 1 : (lds > 40 * 1024 ? 2 : QB_UH_SMALL_PER_CU);
   const int n_slices = E / S;
-  const int64_t G = uh_groups<S>(L, N, E, per_cu);
+  const int64_t G = uh_groups<S>(L, N, E, uh_per_cu<S>(n_bins));
   const int64_t blocks = int64_t(L) * n_slices * G;
   const int ea = uh_allow_lds<S>();
   if (ea != int(hipSuccess)) return ea;
   hipLaunchKernelGGL((k_uniform_hist<S>), dim3(unsigned(blocks)), dim3(kUHThreads), lds, st, s, alpha, N, E,
-                     bounds, n_bins, stride, int(G), hist_u);
+                     bounds, n_bins, stride, int(G), hist_u, ws, uh_ws_layout(L, E, G, n_bins));
   return int(hipGetLastError());
 }
 
@@ -244,13 +298,38 @@ static int launch_uh(const float* s, const float* alpha, int L, int64_t N, int E
 #define QB_UH_MIN_ROWS64 2048
 #endif
 
+// Slice width of the binning pass for a shape.
+static int uh_slice(int L, int64_t N, int E, int n_bins) {
+  if (E >= 64 && n_bins <= 1024 && N / uh_groups<64>(L, N, E, 1) >= QB_UH_MIN_ROWS64) return 64;
+  if (E >= 32 && N / uh_groups<32>(L, N, E, 1) >= QB_UH_MIN_ROWS) return 32;
+  return 16;
+}
+
+int64_t uniform_hist_groups(int L, int64_t N, int E, int n_bins) {
+  switch (uh_slice(L, N, E, n_bins)) {
+    case 64: return uh_groups<64>(L, N, E, uh_per_cu<64>(n_bins));
+    case 32: return uh_groups<32>(L, N, E, uh_per_cu<32>(n_bins));
+  }
+  return uh_groups<16>(L, N, E, uh_per_cu<16>(n_bins));
+}
+
+static int launch_uniform_hist_any(const float* s, const float* alpha, int L, int64_t N, int E,
+                                   const float* bounds, int n_bins, int32_t* hist_u, uint8_t* ws, hipStream_t st) {
+  switch (uh_slice(L, N, E, n_bins)) {
+    case 64: return launch_uh<64>(s, alpha, L, N, E, bounds, n_bins, hist_u, ws, st);
+    case 32: return launch_uh<32>(s, alpha, L, N, E, bounds, n_bins, hist_u, ws, st);
+  }
+  return launch_uh<16>(s, alpha, L, N, E, bounds, n_bins, hist_u, ws, st);
+}
+
 int launch_uniform_hist(const float* s, const float* alpha, int L, int64_t N, int E,
                         const float* bounds, int n_bins, int32_t* hist_u, hipStream_t st) {
-  if (E >= 64 && n_bins <= 1024 && N / uh_groups<64>(L, N, E, 1) >= QB_UH_MIN_ROWS64)
-    return launch_uh<64>(s, alpha, L, N, E, bounds, n_bins, hist_u, st);
-  if (E >= 32 && N / uh_groups<32>(L, N, E, 1) >= QB_UH_MIN_ROWS)
-    return launch_uh<32>(s, alpha, L, N, E, bounds, n_bins, hist_u, st);
-  return launch_uh<16>(s, alpha, L, N, E, bounds, n_bins, hist_u, st);
+  return launch_uniform_hist_any(s, alpha, L, N, E, bounds, n_bins, hist_u, nullptr, st);
+}
+
+int launch_uniform_hist_ws(const float* s, const float* alpha, int L, int64_t N, int E, const float* bounds,
+                           int n_bins, uint8_t* ws, hipStream_t st) {
+  return launch_uniform_hist_any(s, alpha, L, N, E, bounds, n_bins, nullptr, ws, st);
 }
 
 // ---------------------------------------------------------------------------

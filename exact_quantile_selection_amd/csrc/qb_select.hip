@@ -462,6 +462,116 @@ int launch_select_lo_ws(int L, int E, int G, const uint8_t* ws, const int32_t* s
   return int(hipGetLastError());
 }
 
+// K3 select from the binning pass's partial rows (qb_uniform_hist_ws): one
+// 1024-thread workgroup per (expert, layer).  Thread t adds bins
+// 4 (t % 256) .. + 3 (and + 1024 on a second step for more than 1024 bins)
+// over the rows t / 256, t / 256 + 4, ... of its expert, reading each row as
+// bytes or uint16 by its flag; the four row groups meet in LDS.  Then threads
+// 0..255 each own a contiguous run of the summed bins, and the rank scan and
+// the in-bin interpolation are those of k_select_rows (UNIFORM), with the
+// token count N given (every token adds one margin per expert, so every
+// consistent row sums to N).  The summed row optionally goes to hist_u
+// (overwritten).
+constexpr int kUWsThreads = 1024;
+__global__ __launch_bounds__(kUWsThreads) void k_select_uniform_ws(int64_t N, int E, int K, int n_bins, int G,
+                                                                   const uint8_t* __restrict__ ws, UhWs wl,
+                                                                   int32_t* __restrict__ hist_u,
+                                                                   float* __restrict__ q_out,
+                                                                   const float* __restrict__ bounds,
+                                                                   int32_t* __restrict__ err) {
+  __shared__ __align__(16) int32_t s_part[4][2048];
+  __shared__ int64_t s_wave[256 / kWave];
+  __shared__ int s_bin;
+  __shared__ int64_t s_before;
+  __shared__ int32_t s_cnt;
+  const int j = blockIdx.x, layer = blockIdx.y, t = threadIdx.x;
+  const int c4 = t & 255, rg = t >> 8;
+  const int64_t row0 = (int64_t(layer) * E + j) * G;
+  for (int b = 4 * c4; b < n_bins; b += 1024) {
+    int32_t acc[4] = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int g = rg; g < G; g += 4) {
+      const int64_t r = row0 + g;
+      if (ws[wl.flag + r]) {
+        const uint2 v = *reinterpret_cast<const uint2*>(ws + wl.p16 + r * wl.b16 + 2 * b);
+        acc[0] += int32_t(v.x & 0xFFFFu);
+        acc[1] += int32_t(v.x >> 16);
+        acc[2] += int32_t(v.y & 0xFFFFu);
+        acc[3] += int32_t(v.y >> 16);
+      } else {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(ws + wl.p8 + r * wl.b8 + b);
+        acc[0] += int32_t(v & 0xFFu);
+        acc[1] += int32_t((v >> 8) & 0xFFu);
+        acc[2] += int32_t((v >> 16) & 0xFFu);
+        acc[3] += int32_t(v >> 24);
+      }
+    }
+    *reinterpret_cast<int4*>(&s_part[rg][b]) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+  }
+  if (t == 0) s_bin = -1;
+  __syncthreads();
+  const int per = (n_bins + 255) / 256;  // <= 8
+  const int lane = t & (kWave - 1), wave = t / kWave;
+  const int h0 = t * per;
+  int64_t mine = 0, incl = 0;
+  if (t < 256) {
+    for (int k = 0; k < per; ++k) {
+      const int h = h0 + k;
+      if (h < n_bins) {
+        const int32_t c = s_part[0][h] + s_part[1][h] + s_part[2][h] + s_part[3][h];
+        mine += c;
+        if (hist_u) hist_u[(int64_t(layer) * E + j) * n_bins + h] = c;
+      }
+    }
+    incl = wave_incl_scan(mine, lane);
+    if (lane == kWave - 1) s_wave[wave] = incl;
+  }
+  __syncthreads();
+  const int64_t rank = (int64_t(K) * N + E - 1) / E;  // 1-based rank ceil(K*N/E)
+  int64_t total = 0;
+  for (int w = 0; w < 256 / kWave; ++w) total += s_wave[w];
+  if (t < 256) {
+    for (int w = 0; w < wave; ++w) incl += s_wave[w];
+    if (mine > 0 && incl >= rank && incl - mine < rank) {  // exactly one thread
+      int64_t run = incl - mine;
+      for (int k = 0; k < per; ++k) {
+        const int h = h0 + k;
+        const int32_t c = h < n_bins ? s_part[0][h] + s_part[1][h] + s_part[2][h] + s_part[3][h] : 0;
+        if (run + c >= rank) {
+          s_bin = h;
+          s_before = run;
+          s_cnt = c;
+          break;
+        }
+        run += c;
+      }
+    }
+  }
+  __syncthreads();
+  if (t != 0) return;
+  const int bin = s_bin;
+  int bits = total != N ? QB_ERR_ROW_TOTALS : 0;
+  if (bin < 0) bits |= QB_ERR_RANK;
+  if (bits && err) atomicOr(err, bits);
+  if (bin < 0 || bits) {
+    q_out[int64_t(layer) * E + j] = __builtin_nanf("");
+    return;
+  }
+  const double lo = double(bounds[2 * layer]);
+  const double w = (double(bounds[2 * layer + 1]) - lo) / double(n_bins);
+  const double frac = double(rank - s_before) / double(s_cnt);
+  q_out[int64_t(layer) * E + j] = float(lo + w * (double(bin) + frac));
+}
+
+int launch_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, int64_t G, const uint8_t* ws,
+                             int32_t* hist_u, float* q_out, float* b, float* bounds, int32_t* err, hipStream_t st) {
+  hipLaunchKernelGGL(k_select_uniform_ws, dim3(unsigned(E), unsigned(L)), dim3(kUWsThreads), 0, st, N, E, K, n_bins,
+                     int(G), ws, uh_ws_layout(L, E, G, n_bins), hist_u, q_out, bounds, err);
+  if (int rc = int(hipGetLastError())) return rc;
+  hipLaunchKernelGGL(k_finalize, dim3(unsigned(L)), dim3(kFinThreads), 0, st, E, q_out, b, bounds, err);
+  return int(hipGetLastError());
+}
+
 // ---------------------------------------------------------------------------
 // Next-range seed for the K3 mode: bounds = [min b - 1, max b + 1].
 __global__ void k_bias_bounds(const float* __restrict__ b, int L, int E, float* __restrict__ bounds) {

@@ -53,6 +53,8 @@ def lib() -> C.CDLL:
             "qb_margin_keys": [vp, vp, i32, i64, i32, vp, vp],
             "qb_select_update": [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp],
             "qb_uniform_hist": [vp, vp, i32, i64, i32, vp, i32, vp, vp],
+            "qb_uniform_hist_ws": [vp, vp, i32, i64, i32, vp, i32, vp, i64, vp],
+            "qb_select_uniform_ws": [i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "qb_bias_bounds": [vp, i32, i32, vp, vp],
             "qb_fill_i32": [vp, i64, C.c_int32, vp],
             "qb_lei_grad": [vp, vp, i64, i32, i32, f32, vp],
@@ -76,6 +78,8 @@ def lib() -> C.CDLL:
             fn.restype = C.c_int
         L.qb_hist_lo_workspace_bytes.argtypes = [i32, i64, i32]
         L.qb_hist_lo_workspace_bytes.restype = C.c_int64
+        L.qb_uniform_hist_workspace_bytes.argtypes = [i32, i64, i32, i32]
+        L.qb_uniform_hist_workspace_bytes.restype = C.c_int64
         L.qb_status_string.argtypes = [C.c_int]
         L.qb_status_string.restype = C.c_char_p
         L.qb_last_error.argtypes = []
@@ -179,6 +183,40 @@ def qb_uniform_hist(s, alpha, bounds, hist_u, stream=None):
         _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
         _ptr(bounds, torch.float32, "bounds", lead + (2,)), n_bins,
         _ptr(hist_u, torch.int32, "hist_u", lead + (E, n_bins)), _stream(stream)))
+
+
+def qb_uniform_hist_workspace_bytes(L, N, E, n_bins):
+    n = lib().qb_uniform_hist_workspace_bytes(L, N, E, n_bins)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def qb_uniform_hist_ws(s, alpha, bounds, ws, n_bins, stream=None):
+    """K3 binning into per-workgroup partial rows in ws (uint8 tensor of at
+    least qb_uniform_hist_workspace_bytes bytes)."""
+    L, N, E, lead = _lne(s)
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device.type != "cuda":
+        raise ValueError("ws must be a contiguous uint8 GPU tensor")
+    _check(lib().qb_uniform_hist_ws(
+        _ptr(s, torch.float32, "s"), _ptr(alpha, torch.float32, "alpha", lead + (N,)), L, N, E,
+        _ptr(bounds, torch.float32, "bounds", lead + (2,)), n_bins, ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def qb_select_uniform_ws(N, K, n_bins, ws, q_out, b, bounds, hist_u=None, err=None, stream=None):
+    """K3 select from the partial rows of qb_uniform_hist_ws, with the
+    in-place bias / bounds update; hist_u (optional) receives the summed
+    histogram."""
+    if b.dim() == 1:
+        L, E, lead = 1, b.shape[0], ()
+    else:
+        L, E = b.shape
+        lead = (L,)
+    _check(lib().qb_select_uniform_ws(
+        L, N, E, K, n_bins, ws.data_ptr(), _ptr(hist_u, torch.int32, "hist_u", lead + (E, n_bins), opt=True),
+        _ptr(q_out, torch.float32, "q_out", lead + (E,)), _ptr(b, torch.float32, "b", lead + (E,)),
+        _ptr(bounds, torch.float32, "bounds", lead + (2,)), _ptr(err, torch.int32, "err", (1,), opt=True),
+        _stream(stream)))
 
 
 def qb_bias_bounds(b, bounds, stream=None):
@@ -434,6 +472,15 @@ def k3_update(s, b, K, alpha, bounds, hist_u, q_out, err=None, stream=None):
     qb_uniform_hist(s, alpha, bounds, hist_u, stream=stream)
     qb_select_update(QB_SELECT_UNIFORM, K, hist_u, q_out=q_out, b=b, bounds=bounds, err=err,
                      stream=stream)
+
+
+def k3_update_ws(s, b, K, alpha, bounds, ws, q_out, n_bins=1000, hist_u=None, err=None, stream=None):
+    """k3_update with the binning merged through the workspace ws
+    (qb_uniform_hist_workspace_bytes): nothing to zero; same q, b and
+    bounds."""
+    qb_margins_topk(s, b, K, alpha, stream=stream)
+    qb_uniform_hist_ws(s, alpha, bounds, ws, n_bins, stream=stream)
+    qb_select_uniform_ws(s.shape[-2], K, n_bins, ws, q_out, b, bounds, hist_u=hist_u, err=err, stream=stream)
 
 
 def _mapped(tag):

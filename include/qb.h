@@ -21,7 +21,8 @@
  *   3. qb_radix_hist_lo                 (low-byte histogram inside that bin)
  *   4. qb_select_update(QB_SELECT_LO)   -> key, q, b_next in place, bounds
  * The K3 mode (1000 uniform bins over the current bounds) is
- *   qb_margins_topk (alpha only) -> qb_uniform_hist -> qb_select_update(UNIFORM).
+ *   qb_margins_topk (alpha only) -> qb_uniform_hist -> qb_select_update(UNIFORM),
+ * or, merged through a workspace, qb_uniform_hist_ws -> qb_select_uniform_ws.
  *
  * Conventions shared by every call:
  *   - Pointers are DEVICE pointers owned by the caller; the library keeps no
@@ -259,6 +260,35 @@ QB_API int qb_radix_lo_select_noalloc(const float* s, const float* alpha, int L,
  */
 QB_API int qb_uniform_hist(const float* s, const float* alpha, int L, int64_t N, int E,
                            const float* bounds, int n_bins, int32_t* hist_u, qb_stream_t stream);
+
+/*
+ * K3 with the merge moved from global atomics to the select, as the EQB
+ * workspace pair does for the low-byte histogram: every workgroup of the
+ * binning pass stores its counts as one partial row per expert in a caller
+ * workspace (a row whose n_bins counts are all <= 255 as uint8, any other as
+ * uint16, with a byte flag per row), and the select sums each expert's
+ * partial rows (integer sums) before the rank scan and the in-bin
+ * interpolation of qb_select_update(QB_SELECT_UNIFORM), then updates b and
+ * bounds in place.  Same q, b and bounds, bit for bit, as qb_uniform_hist
+ * into a zeroed hist_u + qb_select_update(QB_SELECT_UNIFORM); nothing needs
+ * zeroing.
+ *   qb_uniform_hist_workspace_bytes: bytes the workspace needs for this shape
+ *     (49 MB at 1,048,576 x 256 x 1000 bins, 25 MB at 65,536 tokens), or a
+ *     negative status.
+ *   qb_uniform_hist_ws: as qb_uniform_hist, writing ws (16-byte aligned;
+ *     overwritten, every row's flag written).
+ *   qb_select_uniform_ws: ws from the preceding qb_uniform_hist_ws with the
+ *     same L, N, E and n_bins; the rank is ceil(K N / E) (every token adds
+ *     one margin per expert), and an expert whose counts do not sum to N
+ *     gets QB_ERR_ROW_TOTALS and q = NaN (its layer is then left
+ *     unchanged, as in qb_select_update).  hist_u (nullable, int32
+ *     [L][E][n_bins]) receives the summed histogram (overwritten).
+ */
+QB_API int64_t qb_uniform_hist_workspace_bytes(int L, int64_t N, int E, int n_bins);
+QB_API int qb_uniform_hist_ws(const float* s, const float* alpha, int L, int64_t N, int E, const float* bounds,
+                              int n_bins, void* ws, int64_t ws_bytes, qb_stream_t stream);
+QB_API int qb_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, const void* ws, int32_t* hist_u,
+                                float* q_out, float* b, float* bounds, int32_t* err, qb_stream_t stream);
 
 /*
  * Histogram range from a bias vector: bounds[l] = {fl32(min b - 1),
