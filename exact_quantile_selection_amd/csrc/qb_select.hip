@@ -480,6 +480,7 @@ __global__ __launch_bounds__(kUWsThreads) void k_select_uniform_ws(int64_t N, in
                                                                    const float* __restrict__ bounds,
                                                                    int32_t* __restrict__ err) {
   __shared__ __align__(16) int32_t s_part[4][2048];
+  __shared__ uint8_t s_flag[kUWsThreads];
   __shared__ int64_t s_wave[256 / kWave];
   __shared__ int s_bin;
   __shared__ int64_t s_before;
@@ -487,26 +488,42 @@ __global__ __launch_bounds__(kUWsThreads) void k_select_uniform_ws(int64_t N, in
   const int j = blockIdx.x, layer = blockIdx.y, t = threadIdx.x;
   const int c4 = t & 255, rg = t >> 8;
   const int64_t row0 = (int64_t(layer) * E + j) * G;
-  for (int b = 4 * c4; b < n_bins; b += 1024) {
-    int32_t acc[4] = {0, 0, 0, 0};
-#pragma unroll 4
-    for (int g = rg; g < G; g += 4) {
-      const int64_t r = row0 + g;
-      if (ws[wl.flag + r]) {
-        const uint2 v = *reinterpret_cast<const uint2*>(ws + wl.p16 + r * wl.b16 + 2 * b);
-        acc[0] += int32_t(v.x & 0xFFFFu);
-        acc[1] += int32_t(v.x >> 16);
-        acc[2] += int32_t(v.y & 0xFFFFu);
-        acc[3] += int32_t(v.y >> 16);
-      } else {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(ws + wl.p8 + r * wl.b8 + b);
-        acc[0] += int32_t(v & 0xFFu);
-        acc[1] += int32_t((v >> 8) & 0xFFu);
-        acc[2] += int32_t((v >> 16) & 0xFFu);
-        acc[3] += int32_t(v >> 24);
+  // Rows in chunks of 1024: the chunk's flags go to LDS first, so that each
+  // row's load does not wait for its flag's.
+  int32_t acc[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};  // bins 4 c4 + k, and + 1024
+  for (int g0 = 0; g0 < G; g0 += kUWsThreads) {
+    const int gn = G - g0 < kUWsThreads ? G - g0 : kUWsThreads;
+    __syncthreads();  // the previous chunk's flags are read
+    if (t < gn) s_flag[t] = ws[wl.flag + row0 + g0 + t];
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int b = 4 * c4 + 1024 * pass;
+      if (b >= n_bins) break;
+#pragma unroll 8
+      for (int gi = rg; gi < gn; gi += 4) {
+        const int64_t r = row0 + g0 + gi;
+        if (s_flag[gi]) {
+          const uint2 v = *reinterpret_cast<const uint2*>(ws + wl.p16 + r * wl.b16 + 2 * b);
+          acc[pass][0] += int32_t(v.x & 0xFFFFu);
+          acc[pass][1] += int32_t(v.x >> 16);
+          acc[pass][2] += int32_t(v.y & 0xFFFFu);
+          acc[pass][3] += int32_t(v.y >> 16);
+        } else {
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(ws + wl.p8 + r * wl.b8 + b);
+          acc[pass][0] += int32_t(v & 0xFFu);
+          acc[pass][1] += int32_t((v >> 8) & 0xFFu);
+          acc[pass][2] += int32_t((v >> 16) & 0xFFu);
+          acc[pass][3] += int32_t(v >> 24);
+        }
       }
     }
-    *reinterpret_cast<int4*>(&s_part[rg][b]) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int b = 4 * c4 + 1024 * pass;
+    if (b < n_bins)
+      *reinterpret_cast<int4*>(&s_part[rg][b]) = make_int4(acc[pass][0], acc[pass][1], acc[pass][2], acc[pass][3]);
   }
   if (t == 0) s_bin = -1;
   __syncthreads();

@@ -193,3 +193,28 @@ def test_fused_epilogue_saturated_equals_unfused(O):
     ref_a, ref_load = O.alpha(s_np, b_np, K)
     G.assert_same("load", load_np, ref_load)
     G.assert_same("hist_hi", hist_np, O.eqb_layer(s_np, b_np, K)["hist_hi"])
+
+
+def test_fused_epilogue_without_loads(O):
+    """qb_router_fused with no load buffer (the loads then come from pass 2):
+    alpha and the high-byte histogram as with it, and the loads that
+    qb_radix_hist_lo_ws_loads counts afterwards equal the oracle's."""
+    N, H, E, K = 1500, 256, 256, 6
+    hidden_np, w_np, _, _, _, _ = synth.router(seed=12, N=N, H=H, E=E)
+    b_np = np.random.default_rng(13).uniform(-0.05, 0.05, E).astype(np.float32)
+    hidden, w, b = bf16_dev(hidden_np), bf16_dev(w_np), G.dev(b_np)
+    s = torch.empty((N, E), dtype=torch.float32, device=G.DEV)
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    buf = qb.EqbBuffers(1, E, device=G.DEV, lead=False)
+    G.say("fused epilogue without loads")
+    qb.qb_router_fused(hidden, w, b, K, s, alpha, hist_hi=buf.hist_hi)
+    qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo, err=buf.err)
+    ws = torch.empty(qb.qb_hist_lo_workspace_bytes(1, N, E), dtype=torch.uint8, device=G.DEV)
+    load = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+    qb.qb_radix_hist_lo_ws_loads(s, alpha, buf.sel_hi, ws, b, K, load)
+    torch.cuda.synchronize()
+    s_np = G.host(s)
+    ref = O.eqb_layer(s_np, b_np, K)
+    G.assert_same("alpha", G.host(alpha), ref["alpha"])
+    G.assert_same("hist_hi", G.host(buf.hist_hi), ref["hist_hi"])
+    G.assert_same("load (pass 2)", G.host(load), ref["load"])
