@@ -464,33 +464,33 @@ int launch_select_lo_ws(int L, int E, int G, const uint8_t* ws, const int32_t* s
 
 // K3 select from the binning pass's partial rows (qb_uniform_hist_ws): one
 // 1024-thread workgroup per (expert, layer).  Thread t adds bins
-// 4 (t % 256) .. + 3 (and + 1024 on a second step for more than 1024 bins)
-// over the rows t / 256, t / 256 + 4, ... of its expert, reading each row as
-// bytes or uint16 by its flag; the four row groups meet in LDS.  Then threads
-// 0..255 each own a contiguous run of the summed bins, and the rank scan and
-// the in-bin interpolation are those of k_select_rows (UNIFORM), with the
-// token count N given (every token adds one margin per expert, so every
-// consistent row sums to N).  The summed row optionally goes to hist_u
-// (overwritten).
+// 8 (t % 128) .. + 7 (and + 1024 on a second step for more than 1024 bins)
+// over the rows t / 128, t / 128 + 8, ... of its expert, one 16-byte
+// (uint16 row) or 8-byte (byte row) load per row, with the rows' flags
+// staged in LDS first so that no load waits for its flag; the eight row
+// groups meet in LDS.  Then threads 0..255 each own a contiguous run of the
+// summed bins, and the rank scan and the in-bin interpolation are those of
+// k_select_rows (UNIFORM), with the token count N given (every token adds
+// one margin per expert, so every consistent row sums to N).  The summed row
+// optionally goes to hist_u (overwritten).
 constexpr int kUWsThreads = 1024;
+constexpr int kUWsGroups = kUWsThreads / 128;  // row groups
 __global__ __launch_bounds__(kUWsThreads) void k_select_uniform_ws(int64_t N, int E, int K, int n_bins, int G,
                                                                    const uint8_t* __restrict__ ws, UhWs wl,
                                                                    int32_t* __restrict__ hist_u,
                                                                    float* __restrict__ q_out,
                                                                    const float* __restrict__ bounds,
                                                                    int32_t* __restrict__ err) {
-  __shared__ __align__(16) int32_t s_part[4][2048];
+  __shared__ __align__(16) int32_t s_part[kUWsGroups][2048];
   __shared__ uint8_t s_flag[kUWsThreads];
   __shared__ int64_t s_wave[256 / kWave];
   __shared__ int s_bin;
   __shared__ int64_t s_before;
   __shared__ int32_t s_cnt;
   const int j = blockIdx.x, layer = blockIdx.y, t = threadIdx.x;
-  const int c4 = t & 255, rg = t >> 8;
+  const int c8 = t & 127, rg = t >> 7;
   const int64_t row0 = (int64_t(layer) * E + j) * G;
-  // Rows in chunks of 1024: the chunk's flags go to LDS first, so that each
-  // row's load does not wait for its flag's.
-  int32_t acc[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};  // bins 4 c4 + k, and + 1024
+  int32_t acc[2][8] = {};  // bins 8 c8 + k, and + 1024
   for (int g0 = 0; g0 < G; g0 += kUWsThreads) {
     const int gn = G - g0 < kUWsThreads ? G - g0 : kUWsThreads;
     __syncthreads();  // the previous chunk's flags are read
@@ -498,44 +498,59 @@ __global__ __launch_bounds__(kUWsThreads) void k_select_uniform_ws(int64_t N, in
     __syncthreads();
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      const int b = 4 * c4 + 1024 * pass;
+      const int b = 8 * c8 + 1024 * pass;
       if (b >= n_bins) break;
 #pragma unroll 8
-      for (int gi = rg; gi < gn; gi += 4) {
+      for (int gi = rg; gi < gn; gi += kUWsGroups) {
         const int64_t r = row0 + g0 + gi;
         if (s_flag[gi]) {
-          const uint2 v = *reinterpret_cast<const uint2*>(ws + wl.p16 + r * wl.b16 + 2 * b);
-          acc[pass][0] += int32_t(v.x & 0xFFFFu);
-          acc[pass][1] += int32_t(v.x >> 16);
-          acc[pass][2] += int32_t(v.y & 0xFFFFu);
-          acc[pass][3] += int32_t(v.y >> 16);
+          const uint4 v = *reinterpret_cast<const uint4*>(ws + wl.p16 + r * wl.b16 + 2 * b);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            acc[pass][2 * k] += int32_t(w[k] & 0xFFFFu);
+            acc[pass][2 * k + 1] += int32_t(w[k] >> 16);
+          }
         } else {
-          const uint32_t v = *reinterpret_cast<const uint32_t*>(ws + wl.p8 + r * wl.b8 + b);
-          acc[pass][0] += int32_t(v & 0xFFu);
-          acc[pass][1] += int32_t((v >> 8) & 0xFFu);
-          acc[pass][2] += int32_t((v >> 16) & 0xFFu);
-          acc[pass][3] += int32_t(v >> 24);
+          const uint2 v = *reinterpret_cast<const uint2*>(ws + wl.p8 + r * wl.b8 + b);
+          const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            acc[pass][4 * k] += int32_t(w[k] & 0xFFu);
+            acc[pass][4 * k + 1] += int32_t((w[k] >> 8) & 0xFFu);
+            acc[pass][4 * k + 2] += int32_t((w[k] >> 16) & 0xFFu);
+            acc[pass][4 * k + 3] += int32_t(w[k] >> 24);
+          }
         }
       }
     }
   }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    const int b = 4 * c4 + 1024 * pass;
-    if (b < n_bins)
-      *reinterpret_cast<int4*>(&s_part[rg][b]) = make_int4(acc[pass][0], acc[pass][1], acc[pass][2], acc[pass][3]);
+    const int b = 8 * c8 + 1024 * pass;
+    if (b < n_bins) {
+      int4* dst = reinterpret_cast<int4*>(&s_part[rg][b]);
+      dst[0] = make_int4(acc[pass][0], acc[pass][1], acc[pass][2], acc[pass][3]);
+      dst[1] = make_int4(acc[pass][4], acc[pass][5], acc[pass][6], acc[pass][7]);
+    }
   }
   if (t == 0) s_bin = -1;
   __syncthreads();
   const int per = (n_bins + 255) / 256;  // <= 8
   const int lane = t & (kWave - 1), wave = t / kWave;
   const int h0 = t * per;
+  auto summed = [&](int h) {
+    int32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < kUWsGroups; ++q) c += s_part[q][h];
+    return c;
+  };
   int64_t mine = 0, incl = 0;
   if (t < 256) {
     for (int k = 0; k < per; ++k) {
       const int h = h0 + k;
       if (h < n_bins) {
-        const int32_t c = s_part[0][h] + s_part[1][h] + s_part[2][h] + s_part[3][h];
+        const int32_t c = summed(h);
         mine += c;
         if (hist_u) hist_u[(int64_t(layer) * E + j) * n_bins + h] = c;
       }
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(kUWsThreads) void k_select_uniform_ws(int64_t N, in
       int64_t run = incl - mine;
       for (int k = 0; k < per; ++k) {
         const int h = h0 + k;
-        const int32_t c = h < n_bins ? s_part[0][h] + s_part[1][h] + s_part[2][h] + s_part[3][h] : 0;
+        const int32_t c = h < n_bins ? summed(h) : 0;
         if (run + c >= rank) {
           s_bin = h;
           s_before = run;
