@@ -160,3 +160,43 @@ def test_fused_pass1_microbatch_loads(O, N, E, K, n_mb, quant):
     G.assert_same("load", G.host(load), ref["load"])
     G.assert_same("hist_hi", G.host(hist), ref["hist_hi"])
     G.assert_same("load_mb", G.host(load_mb), O.microbatch_loads(s, b, K, n_mb))
+
+
+def test_controller_step_graph_replays():
+    """One controller step (loads counted in pass 2) captured in a HIP graph
+    and replayed four times, with eager steps and synchronizations between
+    the replays: every replay gives the eager step's loads, microbatch
+    loads, MaxVio and bias, bit for bit."""
+    L, N, E, K, n_mb = 2, 8192, 64, 4, 2048
+    s = G.dev(synth.stream_batch(0, N, E, L=L))
+    ctl = BiasController(L, N, E, K, n_mb, device=G.DEV)
+    assert ctl.loads_in_pass2
+    b0 = ctl.b.clone()
+
+    def snapshot():
+        return [G.host(x) for x in (ctl.load, ctl.load_mb, ctl.mv_global, ctl.mv_local, ctl.b, ctl.buf.bounds)]
+
+    G.say("controller step graph replays")
+    ctl.step(s)  # eager reference from b0
+    torch.cuda.synchronize()
+    want = snapshot()
+    stream = torch.cuda.Stream()
+    ctl.b.copy_(b0)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ctl.step(s)  # warm-up outside capture
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    ctl.b.copy_(b0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        ctl.step(s)
+    for rep in range(4):
+        ctl.step(s)  # eager work between the replays
+        ctl.b.copy_(b0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, g, w in zip(("load", "load_mb", "mv_global", "mv_local", "b", "bounds"), snapshot(), want):
+            G.assert_same(f"replay {rep} {name}", g, w)
+        assert int(ctl.buf.err.item()) == 0
