@@ -454,12 +454,17 @@ def eqb_update_ws(s, b, K, alpha, buf: EqbBuffers, ws, load=None, reset_hist_hi=
     """eqb_update with pass 2 merged through the workspace `ws` (see
     qb_radix_hist_lo_ws): same results; buf.hist_lo receives the summed
     low-byte histogram.  buf.hist_hi must be zero on entry; with
-    reset_hist_hi it is zero again on return (cleared by the select)."""
+    reset_hist_hi it is zero again on return (cleared by the select).  With
+    `load`, the top-K loads are counted in pass 2 (qb_radix_hist_lo_ws_loads),
+    where they cost less than in pass 1."""
     L, N, E, lead = _lne(s)
-    qb_margins_topk(s, b, K, alpha, load=load, hist_hi=buf.hist_hi, stream=stream)
+    qb_margins_topk(s, b, K, alpha, hist_hi=buf.hist_hi, stream=stream)
     qb_select_update(QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
                      err=buf.err, stream=stream)
-    qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws, stream=stream)
+    if load is not None:
+        qb_radix_hist_lo_ws_loads(s, alpha, buf.sel_hi, ws, b, K, load, stream=stream)
+    else:
+        qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws, stream=stream)
     qb_select_lo_ws(N, ws, buf.sel_hi, buf.rank_lo, buf.q, b, buf.bounds, hist_lo=buf.hist_lo,
                     key_out=buf.key, err=buf.err, hist_hi=buf.hist_hi if reset_hist_hi else None,
                     stream=stream)
