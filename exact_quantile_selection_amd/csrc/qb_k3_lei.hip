@@ -19,7 +19,9 @@
 // instruction; the row stride of the counter table is one more than a
 // multiple of 64 dwords, so the lanes of different experts that hit the
 // same bin land in different banks.  The counts are flushed once per
-// workgroup into the int32 [E][n_bins] histogram with agent-scope atomics.
+// workgroup into the int32 [E][n_bins] histogram with agent-scope atomics,
+// or stored as the workgroup's partial rows in a workspace that the
+// workspace select (qb_select.hip) sums.
 #include <algorithm>
 #include <atomic>
 #include <mutex>

@@ -14,7 +14,9 @@
 // lane l owns a contiguous block of ceil(n_bins/64) bins, the lane totals
 // are prefix-summed across the wave (shuffles), a ballot finds the first
 // lane whose running count reaches the rank, and that lane walks its block.
-// A small per-layer kernel then forms the bias update; the float64 mean runs
+// The workspace selects (low byte, K3) first sum the passes' per-workgroup
+// partial rows, one workgroup per expert, then scan the sum.  A small
+// per-layer kernel then forms the bias update; the float64 mean runs
 // sequentially on one thread in expert order, so the result does not
 // depend on the launch shape.
 #include <algorithm>
