@@ -182,7 +182,10 @@ __device__ __forceinline__ void hist16_flush(const uint32_t* lds, int32_t* out, 
 // two experts, in either order).  out must be 8-byte aligned.  Each 32-bit
 // half takes its own sum: counts stay below 2^31, so the low half never
 // carries into the high one.
-template <int E>
+// NC > 1: the table is NC copies one after the other (counted by different
+// lanes), added here; the copies' counts of one counter sum to at most the
+// workgroup's rows (<= 65535), so the packed halves add without carries.
+template <int E, int NC = 1>
 __device__ __forceinline__ void hist16_flush_pairs(const uint32_t* lds, int32_t* out, int tid, int nthreads,
                                                    int start) {
   constexpr int HDW2 = (E / 2) * 128;
@@ -194,7 +197,13 @@ __device__ __forceinline__ void hist16_flush_pairs(const uint32_t* lds, int32_t*
     blk = blk >= nblk ? blk - nblk : blk;
     const int d2 = blk * nthreads + tid;
     if (d2 >= HDW2) continue;
-    const uint2 v = l2[d2];
+    uint2 v = l2[d2];
+#pragma unroll
+    for (int c = 1; c < NC; ++c) {
+      const uint2 w = l2[c * HDW2 + d2];
+      v.x += w.x;
+      v.y += w.y;
+    }
     if ((v.x | v.y) == 0u) continue;
     const int d = 2 * d2;
     const int pair = d >> 8;

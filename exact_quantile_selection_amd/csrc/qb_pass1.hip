@@ -8,13 +8,14 @@
 // Mixture-of-Experts" (summary page), EQB paragraph (first radix pass: 256-bin
 // histogram of the high byte of the bf16 margins).
 //
-// Layout on gfx950: a row of E fp32 scores is split over LPR = E/64 lanes
-// (E <= 64: one lane per row), each lane holding V = min(E, 64) scores in
-// registers (V/4 float4 loads).  A wave therefore takes 64/LPR rows per trip.
-// The lanes of one row read 64 contiguous bytes per load; the starting
-// column block is rotated by the row index so that, in every later
-// instruction, the 64 lanes of the wave touch 64 distinct experts (distinct
-// LDS banks for the histogram atomics, distinct bias entries).
+// Layout on gfx950: a row of E fp32 scores is split over 4 lanes, each
+// holding V = E/4 scores in registers (V/4 float4 loads), so a load
+// instruction covers 16 rows; a wave trip takes 16 / (V/4) such row groups
+// (64 scores per lane).  The lanes of one row read 64 contiguous bytes per
+// load; the starting column block is rotated by the row index so that, in
+// every later instruction, the lanes of the wave touch distinct experts
+// (distinct LDS banks for the histogram atomics, distinct bias entries) as
+// far as E allows.
 //   * top-(K+1): per-lane insertion with v_med3_f32 (one op per list slot),
 //     then DPP merges across the row's lanes (bitonic), the last merge only
 //     producing the minimum of the merged top list, which is alpha.
@@ -54,14 +55,28 @@ namespace qbk {
 template <bool LOAD, int P, bool MB = false>
 constexpr int p1_waves() { return P > 8 ? 8 : (MB ? 12 : QB_P1_WAVES); }
 
+// Every E splits a row over 4 lanes, so the lanes of one row read E bytes
+// contiguously (64 B at E = 16, 1 KiB at E = 256) and a load instruction
+// covers 16 rows; narrower rows give each lane several row groups per trip
+// (U), so that every lane holds 64 scores per trip at every E.  (One lane
+// per row for E <= 64 made each load instruction touch 64 rows 16 bytes at
+// a time: 1 GiB of scores at E = 64 took 247 us in pass 1 against 190 at
+// E = 256.)
 template <int E>
 struct P1Shape {
-  static constexpr int V = E < 64 ? E : 64;  // scores per lane
-  static constexpr int LPR = E / V;          // lanes per row
-  static constexpr int F4 = V / 4;           // float4 loads per lane
-  static constexpr int RPW = kWave / LPR;    // rows per wave trip
+  static constexpr int LPR = 4;              // lanes per row
+  static constexpr int V = E / LPR;          // scores per lane and row
+  static constexpr int F4 = V / 4;           // float4 loads per lane and row
+  static constexpr int RPW = kWave / LPR;    // rows per row group of a wave (16)
+  static constexpr int U = 16 / F4;          // row groups per wave trip
+  static constexpr int WROWS = RPW * U;      // rows per wave trip
   static constexpr int HDW = (E / 2) * 256;
-  static_assert(LPR == 1 || LPR == 2 || LPR == 4, "lanes per row");
+  // copies of the high-byte table (128 KiB in all): the 16 rows of a load
+  // instruction share E/4 expert groups, and with fewer than 256 experts
+  // lanes of different rows would add into the same hot counters; row rho
+  // of the group counts into copy rho % NC.
+  static constexpr int NC = 256 / E;
+  static_assert(E % 16 == 0 && E <= 256, "experts");
   static_assert((F4 & (F4 - 1)) == 0, "power-of-two loads per lane");
 };
 
@@ -247,12 +262,13 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
   }
   if constexpr (HM == 1) {
     if (valid) {
+      uint32_t* h = lds_hist + (S::NC > 1 ? (rho % S::NC) * S::HDW : 0);
 #pragma unroll
       for (int t = 0; t < S::F4; ++t) {
         const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
         const uint32_t swz = hist16_swizzle2(quad);
-        hist16_add_hi(lds_hist, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
-        hist16_add_hi(lds_hist, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
+        hist16_add_hi(h, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
+        hist16_add_hi(h, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
       }
     }
   }
@@ -278,7 +294,7 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   static_assert(!MB || LOAD, "microbatch loads need load counting");
   constexpr int kWaves = p1_waves<LOAD, P, MB>();
   constexpr int kThreads = kWaves * kWave;
-  __shared__ uint32_t lds_hist[HM == 1 ? S::HDW : 4];
+  __shared__ uint32_t lds_hist[HM == 1 ? S::HDW * S::NC : 4];
   __shared__ float lds_b[E];
   __shared__ int32_t lds_load[E];
 
@@ -292,7 +308,7 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   if (LOAD) load += int64_t(layer) * E;
   if (MB) load_mb += int64_t(layer) * (N / n_mb) * E;
 
-  if constexpr (HM == 1) hist16_zero<E>(lds_hist, tid, kThreads);
+  if constexpr (HM == 1) hist16_zero<E * S::NC>(lds_hist, tid, kThreads);
   for (int j = tid; j < E; j += kThreads) {
     lds_b[j] = b[j];
     lds_load[j] = 0;
@@ -303,7 +319,7 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int rho = lane / S::LPR;
   const int ql = lane % S::LPR;
-  constexpr int64_t kTrip = int64_t(kWaves) * S::RPW;
+  constexpr int64_t kTrip = int64_t(kWaves) * S::WROWS;
   if constexpr (!MB) {
     // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
     // Every wave runs the same number of trips (rows past N are clamped and
@@ -319,16 +335,21 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
     const int64_t trips = (N + kTrip - 1) / kTrip;
     const bool early = wave >= kWaves / 2;
     for (int64_t T = g; T < trips; T += wg_per_layer) {
-      const int64_t base = T * kTrip + int64_t(wave) * S::RPW;
-      float4 x[S::F4];
+      const int64_t base = T * kTrip + int64_t(wave) * S::WROWS;
+      float4 x[S::U][S::F4];
       if (early) {
-        p1_load<E>(s, base, N, rho, ql, x);
+#pragma unroll
+        for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, x[u]);
         __builtin_amdgcn_s_barrier();
       } else {
         __builtin_amdgcn_s_barrier();
-        p1_load<E>(s, base, N, rho, ql, x);
+#pragma unroll
+        for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, x[u]);
       }
-      p1_rows<E, P, HM, LOAD>(x, base, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist);
+#pragma unroll
+      for (int u = 0; u < S::U; ++u)
+        p1_rows<E, P, HM, LOAD>(x[u], base + u * S::RPW, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha,
+                                ghist);
     }
   } else {
     // Contiguous block of whole trips, split at microbatch boundaries.
@@ -339,10 +360,14 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
     for (int64_t seg0 = r0; seg0 < r1;) {
       const int64_t mb = seg0 / n_mb;
       const int64_t seg1 = (mb + 1) * n_mb < r1 ? (mb + 1) * n_mb : r1;
-      for (int64_t base = seg0 + int64_t(wave) * S::RPW; base < seg1; base += kTrip) {
-        float4 x[S::F4];
-        p1_load<E>(s, base, seg1, rho, ql, x);
-        p1_rows<E, P, HM, LOAD>(x, base, seg1, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha, ghist);
+      for (int64_t base = seg0 + int64_t(wave) * S::WROWS; base < seg1; base += kTrip) {
+        float4 x[S::U][S::F4];
+#pragma unroll
+        for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, seg1, rho, ql, x[u]);
+#pragma unroll
+        for (int u = 0; u < S::U; ++u)
+          p1_rows<E, P, HM, LOAD>(x[u], base + u * S::RPW, seg1, rho, ql, lane, K, lds_b, lds_hist, lds_load,
+                                  alpha, ghist);
       }
       __syncthreads();
       for (int j = tid; j < E; j += kThreads) {
@@ -361,7 +386,8 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   // The high-byte counts crowd into a few adjacent bins per expert, so a
   // 64-bit atomic per bin pair halves the flush's atomics (190 -> 188 us
   // at 1M x 256).
-  if constexpr (HM == 1) hist16_flush_pairs<E>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
+  if constexpr (HM == 1)
+    hist16_flush_pairs<E, S::NC>(lds_hist, hist_hi + int64_t(layer) * E * 256, tid, kThreads, g);
   if constexpr (LOAD && !MB) {
     for (int j = tid; j < E; j += kThreads)
       if (lds_load[j]) atomicAdd(load + j, lds_load[j]);
@@ -373,7 +399,7 @@ static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t 
                        int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb = nullptr,
                        int64_t n_mb = 1) {
   constexpr int kThreads = p1_waves<LOAD, P, MB>() * kWave;
-  const RowSplit sp = split_rows(L, N, p1_waves<LOAD, P, MB>() * P1Shape<E>::RPW, QB_P1_MAXROWS);
+  const RowSplit sp = split_rows(L, N, p1_waves<LOAD, P, MB>() * P1Shape<E>::WROWS, QB_P1_MAXROWS);
   hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD, MB>), dim3(unsigned(sp.blocks)), dim3(kThreads),
                      0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi, load_mb, n_mb);
   return int(hipGetLastError());
