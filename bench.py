@@ -722,6 +722,21 @@ def router_suite(torch, qb, synth, dev, args):
     t_pass1 = reps(lambda: qb.qb_margins_topk(s, b, K, alpha, load=load, hist_hi=hist), n)
     qb.qb_fill_i32(hist, 0)
     qb.qb_fill_i32(load, 0)
+    # the vendor GEMM (torch.mm, hipBLASLt) for comparison: bf16 output
+    # (half the score bytes) and fp32 output as the scores need, the latter
+    # also with a separate sigmoid
+    vendor = {}
+    wt = w.t()
+    vendor["bf16_out"] = reps(lambda: torch.mm(hidden, wt), n)
+    try:
+        s32 = torch.empty((N, E), dtype=torch.float32, device=dev)
+        vendor["fp32_out"] = reps(lambda: torch.mm(hidden, wt, out_dtype=torch.float32), n)
+        vendor["fp32_out_then_sigmoid"] = reps(
+            lambda: torch.sigmoid(torch.mm(hidden, wt, out_dtype=torch.float32), out=s32), n)
+        del s32
+    except (RuntimeError, TypeError) as e:  # out_dtype not supported by this build
+        vendor["fp32_out_error"] = str(e)[:120]
+    torch.cuda.empty_cache()
 
     ws = torch.empty(qb.qb_hist_lo_workspace_bytes(1, N, E), dtype=torch.uint8, device=dev)
 
@@ -780,6 +795,7 @@ def router_suite(torch, qb, synth, dev, args):
                chain_fused_loads_in_pass2_us=round(chains["fused_loads_in_pass2"] * 1e6, 2),
                chain_unfused_loads_in_pass2_us=round(chains["unfused_loads_in_pass2"] * 1e6, 2),
                chain_same_b_next_and_lei=True,
+               vendor_gemm_us={k: (round(v * 1e6, 2) if isinstance(v, float) else v) for k, v in vendor.items()},
                chain="router GEMM + sigmoid, pass 1 (in the GEMM's epilogue, or after it), select HI, "
                      "pass 2, select LO, LEI; one graph of the steps",
                timing="HIP events around back-to-back launches of each call")
