@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -118,6 +119,21 @@ int hip_status(int rc, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+// Every non-null pointer of the list is a multiple of `a` bytes (a power of
+// two): the element alignment of the float, int32 and uint16 arrays.
+bool aligned_all(uintptr_t a, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0) return false;
+  return true;
+}
+
+// The element alignment of a call's 4-byte arrays and 2-byte keys.
+int check_elem_align(const char* fn, std::initializer_list<const void*> words, const void* key = nullptr) {
+  if (!aligned_all(4, words)) return fail(QB_EINVAL, "%s: float and int32 arrays must be 4-byte aligned", fn);
+  if (!aligned_all(2, {key})) return fail(QB_EINVAL, "%s: key_out must be 2-byte aligned", fn);
+  return QB_OK;
+}
 
 // Common shape checks of the passes over s [L][N][E].
 int check_pass(const char* fn, const float* s, int L, int64_t N, int E) {
@@ -290,6 +306,7 @@ QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_
     return fail(QB_EINVAL, "%s: ws_bytes=%lld, this shape needs %lld (qb_hist_lo_workspace_bytes)", fn,
                 (long long)ws_bytes, (long long)need);
   if (!aligned16(ws)) return fail(QB_EINVAL, "%s: ws must be 16-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {alpha, sel_hi})) return rc;
   return hip_status(qbk::launch_radix_hist_lo_ws(s, alpha, L, N, E, sel_hi, static_cast<uint8_t*>(ws), stream), fn);
 }
 
@@ -310,6 +327,7 @@ QB_API int qb_radix_hist_lo_ws_loads(const float* s, const float* alpha, int L, 
   if (!aligned16(ws)) return fail(QB_EINVAL, "%s: ws must be 16-byte aligned", fn);
   if (!aligned4(b) || !aligned4(load) || (load_mb && !aligned4(load_mb)))
     return fail(QB_EINVAL, "%s: b, load and load_mb must be 4-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {alpha, sel_hi})) return rc;
   if (load_mb) {
     const int trip = qbk::radix_lo_trip_rows(E);
     if (n_mb < 1 || N % n_mb != 0 || n_mb % trip != 0)
@@ -334,6 +352,7 @@ QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_
                 fn, L, E);
   if (!aligned16(ws) || (hist_lo && !aligned4(hist_lo)) || (hist_hi && !aligned4(hist_hi)))
     return fail(QB_EINVAL, "%s: ws must be 16-byte aligned, hist_lo and hist_hi 4-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {sel_hi, rank_lo, q_out, b, bounds, err}, key_out)) return rc;
   return hip_status(qbk::launch_select_lo_ws(L, E, qbk::radix_wg_per_layer(L, N, E), static_cast<const uint8_t*>(ws),
                                              sel_hi, rank_lo, hist_lo, key_out, q_out, b, bounds, hist_hi, err,
                                              stream),
@@ -400,6 +419,7 @@ QB_API int qb_radix_lo_select_noalloc(const float* s, const float* alpha, int L,
                 fn, L, E);
   if ((hist_lo && !aligned4(hist_lo)) || (hist_hi && !aligned4(hist_hi)))
     return fail(QB_EINVAL, "%s: hist_lo and hist_hi must be 4-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {alpha, sel_hi, rank_lo, q_out, b, bounds, err}, key_out)) return rc;
   const int64_t one = group_ws_bytes(1, N, E);
   if (one > int64_t(QB_NOALLOC_SCRATCH_BYTES))
     return fail(QB_EINVAL,
@@ -436,6 +456,7 @@ QB_API int qb_radix_hist_hi(const float* s, const float* alpha, int L, int64_t N
     return fail(QB_EINVAL, "%s: alpha (float [L][N]) and hist_hi (int32 [L=%d][E=%d][256]) are required",
                 fn, L, E);
   if (!aligned8(hist_hi)) return fail(QB_EINVAL, "%s: hist_hi must be 8-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {alpha})) return rc;
   return hip_status(qbk::launch_radix_hist(false, s, alpha, L, N, E, nullptr, hist_hi, stream), fn);
 }
 
@@ -448,6 +469,7 @@ QB_API int qb_radix_hist_lo(const float* s, const float* alpha, int L, int64_t N
                 "%s: alpha (float [L][N]), sel_hi (int32 [L=%d][E=%d]) and hist_lo (int32 [L][E][256]) are required",
                 fn, L, E);
   if (!aligned8(hist_lo)) return fail(QB_EINVAL, "%s: hist_lo must be 8-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {alpha, sel_hi})) return rc;
   return hip_status(qbk::launch_radix_hist(true, s, alpha, L, N, E, sel_hi, hist_lo, stream), fn);
 }
 
@@ -460,6 +482,7 @@ QB_API int qb_margin_keys(const float* s, const float* alpha, int L, int64_t N, 
                 L, E);
   if ((reinterpret_cast<uintptr_t>(keys) & 7u) != 0)
     return fail(QB_EINVAL, "%s: keys must be 8-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {alpha})) return rc;
   return hip_status(qbk::launch_margin_keys(s, alpha, L, N, E, keys, stream), fn);
 }
 
@@ -505,6 +528,7 @@ QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist,
                   "%s: phase=%d, expected QB_SELECT_HI, QB_SELECT_LO, QB_SELECT_UNIFORM or QB_SELECT_FULL", fn,
                   phase);
   }
+  if (int rc = check_elem_align(fn, {hist, sel_hi, rank_lo, q_out, b, bounds, err}, key_out)) return rc;
   return hip_status(qbk::launch_select(phase, L, E, K, hist, n_bins, sel_hi, rank_lo, key_out, q_out, b,
                                        bounds, err, stream),
                     fn);
@@ -520,6 +544,7 @@ QB_API int qb_uniform_hist(const float* s, const float* alpha, int L, int64_t N,
                 fn, L, E);
   if (n_bins < 1 || n_bins > 2048)
     return fail(QB_EINVAL, "%s: n_bins=%d, expected 1 <= n_bins <= 2048", fn, n_bins);
+  if (int rc = check_elem_align(fn, {alpha, bounds, hist_u})) return rc;
   return hip_status(qbk::launch_uniform_hist(s, alpha, L, N, E, bounds, n_bins, hist_u, stream), fn);
 }
 
@@ -541,6 +566,7 @@ QB_API int qb_uniform_hist_ws(const float* s, const float* alpha, int L, int64_t
     return fail(QB_EINVAL, "%s: ws_bytes=%lld, this shape needs %lld (qb_uniform_hist_workspace_bytes)", fn,
                 (long long)ws_bytes, (long long)need);
   if (!aligned16(ws)) return fail(QB_EINVAL, "%s: ws must be 16-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {alpha, bounds})) return rc;
   return hip_status(qbk::launch_uniform_hist_ws(s, alpha, L, N, E, bounds, n_bins, static_cast<uint8_t*>(ws), stream),
                     fn);
 }
@@ -558,6 +584,7 @@ QB_API int qb_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, cons
     return fail(QB_EINVAL, "%s: ws, q_out, b (float [L=%d][E=%d]) and bounds (float [L][2]) are required", fn, L, E);
   if (!aligned16(ws) || (hist_u && !aligned4(hist_u)) || (err && !aligned4(err)))
     return fail(QB_EINVAL, "%s: ws must be 16-byte aligned, hist_u and err 4-byte aligned", fn);
+  if (int rc = check_elem_align(fn, {q_out, b, bounds})) return rc;
   return hip_status(qbk::launch_select_uniform_ws(L, N, E, K, n_bins, qbk::uniform_hist_groups(L, N, E, n_bins),
                                                   static_cast<const uint8_t*>(ws), hist_u, q_out, b, bounds, err,
                                                   stream),
@@ -568,6 +595,7 @@ QB_API int qb_bias_bounds(const float* b, int L, int E, float* bounds, qb_stream
   const char* fn = "qb_bias_bounds";
   if (!b || !bounds) return fail(QB_EINVAL, "%s: b (float [L][E]) and bounds (float [L][2]) are required", fn);
   if (L < 1 || E < 1) return fail(QB_EINVAL, "%s: L=%d E=%d, expected >= 1", fn, L, E);
+  if (int rc = check_elem_align(fn, {b, bounds})) return rc;
   return hip_status(qbk::launch_bias_bounds(b, L, E, bounds, stream), fn);
 }
 
@@ -630,6 +658,7 @@ QB_API int qb_lei_grad(float* g, const int32_t* load, int64_t N, int E, int K, f
   if (!qbk::supported_E(E))
     return fail(QB_EUNSUPPORTED, "%s: E=%d, expected E in {16, 32, 64, 128, 256}", fn, E);
   if (K < 1 || K >= E) return fail(QB_EINVAL, "%s: K=%d, expected 1 <= K < E=%d", fn, K, E);
+  if (int rc = check_elem_align(fn, {load})) return rc;
   return hip_status(qbk::launch_lei(g, load, N, E, K, eta, stream), fn);
 }
 

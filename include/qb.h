@@ -39,6 +39,9 @@
  *       hist_u  int32  [L][E][n_bins]
  *       sel_hi, rank_lo int32 [L][E];  key_out uint16 [L][E]; q_out float [L][E]
  *       bounds  float  [L][2]  ({lo, hi})
+ *     Every array is aligned at least to its element (4 bytes; 2 for the
+ *     uint16 keys); the larger alignments above and in each call's notes
+ *     come on top.  A misaligned pointer is QB_EINVAL.
  *   - Histograms and loads are ACCUMULATED (+=) so that several token chunks
  *     (microbatches) of one global batch can be added into one buffer.  The
  *     caller clears them in place (qb_fill_i32) after the update; buffer

@@ -116,6 +116,32 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
         assert libqb.qb_status_string(st).startswith(b"QB_")
 
 
+def test_misaligned_element_arrays_are_rejected(libqb):
+    """float and int32 arrays must sit on 4-byte and the uint16 keys on
+    2-byte boundaries; a pointer off by one element part is refused before
+    any launch."""
+    from exact_quantile_selection_amd import qb
+
+    fake = 0x1000  # never dereferenced: validation fails first
+    rc = libqb.qb_select_update(qb.QB_SELECT_LO, 1, 256, 6, fake, 256, fake + 2, fake, None, fake, fake, fake,
+                                None, None)
+    assert rc == qb.QB_EINVAL and "4-byte aligned" in _last(libqb)
+    rc = libqb.qb_select_update(qb.QB_SELECT_LO, 1, 256, 6, fake, 256, fake, fake, fake + 1, fake, fake, fake,
+                                None, None)
+    assert rc == qb.QB_EINVAL and "key_out must be 2-byte aligned" in _last(libqb)
+    rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 256, fake, fake, fake, None, None, fake, fake + 1, fake,
+                               None, None, None)
+    assert rc == qb.QB_EINVAL and "4-byte aligned" in _last(libqb)
+    rc = libqb.qb_radix_hist_lo(fake, fake + 2, 1, 10, 256, fake, fake, None)
+    assert rc == qb.QB_EINVAL and "4-byte aligned" in _last(libqb)
+    rc = libqb.qb_uniform_hist(fake, fake, 1, 10, 256, fake + 3, 1000, fake, None)
+    assert rc == qb.QB_EINVAL and "4-byte aligned" in _last(libqb)
+    rc = libqb.qb_bias_bounds(fake + 2, 1, 256, fake, None)
+    assert rc == qb.QB_EINVAL and "4-byte aligned" in _last(libqb)
+    rc = libqb.qb_lei_grad(fake, fake + 2, 10, 256, 6, C.c_float(1e-5), None)
+    assert rc == qb.QB_EINVAL and "4-byte aligned" in _last(libqb)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     from exact_quantile_selection_amd import qb
 
