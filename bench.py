@@ -176,8 +176,41 @@ def ceilings(torch, s, reps=10):
             sec = timed(lambda: sp.read(s, sink, per_cu * cus, u))
             sweep[f"grid={per_cu * cus},unroll={u}"] = round(nbytes / sec / 1e9, 1)
     best = max(sweep, key=sweep.get)
-    return {"read": dict(GBps=sweep[best], us=round(nbytes / sweep[best] / 1e3, 2), bytes=nbytes, best=best,
-                         frac_of_peak=round(sweep[best] / PEAK_HBM_GBS, 4), sweep=sweep)}
+    out = {"read": dict(GBps=sweep[best], us=round(nbytes / sweep[best] / 1e3, 2), bytes=nbytes, best=best,
+                        frac_of_peak=round(sweep[best] / PEAK_HBM_GBS, 4), sweep=sweep)}
+    out["copy"] = copy_ceiling(torch, s.view(-1)[: s.numel() // 2], reps)
+    return out
+
+
+def copy_ceiling(torch, src, reps=10):
+    """The measured ceiling of a stream that reads and writes equal amounts:
+    libstreamprobe's plain copy of `src` into a buffer of the same size at a
+    few (grid, unroll), HIP events around `reps` back-to-back launches;
+    GB/s counts the bytes read plus the bytes written."""
+    from exact_quantile_selection_amd import stream_probe as sp
+
+    cus = torch.cuda.get_device_properties(src.device).multi_processor_count
+    dst = torch.empty_like(src)
+    moved = 2 * src.numel() * src.element_size()
+    stream = torch.cuda.current_stream()
+    sweep = {}
+    for per_cu in (1, 2, 4, 8):
+        for u in (2, 4):
+            f = lambda: sp.copy(src, dst, per_cu * cus, u)
+            f()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            sweep[f"grid={per_cu * cus},unroll={u}"] = round(moved / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9, 1)
+    assert torch.equal(dst, src)
+    del dst
+    best = max(sweep, key=sweep.get)
+    return dict(GBps=sweep[best], us=round(moved / sweep[best] / 1e3, 2), bytes_moved=moved, best=best,
+                frac_of_peak=round(sweep[best] / PEAK_HBM_GBS, 4), sweep=sweep)
 
 
 def cpu_baseline(s_np, b_np, K, rows):
@@ -465,6 +498,15 @@ def lei_backward_suite(torch, qb, synth, dev, args):
         out["bounded_GBps" if bounded else "unbounded_GBps"] = round(16 * N * E / us / 1e3, 1)
     del grad, s, gout, d
     torch.cuda.empty_cache()
+    # the ceiling of a stream that reads 512 MiB and writes 512 MiB, as one
+    # launch of this kernel does: the plain copy of the stream probe
+    src = torch.ones(2 * N * E, dtype=torch.float32, device=dev)
+    ceil = copy_ceiling(torch, src)
+    del src
+    torch.cuda.empty_cache()
+    out["copy_ceiling"] = ceil
+    for k in ("unbounded", "bounded"):
+        out[f"{k}_frac_of_copy_ceiling"] = round(out[f"{k}_GBps"] / ceil["GBps"], 4)
     return out
 
 

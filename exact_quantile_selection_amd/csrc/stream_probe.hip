@@ -47,6 +47,31 @@ __global__ __launch_bounds__(kThreads) void k_read(const u32x4* __restrict__ p, 
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
+// The same walk, storing every item to dst at its own offset: a plain copy,
+// the ceiling of the passes that read and write equal amounts (the LEI
+// gradient offsets).
+template <int U>
+__global__ __launch_bounds__(kThreads) void k_copy(const u32x4* __restrict__ p, u32x4* __restrict__ q,
+                                                   int64_t n16) {
+  const int64_t trip_items = int64_t(kThreads) * U;
+  const int64_t stride = int64_t(gridDim.x) * trip_items;
+  for (int64_t base = int64_t(blockIdx.x) * trip_items; base < n16; base += stride) {
+    if (base + trip_items <= n16) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = p[base + int64_t(u) * kThreads + threadIdx.x];
+#pragma unroll
+      for (int u = 0; u < U; ++u) q[base + int64_t(u) * kThreads + threadIdx.x] = v[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + int64_t(u) * kThreads + threadIdx.x;
+        if (i < n16) q[i] = p[i];
+      }
+    }
+  }
+}
+
 bool bad_args(const void* p, int64_t bytes, int grid) {
   return p == nullptr || bytes < 16 || (bytes % 16) != 0 || (reinterpret_cast<uintptr_t>(p) % 16) != 0 ||
          grid < 1 || grid > (1 << 20);
@@ -55,6 +80,11 @@ bool bad_args(const void* p, int64_t bytes, int grid) {
 template <int U>
 void launch_read(const u32x4* q, int64_t n16, int grid, uint32_t* sink, hipStream_t st) {
   hipLaunchKernelGGL(k_read<U>, dim3(grid), dim3(kThreads), 0, st, q, n16, sink);
+}
+
+template <int U>
+void launch_copy(const u32x4* p, u32x4* q, int64_t n16, int grid, hipStream_t st) {
+  hipLaunchKernelGGL(k_copy<U>, dim3(grid), dim3(kThreads), 0, st, p, q, n16);
 }
 
 }  // namespace
@@ -72,6 +102,25 @@ int sp_read(const void* p, int64_t bytes, int grid, int unroll, uint32_t* sink, 
     case 4: launch_read<4>(q, n16, grid, sink, st); break;
     case 8: launch_read<8>(q, n16, grid, sink, st); break;
     case 16: launch_read<16>(q, n16, grid, sink, st); break;
+    default: return SP_EINVAL;
+  }
+  return hipGetLastError() == hipSuccess ? SP_OK : SP_EHIP;
+}
+
+int sp_copy(const void* src, void* dst, int64_t bytes, int grid, int unroll, sp_stream_t stream) {
+  if (bad_args(src, bytes, grid) || bad_args(dst, bytes, grid)) return SP_EINVAL;
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (a < b + bytes && b < a + bytes) return SP_EINVAL;  // overlapping buffers
+  const u32x4* p = static_cast<const u32x4*>(src);
+  u32x4* q = static_cast<u32x4*>(dst);
+  const int64_t n16 = bytes / 16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  switch (unroll) {
+    case 1: launch_copy<1>(p, q, n16, grid, st); break;
+    case 2: launch_copy<2>(p, q, n16, grid, st); break;
+    case 4: launch_copy<4>(p, q, n16, grid, st); break;
+    case 8: launch_copy<8>(p, q, n16, grid, st); break;
     default: return SP_EINVAL;
   }
   return hipGetLastError() == hipSuccess ? SP_OK : SP_EHIP;

@@ -24,6 +24,8 @@ def lib() -> C.CDLL:
         vp, i32, i64 = C.c_void_p, C.c_int, C.c_int64
         L.sp_read.argtypes = [vp, i64, i32, i32, vp, vp]
         L.sp_read.restype = i32
+        L.sp_copy.argtypes = [vp, vp, i64, i32, i32, vp]
+        L.sp_copy.restype = i32
         _lib = L
     return _lib
 
@@ -47,3 +49,15 @@ def read(t: torch.Tensor, sink: torch.Tensor, grid: int, unroll: int) -> None:
     rc = lib().sp_read(C.c_void_p(t.data_ptr()), nbytes, grid, unroll, C.c_void_p(sink.data_ptr()), _stream())
     if rc != 0:
         raise RuntimeError(f"sp_read failed ({rc}): bytes={nbytes} grid={grid} unroll={unroll}")
+
+
+def copy(src: torch.Tensor, dst: torch.Tensor, grid: int, unroll: int) -> None:
+    """Copy every byte of src into dst (same size, no overlap)."""
+    _check(src, "src")
+    _check(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    rc = lib().sp_copy(C.c_void_p(src.data_ptr()), C.c_void_p(dst.data_ptr()), nbytes, grid, unroll, _stream())
+    if rc != 0:
+        raise RuntimeError(f"sp_copy failed ({rc}): bytes={nbytes} grid={grid} unroll={unroll}")
