@@ -776,7 +776,7 @@ def router_suite(torch, qb, synth, dev, args):
         vendor["fp32_out_then_sigmoid"] = reps(
             lambda: torch.sigmoid(torch.mm(hidden, wt, out_dtype=torch.float32), out=s32), n)
         del s32
-    except (RuntimeError, TypeError) as e:  # out_dtype not supported by this build
+    except (RuntimeError, TypeError) as e:  # out_dtype not supported by this PyTorch
         vendor["fp32_out_error"] = str(e)[:120]
     torch.cuda.empty_cache()
 
