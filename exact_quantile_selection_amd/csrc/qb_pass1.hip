@@ -34,6 +34,14 @@
 #include "qb_device.hpp"
 #include "qb_internal.hpp"
 
+// Pass 1 without loads refills each score slot with the next trip's row as
+// soon as the slot's key is counted (1; 0: the whole trip loaded at once by
+// half of the waves before the trip's barrier and half after it; 2: rolling
+// without the barrier).
+#ifndef QB_P1_ROLL
+#define QB_P1_ROLL 1
+#endif
+
 // Rows per workgroup at most (16-bit LDS counters hold 65535); smaller
 // values give more, shorter-lived workgroups.
 #ifndef QB_P1_MAXROWS
@@ -209,6 +217,65 @@ __device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N,
   }
 }
 
+// p1_rows without loads (HM = 1) that refills each slot of x with the next
+// trip's scores (rows nbase + rho) as soon as the slot's last use, its key,
+// is done: the next trip streams in while this one is counted.
+template <int E, int P>
+__device__ __forceinline__ void p1_rows_roll(float4 (&x)[P1Shape<E>::F4], const float* s, int64_t base,
+                                             int64_t nbase, bool more, int64_t N, int rho, int ql,
+                                             const float* lds_b, uint32_t* lds_hist, float* alpha) {
+  using S = P1Shape<E>;
+  const int64_t row = base + rho;
+  const bool valid = row < N;
+  int rot = rho;
+  asm volatile("" : "+v"(rot));
+  float top[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) top[k] = -__builtin_inff();
+#pragma unroll
+  for (int t = 0; t < S::F4; ++t) {
+    const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+    const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
+    top_insert<P>(top, x[t].x + bb.x);
+    top_insert<P>(top, x[t].y + bb.y);
+    top_insert<P>(top, x[t].z + bb.z);
+    top_insert<P>(top, x[t].w + bb.w);
+  }
+  float a;
+  if constexpr (S::LPR == 1) {
+    a = top[P - 1];
+  } else if constexpr (S::LPR == 2) {
+    a = top_merge_last<P, kQuadXor1>(top);
+  } else {
+    top_merge<P, kQuadXor1>(top);
+    a = top_merge_last<P, kQuadXor2>(top);
+  }
+  if (valid && ql == 0) __builtin_nontemporal_store(a, alpha + row);
+  uint32_t* h = lds_hist + (S::NC > 1 ? (rho % S::NC) * S::HDW : 0);
+  if (more) {
+    const int64_t nrow = nbase + rho;
+    const float* np = s + (nrow < N ? nrow : N - 1) * E;
+#pragma unroll
+    for (int t = 0; t < S::F4; ++t) {
+      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+      if (valid) {
+        const uint32_t swz = hist16_swizzle2(quad);
+        hist16_add_hi(h, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
+        hist16_add_hi(h, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
+      }
+      x[t] = ld4(np + 4 * quad);
+    }
+  } else if (valid) {
+#pragma unroll
+    for (int t = 0; t < S::F4; ++t) {
+      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+      const uint32_t swz = hist16_swizzle2(quad);
+      hist16_add_hi(h, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
+      hist16_add_hi(h, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
+    }
+  }
+}
+
 // alpha, loads and the high-byte histogram of one trip's rows.
 template <int E, int P, int HM, bool LOAD>
 __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64_t base, int64_t N,
@@ -334,6 +401,32 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
     // no ordering until the flush, which a full barrier precedes.
     const int64_t trips = (N + kTrip - 1) / kTrip;
     const bool early = wave >= kWaves / 2;
+    if constexpr (QB_P1_ROLL != 0 && HM == 1 && !LOAD) {
+      // Rolling refill (p1_rows_roll): the next trip's rows stream in while
+      // this trip is counted, with no extra registers; the waves still meet
+      // once per trip.  EQB step against the half-and-half loads below:
+      // 1,048,576 x 256 371-376 against 373-381 us, 262,144 x 256 111 against
+      // 116.5 us, 65,536 x 256 54.7 against 56.9 us; one GiB of scores at
+      // E = 16 / 32 / 64 620 / 407 / 410 against 653 / 421 / 420 us; the
+      // 48-layer step 4.29 against 4.26-4.28 ms.  Without the barrier: 386-390
+      // us at 1M.
+      float4 x[S::U][S::F4];
+      if (g < trips) {
+        const int64_t base = int64_t(g) * kTrip + int64_t(wave) * S::WROWS;
+#pragma unroll
+        for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, x[u]);
+      }
+      for (int64_t T = g; T < trips; T += wg_per_layer) {
+        const int64_t base = T * kTrip + int64_t(wave) * S::WROWS;
+        const int64_t nbase = (T + wg_per_layer) * kTrip + int64_t(wave) * S::WROWS;
+        const bool more = T + wg_per_layer < trips;
+        if (QB_P1_ROLL == 1) __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int u = 0; u < S::U; ++u)
+          p1_rows_roll<E, P>(x[u], s, base + u * S::RPW, nbase + u * S::RPW, more, N, rho, ql, lds_b, lds_hist,
+                             alpha);
+      }
+    } else
     for (int64_t T = g; T < trips; T += wg_per_layer) {
       const int64_t base = T * kTrip + int64_t(wave) * S::WROWS;
       float4 x[S::U][S::F4];
