@@ -339,9 +339,9 @@ QB_API int qb_radix_hist_lo_ws_loads(const float* s, const float* alpha, int L, 
                     fn);
 }
 
-QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_t* sel_hi, const int32_t* rank_lo,
-                           int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
-                           int32_t* hist_hi, int32_t* err, qb_stream_t stream) {
+QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, int64_t ws_bytes, const int32_t* sel_hi,
+                           const int32_t* rank_lo, int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b,
+                           float* bounds, int32_t* hist_hi, int32_t* err, qb_stream_t stream) {
   const char* fn = "qb_select_lo_ws";
   if (L < 1 || N < 1) return fail(QB_EINVAL, "%s: L=%d, N=%lld, expected both >= 1", fn, L, (long long)N);
   if (!qbk::supported_E(E))
@@ -350,6 +350,10 @@ QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_
     return fail(QB_EINVAL,
                 "%s: ws, sel_hi, rank_lo (int32 [L=%d][E=%d]), q_out, b (float [L][E]) and bounds (float [L][2]) are required",
                 fn, L, E);
+  const int64_t need = qb_hist_lo_workspace_bytes(L, N, E);
+  if (ws_bytes < need)
+    return fail(QB_EINVAL, "%s: ws_bytes=%lld, this shape needs %lld (qb_hist_lo_workspace_bytes)", fn,
+                (long long)ws_bytes, (long long)need);
   if (!aligned16(ws) || (hist_lo && !aligned4(hist_lo)) || (hist_hi && !aligned4(hist_hi)))
     return fail(QB_EINVAL, "%s: ws must be 16-byte aligned, hist_lo and hist_hi 4-byte aligned", fn);
   if (int rc = check_elem_align(fn, {sel_hi, rank_lo, q_out, b, bounds, err}, key_out)) return rc;
@@ -571,8 +575,9 @@ QB_API int qb_uniform_hist_ws(const float* s, const float* alpha, int L, int64_t
                     fn);
 }
 
-QB_API int qb_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, const void* ws, int32_t* hist_u,
-                                float* q_out, float* b, float* bounds, int32_t* err, qb_stream_t stream) {
+QB_API int qb_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, const void* ws, int64_t ws_bytes,
+                                int32_t* hist_u, float* q_out, float* b, float* bounds, int32_t* err,
+                                qb_stream_t stream) {
   const char* fn = "qb_select_uniform_ws";
   if (L < 1 || N < 1) return fail(QB_EINVAL, "%s: L=%d, N=%lld, expected both >= 1", fn, L, (long long)N);
   if (!qbk::supported_E(E))
@@ -582,6 +587,10 @@ QB_API int qb_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, cons
     return fail(QB_EINVAL, "%s: n_bins=%d, expected 1 <= n_bins <= 2048", fn, n_bins);
   if (!ws || !q_out || !b || !bounds)
     return fail(QB_EINVAL, "%s: ws, q_out, b (float [L=%d][E=%d]) and bounds (float [L][2]) are required", fn, L, E);
+  const int64_t need = qb_uniform_hist_workspace_bytes(L, N, E, n_bins);
+  if (ws_bytes < need)
+    return fail(QB_EINVAL, "%s: ws_bytes=%lld, this shape needs %lld (qb_uniform_hist_workspace_bytes)", fn,
+                (long long)ws_bytes, (long long)need);
   if (!aligned16(ws) || (hist_u && !aligned4(hist_u)) || (err && !aligned4(err)))
     return fail(QB_EINVAL, "%s: ws must be 16-byte aligned, hist_u and err 4-byte aligned", fn);
   if (int rc = check_elem_align(fn, {q_out, b, bounds})) return rc;

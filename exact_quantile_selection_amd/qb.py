@@ -54,7 +54,7 @@ def lib() -> C.CDLL:
             "qb_select_update": [i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp],
             "qb_uniform_hist": [vp, vp, i32, i64, i32, vp, i32, vp, vp],
             "qb_uniform_hist_ws": [vp, vp, i32, i64, i32, vp, i32, vp, i64, vp],
-            "qb_select_uniform_ws": [i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
+            "qb_select_uniform_ws": [i32, i64, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp],
             "qb_bias_bounds": [vp, i32, i32, vp, vp],
             "qb_fill_i32": [vp, i64, C.c_int32, vp],
             "qb_lei_grad": [vp, vp, i64, i32, i32, f32, vp],
@@ -68,7 +68,7 @@ def lib() -> C.CDLL:
             "qb_lei_backward": [vp, vp, vp, i64, i32, i32, i64, f32, i32, vp, vp, vp],
             "qb_radix_hist_lo_ws": [vp, vp, i32, i64, i32, vp, vp, i64, vp],
             "qb_radix_hist_lo_ws_loads": [vp, vp, i32, i64, i32, vp, vp, i64, vp, i32, vp, i64, vp, vp],
-            "qb_select_lo_ws": [i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "qb_select_lo_ws": [i32, i64, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "qb_rank_average": [vp, i32, i32, vp, vp, vp],
             "qb_radix_lo_select_noalloc": [vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         }
@@ -132,6 +132,13 @@ def qb_margins_topk(s, b, K, alpha, load=None, hist_hi=None, stream=None):
         _ptr(load, torch.int32, "load", lead + (E,), opt=True),
         _ptr(hist_hi, torch.int32, "hist_hi", lead + (E, 256), opt=True), _stream(stream))
     _check(rc)
+
+
+def _ws(ws):
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or not ws.is_contiguous() \
+            or ws.device.type != "cuda":
+        raise ValueError("ws must be a contiguous uint8 GPU tensor")
+    return ws.data_ptr(), ws.numel()
 
 
 def qb_radix_hist_hi(s, alpha, hist_hi, stream=None):
@@ -212,8 +219,9 @@ def qb_select_uniform_ws(N, K, n_bins, ws, q_out, b, bounds, hist_u=None, err=No
     else:
         L, E = b.shape
         lead = (L,)
+    p, n = _ws(ws)
     _check(lib().qb_select_uniform_ws(
-        L, N, E, K, n_bins, ws.data_ptr(), _ptr(hist_u, torch.int32, "hist_u", lead + (E, n_bins), opt=True),
+        L, N, E, K, n_bins, p, n, _ptr(hist_u, torch.int32, "hist_u", lead + (E, n_bins), opt=True),
         _ptr(q_out, torch.float32, "q_out", lead + (E,)), _ptr(b, torch.float32, "b", lead + (E,)),
         _ptr(bounds, torch.float32, "bounds", lead + (2,)), _ptr(err, torch.int32, "err", (1,), opt=True),
         _stream(stream)))
@@ -365,8 +373,9 @@ def qb_select_lo_ws(N, ws, sel_hi, rank_lo, q_out, b, bounds, hist_lo=None, key_
     else:
         L, E = sel_hi.shape
         lead = (L,)
+    p, n = _ws(ws)
     _check(lib().qb_select_lo_ws(
-        L, N, E, ws.data_ptr(), _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)),
+        L, N, E, p, n, _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)),
         _ptr(rank_lo, torch.int32, "rank_lo", lead + (E,)),
         _ptr(hist_lo, torch.int32, "hist_lo", lead + (E, 256), opt=True),
         _ptr(key_out, torch.uint16, "key_out", lead + (E,), opt=True),

@@ -190,10 +190,11 @@ QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist,
  *     a negative status.  ws must be 16-byte aligned; its contents on entry
  *     do not matter (every row's flag is written).
  *   qb_radix_hist_lo_ws: as qb_radix_hist_lo, writing ws (overwritten).
- *   qb_select_lo_ws: as qb_select_update(QB_SELECT_LO) from ws; ws must be
- *     the workspace the preceding qb_radix_hist_lo_ws call wrote, with the
- *     same L, N and E.  hist_lo (nullable) receives the summed histogram
- *     (overwritten, not accumulated).  hist_hi (nullable, int32
+ *   qb_select_lo_ws: as qb_select_update(QB_SELECT_LO) from ws (ws_bytes
+ *     at least qb_hist_lo_workspace_bytes, so that a wrong N cannot read
+ *     past it); ws must be the workspace the preceding qb_radix_hist_lo_ws
+ *     call wrote, with the same L, N and E.  hist_lo (nullable) receives
+ *     the summed histogram (overwritten, not accumulated).  hist_hi (nullable, int32
  *     [L][E][256]): the high-byte histogram this update was selected from;
  *     it is zeroed in place (addresses unchanged) -- the reset that follows
  *     the bias update in the "Implementation" section -- so the next pass 1
@@ -202,9 +203,9 @@ QB_API int qb_select_update(int phase, int L, int E, int K, const int32_t* hist,
 QB_API int64_t qb_hist_lo_workspace_bytes(int L, int64_t N, int E);
 QB_API int qb_radix_hist_lo_ws(const float* s, const float* alpha, int L, int64_t N, int E, const int32_t* sel_hi,
                                void* ws, int64_t ws_bytes, qb_stream_t stream);
-QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, const int32_t* sel_hi, const int32_t* rank_lo,
-                           int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b, float* bounds,
-                           int32_t* hist_hi, int32_t* err, qb_stream_t stream);
+QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, int64_t ws_bytes, const int32_t* sel_hi,
+                           const int32_t* rank_lo, int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b,
+                           float* bounds, int32_t* hist_hi, int32_t* err, qb_stream_t stream);
 
 /*
  * qb_radix_hist_lo_ws that also counts the top-K loads on its read of the
@@ -286,12 +287,15 @@ QB_API int qb_uniform_hist(const float* s, const float* alpha, int L, int64_t N,
  *     gets QB_ERR_ROW_TOTALS and q = NaN (its layer is then left
  *     unchanged, as in qb_select_update).  hist_u (nullable, int32
  *     [L][E][n_bins]) receives the summed histogram (overwritten).
+ *   qb_select_uniform_ws takes the workspace's size (ws_bytes) and refuses
+ *   one smaller than the shape needs, so that a wrong N cannot read past it.
  */
 QB_API int64_t qb_uniform_hist_workspace_bytes(int L, int64_t N, int E, int n_bins);
 QB_API int qb_uniform_hist_ws(const float* s, const float* alpha, int L, int64_t N, int E, const float* bounds,
                               int n_bins, void* ws, int64_t ws_bytes, qb_stream_t stream);
-QB_API int qb_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, const void* ws, int32_t* hist_u,
-                                float* q_out, float* b, float* bounds, int32_t* err, qb_stream_t stream);
+QB_API int qb_select_uniform_ws(int L, int64_t N, int E, int K, int n_bins, const void* ws, int64_t ws_bytes,
+                                int32_t* hist_u, float* q_out, float* b, float* bounds, int32_t* err,
+                                qb_stream_t stream);
 
 /*
  * Histogram range from a bias vector: bounds[l] = {fl32(min b - 1),

@@ -107,9 +107,12 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
     assert rc == qb.QB_EINVAL and "ws_bytes=16" in _last(libqb)
     rc = libqb.qb_radix_hist_lo_ws(fake, fake, 1, 1024, 256, fake, fake + 4, C.c_int64(1 << 30), None)
     assert rc == qb.QB_EINVAL and "16-byte aligned" in _last(libqb)
-    rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 48, fake, fake, fake, None, None, fake, None, None, None,
-                               None, None)
+    rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 48, fake, C.c_int64(1 << 30), fake, fake, None, None, fake,
+                               None, None, None, None, None)
     assert rc == qb.QB_EUNSUPPORTED and "E=48" in _last(libqb)
+    rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 256, fake, C.c_int64(16), fake, fake, None, None, fake,
+                               fake, fake, None, None, None)
+    assert rc == qb.QB_EINVAL and "ws_bytes=16" in _last(libqb)
     assert libqb.qb_fill_i32(None, 0, 0, None) == qb.QB_OK  # empty fill is a no-op
     assert libqb.qb_fill_i32(None, 5, 0, None) == qb.QB_EINVAL
     for st in (0, -1, -2, -3):
@@ -129,8 +132,8 @@ def test_misaligned_element_arrays_are_rejected(libqb):
     rc = libqb.qb_select_update(qb.QB_SELECT_LO, 1, 256, 6, fake, 256, fake, fake, fake + 1, fake, fake, fake,
                                 None, None)
     assert rc == qb.QB_EINVAL and "key_out must be 2-byte aligned" in _last(libqb)
-    rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 256, fake, fake, fake, None, None, fake, fake + 1, fake,
-                               None, None, None)
+    rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 256, fake, C.c_int64(1 << 30), fake, fake, None, None, fake,
+                               fake + 1, fake, None, None, None)
     assert rc == qb.QB_EINVAL and "4-byte aligned" in _last(libqb)
     rc = libqb.qb_radix_hist_lo(fake, fake + 2, 1, 10, 256, fake, fake, None)
     assert rc == qb.QB_EINVAL and "4-byte aligned" in _last(libqb)
@@ -266,7 +269,9 @@ def test_k3_workspace_entry_points_reject_bad_arguments(libqb):
     assert rc == qb.QB_EINVAL and "ws_bytes" in _last(libqb)
     rc = libqb.qb_uniform_hist_ws(fake, fake, 1, N, E, fake, 1000, fake + 4, wsb, None)
     assert rc == qb.QB_EINVAL and "16-byte" in _last(libqb)
-    rc = libqb.qb_select_uniform_ws(1, N, E, 0, 1000, fake, None, fake, fake, fake, None, None)
+    rc = libqb.qb_select_uniform_ws(1, N, E, 0, 1000, fake, wsb, None, fake, fake, fake, None, None)
     assert rc == qb.QB_EINVAL and "K=0" in _last(libqb)
-    rc = libqb.qb_select_uniform_ws(1, N, 48, 6, 1000, fake, None, fake, fake, fake, None, None)
+    rc = libqb.qb_select_uniform_ws(1, N, 48, 6, 1000, fake, wsb, None, fake, fake, fake, None, None)
     assert rc == qb.QB_EUNSUPPORTED and "E=48" in _last(libqb)
+    rc = libqb.qb_select_uniform_ws(1, N, E, 6, 1000, fake, wsb - 1, None, fake, fake, fake, None, None)
+    assert rc == qb.QB_EINVAL and "ws_bytes" in _last(libqb)
