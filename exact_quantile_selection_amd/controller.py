@@ -23,16 +23,22 @@ from . import qb
 class BiasController:
     """EQB bias state and metric buffers for L router layers of E experts."""
 
-    def __init__(self, L: int, N: int, E: int, K: int, n_mb: int, b0=None, device="cuda"):
+    def __init__(self, L: int, N: int, E: int, K: int, n_mb: int, b0=None, device="cuda",
+                 loads_in_pass2=None):
         if N % n_mb:
             raise ValueError(f"n_mb={n_mb} must divide N={N}")
         self.L, self.N, self.E, self.K, self.n_mb = L, N, E, K, n_mb
         self.C = N // n_mb
         # The low-byte pass counts the loads when its microbatches are whole
-        # row trips of that pass (every multiple of 2048 tokens is); it then
-        # costs 2-3 us at 262144 x 256 against 13 us for counting them in
-        # pass 1.  Other microbatch sizes count them in pass 1.
-        self.loads_in_pass2 = n_mb % 2048 == 0
+        # row trips of that pass (qb_radix_lo_trip_rows: 256 rows at E = 256,
+        # 2048 at E = 16); it then costs 2-3 us at 262144 x 256 against 13 us
+        # for counting them in pass 1.  Other microbatch sizes count them in
+        # pass 1; loads_in_pass2=False forces that path.
+        fits = n_mb % qb.qb_radix_lo_trip_rows(E) == 0
+        if loads_in_pass2 and not fits:
+            raise ValueError(f"n_mb={n_mb} is not a multiple of the low-byte pass's "
+                             f"{qb.qb_radix_lo_trip_rows(E)}-row trip at E={E}")
+        self.loads_in_pass2 = fits if loads_in_pass2 is None else bool(loads_in_pass2)
         kw = dict(device=device)
         self.b = (torch.zeros((L, E), dtype=torch.float32, **kw) if b0 is None
                   else b0.to(device=device, dtype=torch.float32).reshape(L, E).clone())

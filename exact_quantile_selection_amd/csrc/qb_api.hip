@@ -339,6 +339,12 @@ QB_API int qb_radix_hist_lo_ws_loads(const float* s, const float* alpha, int L, 
                     fn);
 }
 
+QB_API int qb_radix_lo_trip_rows(int E) {
+  if (!qbk::supported_E(E))
+    return fail(QB_EUNSUPPORTED, "qb_radix_lo_trip_rows: E=%d, expected E in {16, 32, 64, 128, 256}", E);
+  return qbk::radix_lo_trip_rows(E);
+}
+
 QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, int64_t ws_bytes, const int32_t* sel_hi,
                            const int32_t* rank_lo, int32_t* hist_lo, uint16_t* key_out, float* q_out, float* b,
                            float* bounds, int32_t* hist_hi, int32_t* err, qb_stream_t stream) {

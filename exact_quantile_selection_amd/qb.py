@@ -70,6 +70,7 @@ def lib() -> C.CDLL:
             "qb_radix_hist_lo_ws_loads": [vp, vp, i32, i64, i32, vp, vp, i64, vp, i32, vp, i64, vp, vp],
             "qb_select_lo_ws": [i32, i64, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "qb_rank_average": [vp, i32, i32, vp, vp, vp],
+            "qb_radix_lo_trip_rows": [i32],
             "qb_radix_lo_select_noalloc": [vp, vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         }
         for name, args in sig.items():
@@ -362,6 +363,15 @@ def qb_radix_hist_lo_ws_loads(s, alpha, sel_hi, ws, b, K, load, n_mb=None, load_
         _ptr(sel_hi, torch.int32, "sel_hi", lead + (E,)), ws.data_ptr(), ws.numel(),
         _ptr(b, torch.float32, "b", lead + (E,)), K, _ptr(load, torch.int32, "load", lead + (E,)),
         int(n_mb or 1), _ptr(load_mb, torch.int32, "load_mb", lead + (C, E), opt=True), _stream(stream)))
+
+
+def qb_radix_lo_trip_rows(E):
+    """Rows of one trip of the low-byte pass: per-microbatch loads counted
+    there need microbatches that are a multiple of it."""
+    n = lib().qb_radix_lo_trip_rows(E)
+    if n < 0:
+        _check(n)
+    return n
 
 
 def qb_select_lo_ws(N, ws, sel_hi, rank_lo, q_out, b, bounds, hist_lo=None, key_out=None, err=None,

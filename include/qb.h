@@ -229,6 +229,8 @@ QB_API int qb_select_lo_ws(int L, int64_t N, int E, const void* ws, int64_t ws_b
 QB_API int qb_radix_hist_lo_ws_loads(const float* s, const float* alpha, int L, int64_t N, int E,
                                      const int32_t* sel_hi, void* ws, int64_t ws_bytes, const float* b, int K,
                                      int32_t* load, int64_t n_mb, int32_t* load_mb, qb_stream_t stream);
+/* That row trip at E experts, max(256, 32768 / E), or QB_EUNSUPPORTED. */
+QB_API int qb_radix_lo_trip_rows(int E);
 
 /*
  * qb_radix_hist_lo_ws followed by qb_select_lo_ws, with the workspace taken

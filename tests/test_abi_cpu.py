@@ -113,6 +113,8 @@ def test_invalid_arguments_are_rejected_without_launch(libqb):
     rc = libqb.qb_select_lo_ws(1, C.c_int64(1024), 256, fake, C.c_int64(16), fake, fake, None, None, fake,
                                fake, fake, None, None, None)
     assert rc == qb.QB_EINVAL and "ws_bytes=16" in _last(libqb)
+    assert [libqb.qb_radix_lo_trip_rows(e) for e in (16, 32, 64, 128, 256)] == [2048, 1024, 512, 256, 256]
+    assert libqb.qb_radix_lo_trip_rows(48) == qb.QB_EUNSUPPORTED
     assert libqb.qb_fill_i32(None, 0, 0, None) == qb.QB_OK  # empty fill is a no-op
     assert libqb.qb_fill_i32(None, 5, 0, None) == qb.QB_EINVAL
     for st in (0, -1, -2, -3):

@@ -84,9 +84,9 @@ def oracle_loop(O, batches, b0, K, n_mb):
     return out
 
 
-def run_controller(batches, K, n_mb):
+def run_controller(batches, K, n_mb, loads_in_pass2=None):
     L, N, E = batches[0].shape
-    ctl = BiasController(L, N, E, K, n_mb, device=G.DEV)
+    ctl = BiasController(L, N, E, K, n_mb, device=G.DEV, loads_in_pass2=loads_in_pass2)
     got = []
     for t, s in enumerate(batches):
         G.say(f"controller step {t}")
@@ -113,14 +113,17 @@ def compare_loop(got, want):
         G.assert_same(f"step {t} local worst", g["wl"], w["local"][2])
 
 
-@pytest.mark.parametrize("n_mb", [1024, 2048])
-def test_closed_loop_two_layers(O, n_mb):
-    """n_mb = 1024: the loads are counted in pass 1; 2048: in the low-byte
-    pass."""
+@pytest.mark.parametrize("n_mb,in_pass2", [(1024, False), (2048, None), (512, None), (256, None)])
+def test_closed_loop_two_layers(O, n_mb, in_pass2):
+    """The loads counted in pass 1 (forced at n_mb = 1024; chosen for 256,
+    which is not a whole 512-row trip of the low-byte pass at E = 64) and in
+    the low-byte pass (2048 and 512, chosen by the controller)."""
     L, N, E, K, T = 2, 8192, 64, 4, 5
-    assert BiasController(L, N, E, K, n_mb, device=G.DEV).loads_in_pass2 == (n_mb == 2048)
+    ctl = BiasController(L, N, E, K, n_mb, device=G.DEV, loads_in_pass2=in_pass2)
+    assert qb.qb_radix_lo_trip_rows(E) == 512
+    assert ctl.loads_in_pass2 == (n_mb in (2048, 512))
     batches = [synth.stream_batch(t, N, E, L=L) for t in range(T)]
-    got = run_controller(batches, K, n_mb)
+    got = run_controller(batches, K, n_mb, loads_in_pass2=in_pass2)
     want = oracle_loop(O, batches, np.zeros((L, E), np.float32), K, n_mb)
     compare_loop(got, want)
     # the first batch is routed with b = 0 under skewed offsets; once the
