@@ -41,6 +41,12 @@
 #ifndef QB_P1_ROLL
 #define QB_P1_ROLL 1
 #endif
+// The rolling path issues its first trip's loads before it clears the LDS
+// table (65,536 x 256: EQB step 54.1-54.2 against 54.6-54.8 us; no change
+// at 262,144 and 1M tokens).
+#ifndef QB_P1_EARLY
+#define QB_P1_EARLY 1
+#endif
 
 // Rows per workgroup at most (16-bit LDS counters hold 65535); smaller
 // values give more, shorter-lived workgroups.
@@ -375,6 +381,22 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   if (LOAD) load += int64_t(layer) * E;
   if (MB) load_mb += int64_t(layer) * (N / n_mb) * E;
 
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  const int rho = lane / S::LPR;
+  const int ql = lane % S::LPR;
+  constexpr int64_t kTrip = int64_t(kWaves) * S::WROWS;
+  constexpr bool kRoll = QB_P1_ROLL != 0 && HM == 1 && !LOAD && !MB;
+  float4 xr[S::U][S::F4];  // the rolling path's score slots
+  if constexpr (kRoll && QB_P1_EARLY) {
+    // the first trip's loads go out before the table is cleared
+    if (g < (N + kTrip - 1) / kTrip) {
+      const int64_t base = int64_t(g) * kTrip + int64_t(wave) * S::WROWS;
+#pragma unroll
+      for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, xr[u]);
+    }
+  }
+
   if constexpr (HM == 1) hist16_zero<E * S::NC>(lds_hist, tid, kThreads);
   for (int j = tid; j < E; j += kThreads) {
     lds_b[j] = b[j];
@@ -382,11 +404,6 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   }
   __syncthreads();
 
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-  const int rho = lane / S::LPR;
-  const int ql = lane % S::LPR;
-  constexpr int64_t kTrip = int64_t(kWaves) * S::WROWS;
   if constexpr (!MB) {
     // Block-cyclic trips: this workgroup takes trips g, g + G, g + 2G, ...
     // Every wave runs the same number of trips (rows past N are clamped and
@@ -401,7 +418,7 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
     // no ordering until the flush, which a full barrier precedes.
     const int64_t trips = (N + kTrip - 1) / kTrip;
     const bool early = wave >= kWaves / 2;
-    if constexpr (QB_P1_ROLL != 0 && HM == 1 && !LOAD) {
+    if constexpr (kRoll) {
       // Rolling refill (p1_rows_roll): the next trip's rows stream in while
       // this trip is counted, with no extra registers; the waves still meet
       // once per trip.  EQB step against the half-and-half loads below:
@@ -410,8 +427,8 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
       // E = 16 / 32 / 64 620 / 407 / 410 against 653 / 421 / 420 us; the
       // 48-layer step 4.29 against 4.26-4.28 ms.  Without the barrier: 386-390
       // us at 1M.
-      float4 x[S::U][S::F4];
-      if (g < trips) {
+      auto& x = xr;
+      if (!QB_P1_EARLY && g < trips) {
         const int64_t base = int64_t(g) * kTrip + int64_t(wave) * S::WROWS;
 #pragma unroll
         for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, x[u]);
