@@ -149,9 +149,10 @@ def time_kernels(step, torch, reps):
 
 def ceilings(torch, s, reps=10):
     """The measured streaming ceiling over the same score tensor: the plain
-    read kernel of libstreamprobe (include/stream_probe.h) at every (grid,
-    unroll) of a small sweep, each timed with HIP events around `reps`
-    back-to-back launches; the fastest is the ceiling."""
+    read kernel of libstreamprobe (include/stream_probe.h), with cached and
+    with non-temporal loads, at every (grid, unroll) of a small sweep, each
+    timed with HIP events around `reps` back-to-back launches; the fastest
+    is the ceiling."""
     from exact_quantile_selection_amd import stream_probe as sp
 
     cus = torch.cuda.get_device_properties(s.device).multi_processor_count
@@ -171,10 +172,11 @@ def ceilings(torch, s, reps=10):
         return e0.elapsed_time(e1) * 1e-3 / reps
 
     sweep = {}
-    for per_cu in (1, 2, 4, 8, 16):
-        for u in (2, 4, 8):
-            sec = timed(lambda: sp.read(s, sink, per_cu * cus, u))
-            sweep[f"grid={per_cu * cus},unroll={u}"] = round(nbytes / sec / 1e9, 1)
+    for nt in (False, True):
+        for per_cu in (1, 2, 4, 8, 16):
+            for u in (2, 4, 8):
+                sec = timed(lambda: sp.read(s, sink, per_cu * cus, u, nontemporal=nt))
+                sweep[f"{'nontemporal,' if nt else ''}grid={per_cu * cus},unroll={u}"] = round(nbytes / sec / 1e9, 1)
     best = max(sweep, key=sweep.get)
     out = {"read": dict(GBps=sweep[best], us=round(nbytes / sweep[best] / 1e3, 2), bytes=nbytes, best=best,
                         frac_of_peak=round(sweep[best] / PEAK_HBM_GBS, 4), sweep=sweep)}

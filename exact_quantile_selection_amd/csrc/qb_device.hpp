@@ -45,6 +45,7 @@ __device__ __forceinline__ int quad_mov_i(int x) {
 }
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i of each group of 8 reads lane 7 - i
 
 // Insert v into a descending list t[0..P-1] keeping the P largest values:
 // t'_0 = max(t_0, v), t'_k = med3(t_{k-1}, t_k, v).  One VALU op per slot.
@@ -121,6 +122,14 @@ __device__ __forceinline__ float top_merge_last(const float (&t)[P]) {
 }
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// A non-temporal (streaming) 16-byte load.
+__device__ __forceinline__ float4 ld4_nt(const float* p) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 
 __device__ __forceinline__ float comp(const float4& v, int c) {
   return c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w));

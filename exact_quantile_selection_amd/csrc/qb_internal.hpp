@@ -22,6 +22,17 @@ RowSplit split_rows(int L, int64_t N, int step, int64_t max_rows);
 
 int device_cu_count();
 
+// A pass over this many bytes of scores per launch (at least three times the
+// MI355X's 256 MiB Infinity Cache) reads them with non-temporal loads: the
+// cache cannot hand much of such a layer from one pass to the next, and the
+// non-temporal stream is faster (the stream probe reads 1 GiB at 7.0 TB/s
+// with them against 6.3 without).  Smaller layers keep the cached loads, so
+// that the next pass finds the rows the last one read.
+#ifndef QB_STREAM_BYTES
+#define QB_STREAM_BYTES (768LL << 20)
+#endif
+inline bool stream_pass(int L, int64_t N, int E) { return int64_t(L) * N * E * 4 >= QB_STREAM_BYTES; }
+
 // Launchers (return hipError_t as int).  Shapes were validated by the caller.
 // bdiv: that many consecutive layers share one bias row (1: one row per
 // layer; C: layers are the C microbatches of one layer).

@@ -59,7 +59,7 @@ inline int uh_stride(int n_bins) { return (n_bins + 63) / 64 * 64 + 1; }
 // hist_u == nullptr: instead of the atomic flush, the workgroup stores each
 // expert's counts as its own partial row in the workspace ws (UhWs in
 // qb_internal.hpp) for a select that sums them.
-template <int S>
+template <int S, bool ST = false>
 __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
     const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int E,
     const float* __restrict__ bounds, int n_bins, int stride, int wg_per_slice, int32_t* __restrict__ hist_u,
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kUHThreads) void k_uniform_hist(
     for (int u = 0; u < kUHUnroll; ++u) {
       int64_t row = base + u * U::RPI + rsub;
       row = row < N ? row : N - 1;
-      x[u] = ld4(s + row * E + 4 * q);
+      x[u] = (ST ? ld4_nt : ld4)(s + row * E + 4 * q);
       a[u] = alpha[row];
     }
   };
@@ -243,7 +243,7 @@ constexpr int uh_max_bins() { return S == 64 ? 1024 : 2048; }
 // Allows k_uniform_hist<S> the dynamic LDS of the largest table any bin count
 // it serves can need (at most 131,200 B), once per device and thread-safe, so
 // a later call with more bins never launches past the allowed size.
-template <int S>
+template <int S, bool ST>
 static int uh_allow_lds() {
   static std::atomic<uint64_t> done{0};  // bit d: set on device d
   static std::mutex mu;
@@ -256,7 +256,7 @@ static int uh_allow_lds() {
   std::lock_guard<std::mutex> lock(mu);
   if (bit && (done.load(std::memory_order_relaxed) & bit)) return int(hipSuccess);
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uniform_hist<S>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_uniform_hist<S, ST>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return int(e);
   }
@@ -279,7 +279,18 @@ static int launch_uh(const float* s, const float* alpha, int L, int64_t N, int E
   const int n_slices = E / S;
   const int64_t G = uh_groups<S>(L, N, E, uh_per_cu<S>(n_bins));
   const int64_t blocks = int64_t(L) * n_slices * G;
-  const int ea = uh_allow_lds<S>();
+  // layers far larger than the Infinity Cache are read with non-temporal
+  // loads (stream_pass) when the row segments are whole lines (S >= 32)
+  if constexpr (S >= 32) {
+    if (stream_pass(L, N, E)) {
+      const int ea = uh_allow_lds<S, true>();
+      if (ea != int(hipSuccess)) return ea;
+      hipLaunchKernelGGL((k_uniform_hist<S, true>), dim3(unsigned(blocks)), dim3(kUHThreads), lds, st, s, alpha, N,
+                         E, bounds, n_bins, stride, int(G), hist_u, ws, uh_ws_layout(L, E, G, n_bins));
+      return int(hipGetLastError());
+    }
+  }
+  const int ea = uh_allow_lds<S, false>();
   if (ea != int(hipSuccess)) return ea;
   hipLaunchKernelGGL((k_uniform_hist<S>), dim3(unsigned(blocks)), dim3(kUHThreads), lds, st, s, alpha, N, E,
                      bounds, n_bins, stride, int(G), hist_u, ws, uh_ws_layout(L, E, G, n_bins));

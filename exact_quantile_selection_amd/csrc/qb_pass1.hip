@@ -76,12 +76,12 @@ constexpr int p1_waves() { return P > 8 ? 8 : (MB ? 12 : QB_P1_WAVES); }
 // per row for E <= 64 made each load instruction touch 64 rows 16 bytes at
 // a time: 1 GiB of scores at E = 64 took 247 us in pass 1 against 190 at
 // E = 256.)
-template <int E>
+template <int E, int LPR_ = 4>
 struct P1Shape {
-  static constexpr int LPR = 4;              // lanes per row
+  static constexpr int LPR = LPR_;           // lanes per row
   static constexpr int V = E / LPR;          // scores per lane and row
   static constexpr int F4 = V / 4;           // float4 loads per lane and row
-  static constexpr int RPW = kWave / LPR;    // rows per row group of a wave (16)
+  static constexpr int RPW = kWave / LPR;    // rows per row group of a wave
   static constexpr int U = 16 / F4;          // row groups per wave trip
   static constexpr int WROWS = RPW * U;      // rows per wave trip
   static constexpr int HDW = (E / 2) * 256;
@@ -93,6 +93,19 @@ struct P1Shape {
   static_assert(E % 16 == 0 && E <= 256, "experts");
   static_assert((F4 & (F4 - 1)) == 0, "power-of-two loads per lane");
 };
+
+// The high-byte table copy of row rho of a load instruction.  Rows rho and
+// rho' of one instruction read the same columns when rho = rho' mod F4, so
+// those NC rows take NC different copies.
+#ifndef QB_P1_COPYFIX
+#define QB_P1_COPYFIX 0
+#endif
+template <class S>
+__device__ __forceinline__ int p1_copy(int rho) {
+  if constexpr (QB_P1_COPYFIX != 0) return (rho / S::F4) % S::NC;
+  return rho % S::NC;
+}
+
 
 __device__ __forceinline__ uint64_t low_bits(int n) {
   return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
@@ -197,10 +210,10 @@ __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], c
 // Loads one trip's rows (this lane's V scores of row base + rho) into x.
 // `base` is wave-uniform: a full trip addresses its rows from a uniform base
 // pointer with 32-bit lane offsets; a partial last trip clamps the row.
-template <int E>
+template <int E, int LPR = 4, bool STREAM = false>
 __device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N, int rho, int ql,
-                                        float4 (&x)[P1Shape<E>::F4]) {
-  using S = P1Shape<E>;
+                                        float4 (&x)[(P1Shape<E, LPR>::F4)]) {
+  using S = P1Shape<E, LPR>;
   // The per-slot bias values, addresses and swizzles are loop-invariant;
   // kept invariant they would be hoisted out of the row loop and occupy ~100
   // VGPRs.  An opaque copy of the rotation makes them cheap per-trip work.
@@ -211,14 +224,14 @@ __device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N,
     const uint32_t lane_off = uint32_t(rho * E + 4 * ql);
 #pragma unroll
     for (int t = 0; t < S::F4; ++t)
-      x[t] = ld4(ws + (lane_off + uint32_t(4 * S::LPR * ((t + rot) & (S::F4 - 1)))));
+      x[t] = (STREAM ? ld4_nt : ld4)(ws + (lane_off + uint32_t(4 * S::LPR * ((t + rot) & (S::F4 - 1)))));
   } else {
     const int64_t row = base + rho;
     const float* src = s + (row < N ? row : N - 1) * E;
 #pragma unroll
     for (int t = 0; t < S::F4; ++t) {
       const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
-      x[t] = ld4(src + 4 * quad);
+      x[t] = (STREAM ? ld4_nt : ld4)(src + 4 * quad);
     }
   }
 }
@@ -226,11 +239,11 @@ __device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N,
 // p1_rows without loads (HM = 1) that refills each slot of x with the next
 // trip's scores (rows nbase + rho) as soon as the slot's last use, its key,
 // is done: the next trip streams in while this one is counted.
-template <int E, int P>
-__device__ __forceinline__ void p1_rows_roll(float4 (&x)[P1Shape<E>::F4], const float* s, int64_t base,
+template <int E, int P, int LPR = 4, bool STREAM = false>
+__device__ __forceinline__ void p1_rows_roll(float4 (&x)[(P1Shape<E, LPR>::F4)], const float* s, int64_t base,
                                              int64_t nbase, bool more, int64_t N, int rho, int ql,
                                              const float* lds_b, uint32_t* lds_hist, float* alpha) {
-  using S = P1Shape<E>;
+  using S = P1Shape<E, LPR>;
   const int64_t row = base + rho;
   const bool valid = row < N;
   int rot = rho;
@@ -252,12 +265,16 @@ __device__ __forceinline__ void p1_rows_roll(float4 (&x)[P1Shape<E>::F4], const 
     a = top[P - 1];
   } else if constexpr (S::LPR == 2) {
     a = top_merge_last<P, kQuadXor1>(top);
-  } else {
+  } else if constexpr (S::LPR == 4) {
     top_merge<P, kQuadXor1>(top);
     a = top_merge_last<P, kQuadXor2>(top);
+  } else {
+    top_merge<P, kQuadXor1>(top);
+    top_merge<P, kQuadXor2>(top);
+    a = top_merge_last<P, kHalfMirror>(top);
   }
   if (valid && ql == 0) __builtin_nontemporal_store(a, alpha + row);
-  uint32_t* h = lds_hist + (S::NC > 1 ? (rho % S::NC) * S::HDW : 0);
+  uint32_t* h = lds_hist + (S::NC > 1 ? p1_copy<S>(rho) * S::HDW : 0);
   if (more) {
     const int64_t nrow = nbase + rho;
     const float* np = s + (nrow < N ? nrow : N - 1) * E;
@@ -269,7 +286,7 @@ __device__ __forceinline__ void p1_rows_roll(float4 (&x)[P1Shape<E>::F4], const 
         hist16_add_hi(h, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
         hist16_add_hi(h, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
       }
-      x[t] = ld4(np + 4 * quad);
+      x[t] = (STREAM ? ld4_nt : ld4)(np + 4 * quad);
     }
   } else if (valid) {
 #pragma unroll
@@ -335,7 +352,7 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
   }
   if constexpr (HM == 1) {
     if (valid) {
-      uint32_t* h = lds_hist + (S::NC > 1 ? (rho % S::NC) * S::HDW : 0);
+      uint32_t* h = lds_hist + (S::NC > 1 ? p1_copy<S>(rho) * S::HDW : 0);
 #pragma unroll
       for (int t = 0; t < S::F4; ++t) {
         const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
@@ -358,7 +375,7 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
 // counting the members of the current microbatch in LDS and adding them to
 // load_mb and load at each microbatch boundary (one atomic per non-zero
 // counter instead of one device atomic per member).
-template <int E, int P, int HM, bool LOAD, bool MB>
+template <int E, int P, int HM, bool LOAD, bool MB, bool ST = false>
 __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_topk(
     const float* __restrict__ s, const float* __restrict__ b, int64_t N, int wg_per_layer, int bdiv, int K,
     float* __restrict__ alpha, int32_t* __restrict__ load, int32_t* __restrict__ hist_hi,
@@ -387,13 +404,24 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   const int ql = lane % S::LPR;
   constexpr int64_t kTrip = int64_t(kWaves) * S::WROWS;
   constexpr bool kRoll = QB_P1_ROLL != 0 && HM == 1 && !LOAD && !MB;
-  float4 xr[S::U][S::F4];  // the rolling path's score slots
+  // ST (streaming, for layers far larger than the Infinity Cache): the
+  // rolling path reads its rows with non-temporal loads, 8 lanes per row so
+  // that every load instruction takes whole 128-byte lines of a row (with 4
+  // lanes per row, 64-byte halves of a line, non-temporal loads fetch lines
+  // twice).
+  static_assert(!ST || (kRoll && E >= 32), "the streaming variant is the rolling path's");
+  constexpr int kRL = ST ? 8 : 4;
+  constexpr bool kStream = ST;
+  using SR = P1Shape<E, kRL>;
+  static_assert(SR::WROWS == S::WROWS, "one trip shape for every row split");
+  const int rrho = lane / SR::LPR, rql = lane % SR::LPR;
+  float4 xr[SR::U][SR::F4];  // the rolling path's score slots
   if constexpr (kRoll && QB_P1_EARLY) {
     // the first trip's loads go out before the table is cleared
     if (g < (N + kTrip - 1) / kTrip) {
-      const int64_t base = int64_t(g) * kTrip + int64_t(wave) * S::WROWS;
+      const int64_t base = int64_t(g) * kTrip + int64_t(wave) * SR::WROWS;
 #pragma unroll
-      for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, xr[u]);
+      for (int u = 0; u < SR::U; ++u) p1_load<E, kRL, kStream>(s, base + u * SR::RPW, N, rrho, rql, xr[u]);
     }
   }
 
@@ -429,19 +457,19 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
       // us at 1M.
       auto& x = xr;
       if (!QB_P1_EARLY && g < trips) {
-        const int64_t base = int64_t(g) * kTrip + int64_t(wave) * S::WROWS;
+        const int64_t base = int64_t(g) * kTrip + int64_t(wave) * SR::WROWS;
 #pragma unroll
-        for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, x[u]);
+        for (int u = 0; u < SR::U; ++u) p1_load<E, kRL, kStream>(s, base + u * SR::RPW, N, rrho, rql, x[u]);
       }
       for (int64_t T = g; T < trips; T += wg_per_layer) {
-        const int64_t base = T * kTrip + int64_t(wave) * S::WROWS;
-        const int64_t nbase = (T + wg_per_layer) * kTrip + int64_t(wave) * S::WROWS;
+        const int64_t base = T * kTrip + int64_t(wave) * SR::WROWS;
+        const int64_t nbase = (T + wg_per_layer) * kTrip + int64_t(wave) * SR::WROWS;
         const bool more = T + wg_per_layer < trips;
         if (QB_P1_ROLL == 1) __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int u = 0; u < S::U; ++u)
-          p1_rows_roll<E, P>(x[u], s, base + u * S::RPW, nbase + u * S::RPW, more, N, rho, ql, lds_b, lds_hist,
-                             alpha);
+        for (int u = 0; u < SR::U; ++u)
+          p1_rows_roll<E, P, kRL, kStream>(x[u], s, base + u * SR::RPW, nbase + u * SR::RPW, more, N, rrho, rql,
+                                           lds_b, lds_hist, alpha);
       }
     } else
     for (int64_t T = g; T < trips; T += wg_per_layer) {
@@ -504,13 +532,13 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   }
 }
 
-template <int E, int P, int HM, bool LOAD, bool MB = false>
+template <int E, int P, int HM, bool LOAD, bool MB = false, bool ST = false>
 static int launch_p1_v(const float* s, const float* b, int L, int bdiv, int64_t N, int K, float* alpha,
                        int32_t* load, int32_t* hist_hi, hipStream_t st, int32_t* load_mb = nullptr,
                        int64_t n_mb = 1) {
   constexpr int kThreads = p1_waves<LOAD, P, MB>() * kWave;
   const RowSplit sp = split_rows(L, N, p1_waves<LOAD, P, MB>() * P1Shape<E>::WROWS, QB_P1_MAXROWS);
-  hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD, MB>), dim3(unsigned(sp.blocks)), dim3(kThreads),
+  hipLaunchKernelGGL((k_margins_topk<E, P, HM, LOAD, MB, ST>), dim3(unsigned(sp.blocks)), dim3(kThreads),
                      0, st, s, b, N, sp.wg_per_layer, bdiv, K, alpha, load, hist_hi, load_mb, n_mb);
   return int(hipGetLastError());
 }
@@ -524,7 +552,13 @@ static int launch_p1(const float* s, const float* b, int L, int bdiv, int64_t N,
     return launch_p1_v<E, P, 0, true, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st, load_mb, n_mb);
   }
   if (hist_hi && load) return launch_p1_v<E, P, 1, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
-  if (hist_hi) return launch_p1_v<E, P, 1, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  if (hist_hi) {
+    if constexpr (E >= 32 && QB_P1_ROLL != 0) {
+      if (stream_pass(L, N, E))
+        return launch_p1_v<E, P, 1, false, false, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+    }
+    return launch_p1_v<E, P, 1, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
+  }
   if (load) return launch_p1_v<E, P, 0, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
   return launch_p1_v<E, P, 0, false>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
 }

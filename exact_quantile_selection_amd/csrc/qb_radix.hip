@@ -82,7 +82,7 @@ struct RHShape {
 // microbatch c (n_mb a multiple of the trip), the counts of each trip summed
 // in LDS and added to its microbatch's row.  No LDS atomic per element and
 // no bias reads from LDS: the standalone pass 1 pays for both.
-template <int E, bool LO, bool WS, int LD = 0>
+template <int E, bool LO, bool WS, int LD = 0, bool ST = false>
 __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     const float* __restrict__ s, const float* __restrict__ alpha, int64_t N, int wg_per_layer,
     const int32_t* __restrict__ sel_hi, int32_t* __restrict__ hist, uint8_t* __restrict__ ws,
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     const float* aw = alpha + base;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      x[u] = ld4(sw + uint32_t((u * S::RPI + rsub) * E + 4 * quad));
+      x[u] = (ST ? ld4_nt : ld4)(sw + uint32_t((u * S::RPI + rsub) * E + 4 * quad));
       a[u] = aw[u * S::RPI + rsub];
     }
   };
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kRHThreads) void k_radix_hist(
     for (int u = 0; u < S::U; ++u) {
       int64_t row = base + u * S::RPI + rsub;
       row = row < N ? row : N - 1;
-      x[u] = ld4(s + row * E + 4 * quad);
+      x[u] = (ST ? ld4_nt : ld4)(s + row * E + 4 * quad);
       a[u] = alpha[row];
     }
 #pragma unroll
@@ -422,6 +422,23 @@ static int launch_rh_ws(const float* s, const float* alpha, int L, int64_t N, co
   const RowSplit sp = split_rows(L, N, RHShape<E>::STEP, QB_RH_MAXROWS);
   const LoWs lay = lo_ws_layout(L, E, sp.wg_per_layer);
   const dim3 grid(unsigned(sp.blocks)), block(kRHThreads);
+  // layers far larger than the Infinity Cache are read with non-temporal
+  // loads (stream_pass); rows of at least 128 bytes, so that every load
+  // instruction takes whole lines
+  if constexpr (E >= 32) {
+    if (stream_pass(L, N, E)) {
+      if (load && load_mb)
+        hipLaunchKernelGGL((k_radix_hist<E, true, true, 2, true>), grid, block, 0, st, s, alpha, N, sp.wg_per_layer,
+                           sel_hi, nullptr, ws, lay.flag, lay.p16, b, K, load, load_mb, n_mb);
+      else if (load)
+        hipLaunchKernelGGL((k_radix_hist<E, true, true, 1, true>), grid, block, 0, st, s, alpha, N, sp.wg_per_layer,
+                           sel_hi, nullptr, ws, lay.flag, lay.p16, b, K, load, nullptr, int64_t(1));
+      else
+        hipLaunchKernelGGL((k_radix_hist<E, true, true, 0, true>), grid, block, 0, st, s, alpha, N, sp.wg_per_layer,
+                           sel_hi, nullptr, ws, lay.flag, lay.p16, nullptr, 0, nullptr, nullptr, int64_t(1));
+      return int(hipGetLastError());
+    }
+  }
   if (load && load_mb)
     hipLaunchKernelGGL((k_radix_hist<E, true, true, 2>), grid, block, 0, st, s, alpha, N, sp.wg_per_layer, sel_hi,
                        nullptr, ws, lay.flag, lay.p16, b, K, load, load_mb, n_mb);

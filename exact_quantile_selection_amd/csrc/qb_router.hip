@@ -132,8 +132,6 @@ struct RfShape {
   static_assert(kRgBM % R == 0, "steps");
 };
 
-// DPP half-row mirror: lane i of each group of 8 reads lane 7 - i.
-constexpr int kHalfMirror = 0x141;
 
 template <int P, int LPR>
 __device__ __forceinline__ void rf_merge_rows(float (&t)[P]) {

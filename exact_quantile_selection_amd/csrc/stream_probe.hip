@@ -21,7 +21,7 @@ namespace {
 constexpr int kThreads = 1024;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int U>
+template <int U, bool NT = false>
 __global__ __launch_bounds__(kThreads) void k_read(const u32x4* __restrict__ p, int64_t n16,
                                                    uint32_t* __restrict__ sink) {
   const int64_t trip_items = int64_t(kThreads) * U;
@@ -31,7 +31,10 @@ __global__ __launch_bounds__(kThreads) void k_read(const u32x4* __restrict__ p, 
     u32x4 v[U];
     if (base + trip_items <= n16) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = p[base + int64_t(u) * kThreads + threadIdx.x];
+      for (int u = 0; u < U; ++u) {
+        const u32x4* a = p + base + int64_t(u) * kThreads + threadIdx.x;
+        v[u] = NT ? __builtin_nontemporal_load(a) : *a;
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -77,9 +80,9 @@ bool bad_args(const void* p, int64_t bytes, int grid) {
          grid < 1 || grid > (1 << 20);
 }
 
-template <int U>
+template <int U, bool NT = false>
 void launch_read(const u32x4* q, int64_t n16, int grid, uint32_t* sink, hipStream_t st) {
-  hipLaunchKernelGGL(k_read<U>, dim3(grid), dim3(kThreads), 0, st, q, n16, sink);
+  hipLaunchKernelGGL((k_read<U, NT>), dim3(grid), dim3(kThreads), 0, st, q, n16, sink);
 }
 
 template <int U>
@@ -102,6 +105,22 @@ int sp_read(const void* p, int64_t bytes, int grid, int unroll, uint32_t* sink, 
     case 4: launch_read<4>(q, n16, grid, sink, st); break;
     case 8: launch_read<8>(q, n16, grid, sink, st); break;
     case 16: launch_read<16>(q, n16, grid, sink, st); break;
+    default: return SP_EINVAL;
+  }
+  return hipGetLastError() == hipSuccess ? SP_OK : SP_EHIP;
+}
+
+int sp_read_nt(const void* p, int64_t bytes, int grid, int unroll, uint32_t* sink, sp_stream_t stream) {
+  if (bad_args(p, bytes, grid) || sink == nullptr) return SP_EINVAL;
+  const u32x4* q = static_cast<const u32x4*>(p);
+  const int64_t n16 = bytes / 16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  switch (unroll) {
+    case 1: launch_read<1, true>(q, n16, grid, sink, st); break;
+    case 2: launch_read<2, true>(q, n16, grid, sink, st); break;
+    case 4: launch_read<4, true>(q, n16, grid, sink, st); break;
+    case 8: launch_read<8, true>(q, n16, grid, sink, st); break;
+    case 16: launch_read<16, true>(q, n16, grid, sink, st); break;
     default: return SP_EINVAL;
   }
   return hipGetLastError() == hipSuccess ? SP_OK : SP_EHIP;

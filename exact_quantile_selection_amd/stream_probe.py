@@ -24,6 +24,8 @@ def lib() -> C.CDLL:
         vp, i32, i64 = C.c_void_p, C.c_int, C.c_int64
         L.sp_read.argtypes = [vp, i64, i32, i32, vp, vp]
         L.sp_read.restype = i32
+        L.sp_read_nt.argtypes = [vp, i64, i32, i32, vp, vp]
+        L.sp_read_nt.restype = i32
         L.sp_copy.argtypes = [vp, vp, i64, i32, i32, vp]
         L.sp_copy.restype = i32
         _lib = L
@@ -39,16 +41,19 @@ def _stream():
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def read(t: torch.Tensor, sink: torch.Tensor, grid: int, unroll: int) -> None:
-    """Stream every byte of t once (sink: int32 [grid] on the same device)."""
+def read(t: torch.Tensor, sink: torch.Tensor, grid: int, unroll: int, nontemporal: bool = False) -> None:
+    """Stream every byte of t once (sink: int32 [grid] on the same device),
+    with non-temporal loads if asked."""
     _check(t, "t")
     _check(sink, "sink")
     if sink.dtype != torch.int32 or sink.numel() < grid:
         raise ValueError("sink must be int32 with at least `grid` elements")
     nbytes = t.numel() * t.element_size()
-    rc = lib().sp_read(C.c_void_p(t.data_ptr()), nbytes, grid, unroll, C.c_void_p(sink.data_ptr()), _stream())
+    fn = lib().sp_read_nt if nontemporal else lib().sp_read
+    rc = fn(C.c_void_p(t.data_ptr()), nbytes, grid, unroll, C.c_void_p(sink.data_ptr()), _stream())
     if rc != 0:
-        raise RuntimeError(f"sp_read failed ({rc}): bytes={nbytes} grid={grid} unroll={unroll}")
+        raise RuntimeError(f"sp_read{'_nt' if nontemporal else ''} failed ({rc}): bytes={nbytes} grid={grid} "
+                           f"unroll={unroll}")
 
 
 def copy(src: torch.Tensor, dst: torch.Tensor, grid: int, unroll: int) -> None:

@@ -13,6 +13,9 @@
  *   sp_read:  loads every byte of p[0, bytes) once; an integer fold of the
  *             data is kept live and written to sink[blockIdx] only on a value the
  *             data practically never produces (no write traffic).
+ *   sp_read_nt: sp_read with non-temporal loads (the streaming hint): on
+ *             MI355X the faster way to read a buffer once, as the passes do
+ *             for layers far larger than the Infinity Cache.
  *   sp_copy:  loads every byte of src[0, bytes) once and stores it to the
  *             same offset of dst (a plain copy: the ceiling of the passes that
  *             read and write equal amounts, such as the LEI gradient offsets
@@ -42,6 +45,7 @@ typedef struct ihipStream_t* sp_stream_t; /* same type as hipStream_t */
 enum { SP_OK = 0, SP_EINVAL = -1, SP_EHIP = -3 };
 
 SP_API int sp_read(const void* p, int64_t bytes, int grid, int unroll, uint32_t* sink, sp_stream_t stream);
+SP_API int sp_read_nt(const void* p, int64_t bytes, int grid, int unroll, uint32_t* sink, sp_stream_t stream);
 SP_API int sp_copy(const void* src, void* dst, int64_t bytes, int grid, int unroll, sp_stream_t stream);
 
 #ifdef __cplusplus

@@ -180,7 +180,7 @@ def test_stream_probe_exports_its_header():
 
         build.build_probe()
     declared = sorted(set(re.findall(r"SP_API\s+[\w\s\*]+?\b(sp_\w+)\s*\(", open(PROBE_HEADER).read())))
-    assert declared == ["sp_copy", "sp_read"]
+    assert declared == ["sp_copy", "sp_read", "sp_read_nt"]
     out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True).stdout
     assert sorted(set(re.findall(r" T (sp_\w+)", out))) == declared
     import torch  # noqa: F401
@@ -194,6 +194,8 @@ def test_stream_probe_exports_its_header():
     assert L.sp_read(fake + 4, 1024, 1, 8, fake, None) == -1  # misaligned
     assert L.sp_read(fake, 1024, 1, 5, fake, None) == -1    # unroll
     assert L.sp_read(fake, 1024, 0, 8, fake, None) == -1    # grid
+    assert L.sp_read_nt(fake, 1000, 1, 8, fake, None) == -1  # not a multiple of 16
+    assert L.sp_read_nt(fake, 1024, 1, 3, fake, None) == -1    # unroll
     assert L.sp_copy(fake, None, 1024, 1, 4, None) == -1
     assert L.sp_copy(fake, fake + 512, 1024, 1, 4, None) == -1  # overlapping
     assert L.sp_copy(fake, fake + 4096, 1024, 1, 16, None) == -1  # unroll

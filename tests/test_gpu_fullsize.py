@@ -217,3 +217,56 @@ def test_k3_more_bins_on_a_later_call(O):
             G.assert_same(f"{k} ({n_bins} bins)", G.host(t), ref[k])
     del s
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("E", [32, 64, 128, 256])
+def test_streaming_passes_on_a_tiled_gib_layer(O, E):
+    """One GiB of scores per layer (a 4096-row block repeated 2^16 / E
+    times): the size at which both passes read with non-temporal loads, pass
+    1 with 8 lanes per row.  The workspace update without loads, with the
+    loads in pass 2, and with per-microbatch loads in pass 2 all give the
+    block's alpha (every repeat), key, q, b_next and bounds, and T times its
+    histograms and loads."""
+    P, K = 4096, 6 if E >= 64 else 4
+    T = (1 << 16) // E
+    N = P * T
+    assert N * E * 4 == 1 << 30
+    blk, b_np, _ = synth.random_case(41 + E, P, E, K, quant=64.0)
+    ref = O.eqb_layer(blk, b_np, K)
+    n_mb = P * 8
+    mb_ref = O.microbatch_loads(blk, b_np, K, P)  # one block per microbatch row of the oracle
+    s = G.dev(blk).repeat(T, 1)
+    ws = torch.empty(qb.qb_hist_lo_workspace_bytes(1, N, E), dtype=torch.uint8, device=G.DEV)
+    for mode in ("plain", "loads", "microbatch loads"):
+        G.say(f"streaming GiB layer E={E} {mode}")
+        b = G.dev(b_np)
+        alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+        buf = qb.EqbBuffers(1, E, device=G.DEV, lead=False)
+        load = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+        if mode == "plain":
+            qb.eqb_update_ws(s, b, K, alpha, buf, ws)
+        elif mode == "loads":
+            qb.eqb_update_ws(s, b, K, alpha, buf, ws, load=load)
+        else:
+            load_mb = torch.zeros((N // n_mb, E), dtype=torch.int32, device=G.DEV)
+            qb.qb_margins_topk(s, b, K, alpha, hist_hi=buf.hist_hi)
+            qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
+                                err=buf.err)
+            qb.qb_radix_hist_lo_ws_loads(s, alpha, buf.sel_hi, ws, b, K, load, n_mb=n_mb, load_mb=load_mb)
+            qb.qb_select_lo_ws(N, ws, buf.sel_hi, buf.rank_lo, buf.q, b, buf.bounds, hist_lo=buf.hist_lo,
+                               key_out=buf.key, err=buf.err)
+        torch.cuda.synchronize()
+        assert int(buf.err.item()) == 0
+        a = G.host(alpha).reshape(T, P)
+        assert (a == ref["alpha"][None, :]).all(), f"{mode}: alpha differs from the block's in some repeat"
+        G.assert_same(f"{mode} hist_hi", G.host(buf.hist_hi), T * ref["hist_hi"])
+        G.assert_same(f"{mode} hist_lo", G.host(buf.hist_lo), T * ref["hist_lo"])
+        for k, t in (("sel_hi", buf.sel_hi), ("key", buf.key), ("q", buf.q), ("b_next", b), ("bounds", buf.bounds)):
+            G.assert_same(f"{mode} {k}", G.host(t), ref[k])
+        if mode != "plain":
+            G.assert_same(f"{mode} load", G.host(load), T * ref["load"])
+        if mode == "microbatch loads":
+            G.assert_same("load_mb", G.host(load_mb), np.tile(8 * mb_ref, (N // n_mb, 1)))
+    del s
+    torch.cuda.empty_cache()

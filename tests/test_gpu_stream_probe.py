@@ -25,10 +25,11 @@ def test_copy_reproduces_the_source(unroll, n16):
     assert int((big[:64] != 7).sum()) == 0 and int((big[-64:] != 7).sum()) == 0
 
 
+@pytest.mark.parametrize("nt", [False, True])
 @pytest.mark.parametrize("unroll", [1, 2, 4, 8, 16])
-def test_read_completes(unroll):
+def test_read_completes(unroll, nt):
     t = torch.ones(1 << 22, dtype=torch.float32, device="cuda")
     sink = torch.zeros(512, dtype=torch.int32, device="cuda")
-    sp.read(t, sink, 512, unroll)
+    sp.read(t, sink, 512, unroll, nontemporal=nt)
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0  # the fold of all-ones data never hits the sink's trigger value
