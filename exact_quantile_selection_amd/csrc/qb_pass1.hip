@@ -15,7 +15,10 @@
 // load; the starting column block is rotated by the row index so that, in
 // every later instruction, the lanes of the wave touch distinct experts
 // (distinct LDS banks for the histogram atomics, distinct bias entries) as
-// far as E allows.
+// far as E allows.  The high-byte pass without loads rotates whole 128-byte
+// lines instead for E >= 64 (two consecutive loads of a lane take the two
+// halves of one line), and over layers of 768 MiB or more at E = 256 it
+// splits a row over 8 lanes and reads it with non-temporal loads.
 //   * top-(K+1): per-lane insertion with v_med3_f32 (one op per list slot),
 //     then DPP merges across the row's lanes (bitonic), the last merge only
 //     producing the minimum of the merged top list, which is alpha.
@@ -94,15 +97,39 @@ struct P1Shape {
   static_assert((F4 & (F4 - 1)) == 0, "power-of-two loads per lane");
 };
 
-// The high-byte table copy of row rho of a load instruction.  Rows rho and
-// rho' of one instruction read the same columns when rho = rho' mod F4, so
-// those NC rows take NC different copies.
-#ifndef QB_P1_COPYFIX
-#define QB_P1_COPYFIX 0
+// Paired column order for the high-byte pass without loads (1): slots 2i
+// and 2i + 1 of a lane read the two halves of one 128-byte line of its row,
+// the line rotated by the row.  A read probe over 1 GiB of 1 KiB rows, 4
+// lanes per row: 166 us against 177 us for the plain rotation.  Pass 1 over
+// 1 GiB of scores (events, two runs each): E = 64 208-209 against 223-225 us,
+// E = 128 210-215 against 214-219 us, unchanged at 262,144 x 256; the
+// alpha-only pass gains nothing from it (the 65,536-token K3 step 56 against
+// 55 us), and at E = 32 (one line per row: no rotation left) 224 against
+// 215 us, so neither takes it.
+#ifndef QB_P1_PAIR
+#define QB_P1_PAIR 1
 #endif
-template <class S>
+
+// The column block (of LPR float4s) that a lane group reads in slot t of its
+// row; rot is the row index within the load instruction.  Plain: block
+// (t + rot) mod F4, so the rows of one instruction cover distinct columns as
+// far as E allows.  PAIR (4 lanes per row, at least two lines per row): the
+// lines are rotated instead, block 2 ((t / 2 + rot) mod F4/2) + t mod 2.
+template <class S, bool PAIR>
+__device__ __forceinline__ int p1_blk(int t, int rot) {
+  if constexpr (PAIR && S::LPR == 4 && S::F4 >= 4) return ((((t >> 1) + rot) & (S::F4 / 2 - 1)) << 1) | (t & 1);
+  return (t + rot) & (S::F4 - 1);
+}
+
+// The high-byte table copy of row rho of a load instruction.  In the paired
+// order rows rho and rho' of one instruction read the same columns when
+// rho = rho' mod F4/2, and rho / (F4/2) mod NC spreads them over the copies.
+// In the plain order (rho = rho' mod F4) rho mod NC lets some of them share
+// a copy for 32 <= E <= 128; copies chosen by rho / F4 mod NC, which never
+// share, measured the same (one GiB of scores at E = 32: 212-215 us).
+template <class S, bool PAIR = false>
 __device__ __forceinline__ int p1_copy(int rho) {
-  if constexpr (QB_P1_COPYFIX != 0) return (rho / S::F4) % S::NC;
+  if constexpr (PAIR && S::LPR == 4 && S::F4 >= 4) return (rho / (S::F4 / 2)) % S::NC;
   return rho % S::NC;
 }
 
@@ -210,7 +237,7 @@ __device__ __forceinline__ void count_loads(const float4 (&x)[P1Shape<E>::F4], c
 // Loads one trip's rows (this lane's V scores of row base + rho) into x.
 // `base` is wave-uniform: a full trip addresses its rows from a uniform base
 // pointer with 32-bit lane offsets; a partial last trip clamps the row.
-template <int E, int LPR = 4, bool STREAM = false>
+template <int E, int LPR = 4, bool STREAM = false, bool PAIR = false>
 __device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N, int rho, int ql,
                                         float4 (&x)[(P1Shape<E, LPR>::F4)]) {
   using S = P1Shape<E, LPR>;
@@ -224,13 +251,13 @@ __device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N,
     const uint32_t lane_off = uint32_t(rho * E + 4 * ql);
 #pragma unroll
     for (int t = 0; t < S::F4; ++t)
-      x[t] = (STREAM ? ld4_nt : ld4)(ws + (lane_off + uint32_t(4 * S::LPR * ((t + rot) & (S::F4 - 1)))));
+      x[t] = (STREAM ? ld4_nt : ld4)(ws + (lane_off + uint32_t(4 * S::LPR * p1_blk<S, PAIR>(t, rot))));
   } else {
     const int64_t row = base + rho;
     const float* src = s + (row < N ? row : N - 1) * E;
 #pragma unroll
     for (int t = 0; t < S::F4; ++t) {
-      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+      const int quad = S::LPR * p1_blk<S, PAIR>(t, rot) + ql;
       x[t] = (STREAM ? ld4_nt : ld4)(src + 4 * quad);
     }
   }
@@ -239,7 +266,7 @@ __device__ __forceinline__ void p1_load(const float* s, int64_t base, int64_t N,
 // p1_rows without loads (HM = 1) that refills each slot of x with the next
 // trip's scores (rows nbase + rho) as soon as the slot's last use, its key,
 // is done: the next trip streams in while this one is counted.
-template <int E, int P, int LPR = 4, bool STREAM = false>
+template <int E, int P, int LPR = 4, bool STREAM = false, bool PAIR = false>
 __device__ __forceinline__ void p1_rows_roll(float4 (&x)[(P1Shape<E, LPR>::F4)], const float* s, int64_t base,
                                              int64_t nbase, bool more, int64_t N, int rho, int ql,
                                              const float* lds_b, uint32_t* lds_hist, float* alpha) {
@@ -253,7 +280,7 @@ __device__ __forceinline__ void p1_rows_roll(float4 (&x)[(P1Shape<E, LPR>::F4)],
   for (int k = 0; k < P; ++k) top[k] = -__builtin_inff();
 #pragma unroll
   for (int t = 0; t < S::F4; ++t) {
-    const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+    const int quad = S::LPR * p1_blk<S, PAIR>(t, rot) + ql;
     const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
     top_insert<P>(top, x[t].x + bb.x);
     top_insert<P>(top, x[t].y + bb.y);
@@ -274,13 +301,13 @@ __device__ __forceinline__ void p1_rows_roll(float4 (&x)[(P1Shape<E, LPR>::F4)],
     a = top_merge_last<P, kHalfMirror>(top);
   }
   if (valid && ql == 0) __builtin_nontemporal_store(a, alpha + row);
-  uint32_t* h = lds_hist + (S::NC > 1 ? p1_copy<S>(rho) * S::HDW : 0);
+  uint32_t* h = lds_hist + (S::NC > 1 ? p1_copy<S, PAIR>(rho) * S::HDW : 0);
   if (more) {
     const int64_t nrow = nbase + rho;
     const float* np = s + (nrow < N ? nrow : N - 1) * E;
 #pragma unroll
     for (int t = 0; t < S::F4; ++t) {
-      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+      const int quad = S::LPR * p1_blk<S, PAIR>(t, rot) + ql;
       if (valid) {
         const uint32_t swz = hist16_swizzle2(quad);
         hist16_add_hi(h, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
@@ -291,7 +318,7 @@ __device__ __forceinline__ void p1_rows_roll(float4 (&x)[(P1Shape<E, LPR>::F4)],
   } else if (valid) {
 #pragma unroll
     for (int t = 0; t < S::F4; ++t) {
-      const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+      const int quad = S::LPR * p1_blk<S, PAIR>(t, rot) + ql;
       const uint32_t swz = hist16_swizzle2(quad);
       hist16_add_hi(h, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
       hist16_add_hi(h, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
@@ -300,12 +327,13 @@ __device__ __forceinline__ void p1_rows_roll(float4 (&x)[(P1Shape<E, LPR>::F4)],
 }
 
 // alpha, loads and the high-byte histogram of one trip's rows.
-template <int E, int P, int HM, bool LOAD>
+template <int E, int P, int HM, bool LOAD, bool PAIR = false>
 __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64_t base, int64_t N,
                                         int rho, int ql, int lane, int K, const float* lds_b,
                                         uint32_t* lds_hist, int32_t* lds_load, float* alpha,
                                         int32_t* ghist) {
   using S = P1Shape<E>;
+  static_assert(!(PAIR && LOAD), "the load count assumes the plain column order");
   const int64_t row = base + rho;
   const bool valid = row < N;
   int rot = rho;
@@ -315,7 +343,7 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
   for (int k = 0; k < P; ++k) top[k] = -__builtin_inff();
 #pragma unroll
   for (int t = 0; t < S::F4; ++t) {
-    const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+    const int quad = S::LPR * p1_blk<S, PAIR>(t, rot) + ql;
     const float4 bb = *reinterpret_cast<const float4*>(&lds_b[4 * quad]);
     top_insert<P>(top, x[t].x + bb.x);
     top_insert<P>(top, x[t].y + bb.y);
@@ -339,7 +367,7 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
     if (valid) {
 #pragma unroll
       for (int t = 0; t < S::F4; ++t) {
-        const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+        const int quad = S::LPR * p1_blk<S, PAIR>(t, rot) + ql;
         const uint32_t k01 = key2(bf16x2_rne(a - x[t].x, a - x[t].y));
         const uint32_t k23 = key2(bf16x2_rne(a - x[t].z, a - x[t].w));
         int32_t* h = ghist + int64_t(4 * quad) * 65536;
@@ -352,10 +380,10 @@ __device__ __forceinline__ void p1_rows(const float4 (&x)[P1Shape<E>::F4], int64
   }
   if constexpr (HM == 1) {
     if (valid) {
-      uint32_t* h = lds_hist + (S::NC > 1 ? p1_copy<S>(rho) * S::HDW : 0);
+      uint32_t* h = lds_hist + (S::NC > 1 ? p1_copy<S, PAIR>(rho) * S::HDW : 0);
 #pragma unroll
       for (int t = 0; t < S::F4; ++t) {
-        const int quad = S::LPR * ((t + rot) & (S::F4 - 1)) + ql;
+        const int quad = S::LPR * p1_blk<S, PAIR>(t, rot) + ql;
         const uint32_t swz = hist16_swizzle2(quad);
         hist16_add_hi(h, quad, 0, key2(bf16x2_rne(a - x[t].x, a - x[t].y)) ^ swz);
         hist16_add_hi(h, quad, 2, key2(bf16x2_rne(a - x[t].z, a - x[t].w)) ^ swz);
@@ -412,6 +440,7 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
   static_assert(!ST || (kRoll && E >= 32), "the streaming variant is the rolling path's");
   constexpr int kRL = ST ? 8 : 4;
   constexpr bool kStream = ST;
+  constexpr bool kPair = QB_P1_PAIR != 0 && HM == 1 && !LOAD;
   using SR = P1Shape<E, kRL>;
   static_assert(SR::WROWS == S::WROWS, "one trip shape for every row split");
   const int rrho = lane / SR::LPR, rql = lane % SR::LPR;
@@ -421,7 +450,7 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
     if (g < (N + kTrip - 1) / kTrip) {
       const int64_t base = int64_t(g) * kTrip + int64_t(wave) * SR::WROWS;
 #pragma unroll
-      for (int u = 0; u < SR::U; ++u) p1_load<E, kRL, kStream>(s, base + u * SR::RPW, N, rrho, rql, xr[u]);
+      for (int u = 0; u < SR::U; ++u) p1_load<E, kRL, kStream, kPair>(s, base + u * SR::RPW, N, rrho, rql, xr[u]);
     }
   }
 
@@ -459,7 +488,7 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
       if (!QB_P1_EARLY && g < trips) {
         const int64_t base = int64_t(g) * kTrip + int64_t(wave) * SR::WROWS;
 #pragma unroll
-        for (int u = 0; u < SR::U; ++u) p1_load<E, kRL, kStream>(s, base + u * SR::RPW, N, rrho, rql, x[u]);
+        for (int u = 0; u < SR::U; ++u) p1_load<E, kRL, kStream, kPair>(s, base + u * SR::RPW, N, rrho, rql, x[u]);
       }
       for (int64_t T = g; T < trips; T += wg_per_layer) {
         const int64_t base = T * kTrip + int64_t(wave) * SR::WROWS;
@@ -468,8 +497,8 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
         if (QB_P1_ROLL == 1) __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int u = 0; u < SR::U; ++u)
-          p1_rows_roll<E, P, kRL, kStream>(x[u], s, base + u * SR::RPW, nbase + u * SR::RPW, more, N, rrho, rql,
-                                           lds_b, lds_hist, alpha);
+          p1_rows_roll<E, P, kRL, kStream, kPair>(x[u], s, base + u * SR::RPW, nbase + u * SR::RPW, more, N,
+                                                  rrho, rql, lds_b, lds_hist, alpha);
       }
     } else
     for (int64_t T = g; T < trips; T += wg_per_layer) {
@@ -477,16 +506,16 @@ __global__ __launch_bounds__((p1_waves<LOAD, P, MB>() * kWave)) void k_margins_t
       float4 x[S::U][S::F4];
       if (early) {
 #pragma unroll
-        for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, x[u]);
+        for (int u = 0; u < S::U; ++u) p1_load<E, 4, false, kPair>(s, base + u * S::RPW, N, rho, ql, x[u]);
         __builtin_amdgcn_s_barrier();
       } else {
         __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int u = 0; u < S::U; ++u) p1_load<E>(s, base + u * S::RPW, N, rho, ql, x[u]);
+        for (int u = 0; u < S::U; ++u) p1_load<E, 4, false, kPair>(s, base + u * S::RPW, N, rho, ql, x[u]);
       }
 #pragma unroll
       for (int u = 0; u < S::U; ++u)
-        p1_rows<E, P, HM, LOAD>(x[u], base + u * S::RPW, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha,
+        p1_rows<E, P, HM, LOAD, kPair>(x[u], base + u * S::RPW, N, rho, ql, lane, K, lds_b, lds_hist, lds_load, alpha,
                                 ghist);
     }
   } else {
@@ -553,7 +582,12 @@ static int launch_p1(const float* s, const float* b, int L, int bdiv, int64_t N,
   }
   if (hist_hi && load) return launch_p1_v<E, P, 1, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
   if (hist_hi) {
-    if constexpr (E >= 32 && QB_P1_ROLL != 0) {
+    // Streaming pays at E = 256 only: with fewer experts the 8 lanes of a
+    // row hold 4-16 scores each and the extra merge per row costs more than
+    // the faster stream gives (one GiB of scores in pass 1, plain against
+    // streaming: E = 32 206 against 268 us, E = 64 211 against 243, E = 128
+    // 205 against 214; E = 256 193 against 189).
+    if constexpr (E == 256 && QB_P1_ROLL != 0) {
       if (stream_pass(L, N, E))
         return launch_p1_v<E, P, 1, false, false, true>(s, b, L, bdiv, N, K, alpha, load, hist_hi, st);
     }

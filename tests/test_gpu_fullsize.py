@@ -227,7 +227,10 @@ def test_streaming_passes_on_a_tiled_gib_layer(O, E):
     1 with 8 lanes per row.  The workspace update without loads, with the
     loads in pass 2, and with per-microbatch loads in pass 2 all give the
     block's alpha (every repeat), key, q, b_next and bounds, and T times its
-    histograms and loads."""
+    histograms and loads.  The K3 update on the same layer (its alpha-only
+    pass streams too, and so does its binning for 32 experts or more) gives
+    the block's alpha, q, b_next and bounds and T times its 1000-bin
+    histogram."""
     P, K = 4096, 6 if E >= 64 else 4
     T = (1 << 16) // E
     N = P * T
@@ -268,5 +271,21 @@ def test_streaming_passes_on_a_tiled_gib_layer(O, E):
             G.assert_same(f"{mode} load", G.host(load), T * ref["load"])
         if mode == "microbatch loads":
             G.assert_same("load_mb", G.host(load_mb), np.tile(8 * mb_ref, (N // n_mb, 1)))
+    G.say(f"streaming GiB layer E={E} K3")
+    bounds = O.bounds_of(b_np)
+    k3 = O.k3_layer(blk, b_np, K, bounds, 1000)
+    b = G.dev(b_np)
+    bnd = G.dev(bounds.astype(np.float32))
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    hist_u = torch.zeros((E, 1000), dtype=torch.int32, device=G.DEV)
+    q = torch.zeros(E, dtype=torch.float32, device=G.DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+    qb.k3_update(s, b, K, alpha, bnd, hist_u, q_out=q, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert (G.host(alpha).reshape(T, P) == ref["alpha"][None, :]).all(), "K3: alpha differs in some repeat"
+    G.assert_same("K3 hist_u", G.host(hist_u), T * k3["hist_u"])
+    for k, t in (("q", q), ("b_next", b), ("bounds", bnd)):
+        G.assert_same(f"K3 {k}", G.host(t), k3[k])
     del s
     torch.cuda.empty_cache()
