@@ -3,8 +3,10 @@
 A step is one full EQB layer update of the skewed 1,048,576-token workload
 (E=256, K=6): pass 1 (alpha + high-byte histogram), the high-byte select,
 pass 2 (low-byte partial histograms) and the low-byte select with the
-in-place bias update and the in-place reset of the high-byte histogram; the
-bias is restored first so every step does identical work.  Inputs are
+bias update and the in-place reset of the high-byte histogram.  Pass 1
+reads the layer's bias and the select writes b_next into a second buffer
+(the update reads q only, never the old bias), so every step is the same
+update with no copy between steps.  Inputs are
 resident in HBM before timing starts.  The timed steps run back to back from
 one HIP graph that holds all of them.
 
@@ -55,6 +57,8 @@ class EqbStep:
         N, E = s.shape[-2], s.shape[-1]
         Lx = s.shape[0] if lead else 1
         self.N = N
+        # b0 is the bias pass 1 routes with; b receives b_next.  Kept apart,
+        # every step computes the same update from the same input.
         self.b = b0.clone()
         self.alpha = torch.empty(((Lx,) if lead else ()) + (N,), dtype=torch.float32, device=s.device)
         self.buf = qb.EqbBuffers(Lx, E, device=s.device, lead=lead)
@@ -70,22 +74,21 @@ class EqbStep:
         clears both histograms with a fill kernel first."""
         qb, buf = self.qb, self.buf
         body = [
-            ("pass1_topk_hist_hi", lambda: qb.qb_margins_topk(self.s, self.b, self.K, self.alpha,
+            ("pass1_topk_hist_hi", lambda: qb.qb_margins_topk(self.s, self.b0, self.K, self.alpha,
                                                               hist_hi=buf.hist_hi)),
             ("select_hi", lambda: qb.qb_select_update(qb.QB_SELECT_HI, self.K, buf.hist_hi,
                                                       sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
                                                       err=buf.err)),
         ]
-        restore = ("restore_bias", lambda: self.b.copy_(self.b0))
         if self.ws is not None:
-            return [restore] + body + [
+            return body + [
                 ("pass2_hist_lo", lambda: qb.qb_radix_hist_lo_ws(self.s, self.alpha, buf.sel_hi, self.ws)),
                 ("select_lo", lambda: qb.qb_select_lo_ws(self.N, self.ws, buf.sel_hi, buf.rank_lo, buf.q,
                                                          self.b, buf.bounds, hist_lo=buf.hist_lo,
                                                          key_out=buf.key, err=buf.err,
                                                          hist_hi=buf.hist_hi)),
             ]
-        return [restore, ("reset_hist", lambda: buf.reset())] + body + [
+        return [("reset_hist", lambda: buf.reset())] + body + [
             ("pass2_hist_lo", lambda: qb.qb_radix_hist_lo(self.s, self.alpha, buf.sel_hi, buf.hist_lo)),
             ("select_lo", lambda: qb.qb_select_update(qb.QB_SELECT_LO, self.K, buf.hist_lo,
                                                       sel_hi=buf.sel_hi, rank_lo=buf.rank_lo,
@@ -421,13 +424,15 @@ def single_suite(torch, qb, synth, dev, args):
             self_.atomic = atomic
 
         def run(self_):
-            b.copy_(b0)
+            # the select reads the bounds it bins over, then writes the next
+            # range: restored for every step; the bias is read from b0 and
+            # b_next written to b
             bounds.copy_(bounds0)
             if self_.atomic:
                 qb.qb_fill_i32(hist_u, 0)
-                qb.k3_update(s, b, K, alpha, bounds, hist_u, q_u)
+                qb.k3_update(s, b, K, alpha, bounds, hist_u, q_u, b_in=b0)
             else:
-                qb.k3_update_ws(s, b, K, alpha, bounds, ws_u, q_u)
+                qb.k3_update_ws(s, b, K, alpha, bounds, ws_u, q_u, b_in=b0)
 
     sec, _ = time_graph(K3Step(), torch, args.steps, args.warmup)
     b_ws = b.clone()
@@ -531,9 +536,8 @@ def full_hist_suite(torch, qb, synth, dev, args):
 
     class OnePass:
         def run(self_):
-            b.copy_(b0)
             qb.qb_fill_i32(hist, 0)
-            qb.qb_margins_full_hist(s, b, K, alpha, hist)
+            qb.qb_margins_full_hist(s, b0, K, alpha, hist)
             qb.qb_select_update(qb.QB_SELECT_FULL, K, hist, key_out=key, q_out=q, b=b, bounds=bounds, err=err)
 
     sec, _ = time_graph(OnePass(), torch, max(5, args.steps // 2), 2)
@@ -579,13 +583,14 @@ def k3_skew_suite(torch, qb, synth, dev, args):
             self_.ws = ws
 
         def run(self_, i=0):
-            b.copy_(b0)
+            # bounds restored (the select reads them, then writes the next
+            # range); the bias is read from b0 and b_next written to b
             bounds.copy_(bounds0)
             if self_.ws:
-                qb.k3_update_ws(s, b, K, alpha, bounds, ws_u, q, err=err)
+                qb.k3_update_ws(s, b, K, alpha, bounds, ws_u, q, err=err, b_in=b0)
             else:
                 qb.qb_fill_i32(hist_u, 0)
-                qb.k3_update(s, b, K, alpha, bounds, hist_u, q, err=err)
+                qb.k3_update(s, b, K, alpha, bounds, hist_u, q, err=err, b_in=b0)
 
     sec, _ = time_graph(K3Step(), torch, max(5, args.steps // 2), 2)
     assert int(err.item()) == 0
@@ -794,18 +799,18 @@ def router_suite(torch, qb, synth, dev, args):
             self_.p2 = loads_in_pass2
 
         def run(self_):
-            b.copy_(b0)
+            # routed with b0; the select writes b_next to b
             qb.qb_fill_i32(load, 0)
             l1 = None if self_.p2 else load
             if self_.fused:
-                qb.qb_router_fused(hidden, w, b, K, s, alpha, load=l1, hist_hi=buf.hist_hi)
+                qb.qb_router_fused(hidden, w, b0, K, s, alpha, load=l1, hist_hi=buf.hist_hi)
             else:
                 qb.qb_router_scores(hidden, w, s)
-                qb.qb_margins_topk(s, b, K, alpha, load=l1, hist_hi=buf.hist_hi)
+                qb.qb_margins_topk(s, b0, K, alpha, load=l1, hist_hi=buf.hist_hi)
             qb.qb_select_update(qb.QB_SELECT_HI, K, buf.hist_hi, sel_hi=buf.sel_hi,
                                 rank_lo=buf.rank_lo, err=buf.err)
             if self_.p2:
-                qb.qb_radix_hist_lo_ws_loads(s, alpha, buf.sel_hi, ws, b, K, load)
+                qb.qb_radix_hist_lo_ws_loads(s, alpha, buf.sel_hi, ws, b0, K, load)
             else:
                 qb.qb_radix_hist_lo_ws(s, alpha, buf.sel_hi, ws)
             qb.qb_select_lo_ws(N, ws, buf.sel_hi, buf.rank_lo, buf.q, b, buf.bounds, key_out=buf.key,

@@ -489,20 +489,23 @@ def eqb_update_ws(s, b, K, alpha, buf: EqbBuffers, ws, load=None, reset_hist_hi=
                     stream=stream)
 
 
-def k3_update(s, b, K, alpha, bounds, hist_u, q_out, err=None, stream=None):
+def k3_update(s, b, K, alpha, bounds, hist_u, q_out, err=None, stream=None, b_in=None):
     """One K3 update: alpha pass, uniform-bin pass over the current bounds,
-    select + in-place bias/bounds update.  hist_u must be zero on entry."""
-    qb_margins_topk(s, b, K, alpha, stream=stream)
+    select + in-place bias/bounds update.  hist_u must be zero on entry.
+    b_in (optional): the bias the alpha pass reads when it is not b (the
+    select writes b_next to b and never reads the old bias)."""
+    qb_margins_topk(s, b if b_in is None else b_in, K, alpha, stream=stream)
     qb_uniform_hist(s, alpha, bounds, hist_u, stream=stream)
     qb_select_update(QB_SELECT_UNIFORM, K, hist_u, q_out=q_out, b=b, bounds=bounds, err=err,
                      stream=stream)
 
 
-def k3_update_ws(s, b, K, alpha, bounds, ws, q_out, n_bins=1000, hist_u=None, err=None, stream=None):
+def k3_update_ws(s, b, K, alpha, bounds, ws, q_out, n_bins=1000, hist_u=None, err=None, stream=None,
+                 b_in=None):
     """k3_update with the binning merged through the workspace ws
     (qb_uniform_hist_workspace_bytes): nothing to zero; same q, b and
-    bounds."""
-    qb_margins_topk(s, b, K, alpha, stream=stream)
+    bounds.  b_in as in k3_update."""
+    qb_margins_topk(s, b if b_in is None else b_in, K, alpha, stream=stream)
     qb_uniform_hist_ws(s, alpha, bounds, ws, n_bins, stream=stream)
     qb_select_uniform_ws(s.shape[-2], K, n_bins, ws, q_out, b, bounds, hist_u=hist_u, err=err, stream=stream)
 
