@@ -297,18 +297,20 @@ static int launch_uh(const float* s, const float* alpha, int L, int64_t N, int E
   return int(hipGetLastError());
 }
 
-// Wider slices read longer row segments but give each workgroup a larger
-// table to clear and flush; they are used when every workgroup still gets
-// enough rows: 64-expert slices from 2048 rows per workgroup, 32-expert
-// slices (more than 1024 bins) from 8192.  Measured on one MI355X with 1000
-// bins and 256 experts: at 131,072 tokens 52 us with 64-expert slices
-// against 59-63 us with 16; at 65,536 tokens 35 us with 16-expert slices,
-// 42 us with 32 and 47 us with 64.
+// Wider slices read longer row segments (whole lines from 32 experts) but
+// give each workgroup a larger table to clear and merge; they are used when
+// every workgroup still gets enough rows: 64-expert slices from 1024 rows
+// per workgroup, 32-expert slices (more than 1024 bins) from 8192.  Measured
+// on one MI355X with 1000 bins and 256 experts, workspace merge: at 65,536
+// tokens (1024 rows per workgroup) the binning pass takes 20.8-21.1 us with
+// 64-expert slices, 22.4-23.3 with 32 and 27.5-28.3 with 16 (K3 step 48.9-
+// 49.3 against 53.2-54.3 us); at 131,072 tokens 52 us with 64-expert slices
+// against 59-63 us with 16 (atomic merge).
 #ifndef QB_UH_MIN_ROWS
 #define QB_UH_MIN_ROWS 8192
 #endif
 #ifndef QB_UH_MIN_ROWS64
-#define QB_UH_MIN_ROWS64 2048
+#define QB_UH_MIN_ROWS64 1024
 #endif
 
 // Slice width of the binning pass for a shape.
