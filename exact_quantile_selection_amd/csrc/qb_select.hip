@@ -230,8 +230,29 @@ __global__ __launch_bounds__(kFullThreads) void k_select_full(int E, int K, cons
   if (key_out) key_out[le + j] = uint16_t(key);
 }
 
-// b_next = q - mean(q) (float64 sum in expert order on one thread, one
-// rounding to fp32), written over b; bounds = [min - 1, max + 1] (min and
+// The float64 sum of the q values is exact, and so equal in every order,
+// when all of its partial sums fit 53 bits: every term is a multiple of
+// 2^lo (lo: the exponent of the lowest set bit of the term with the lowest
+// one) and the sum of at most 256 terms below 2^hi in magnitude stays below
+// 2^(hi + 8).  Then a tree reduction gives the sum of the expert-order loop
+// bit for bit (zeros enter as +0, as the loop's 0.0 start makes them); a
+// wider spread keeps the loop (1).  The loop alone: 0.
+#ifndef QB_FIN_TREE
+#define QB_FIN_TREE 1
+#endif
+
+// Exponents bounding a finite fp32 value v != 0: v is a multiple of 2^lo
+// and |v| < 2^hi.
+__device__ __forceinline__ void exp_span(float v, int& lo, int& hi) {
+  const uint32_t u = __float_as_uint(v);
+  const int ex = int((u >> 23) & 0xFFu);
+  const uint32_t m = ex ? ((u & 0x7FFFFFu) | 0x800000u) : (u & 0x7FFFFFu);
+  lo = (ex ? ex - 150 : -149) + __builtin_ctz(m);
+  hi = ex ? ex - 126 : -126;
+}
+
+// b_next = q - mean(q) (the float64 sum of q in expert order, one rounding
+// to fp32), written over b; bounds = [min - 1, max + 1] (min and
 // max as a parallel reduction: any order gives the same values up to the
 // sign of a zero, which the -1 / +1 removes).  A layer with a NaN quantile
 // (failed rank search) keeps its b and bounds.  Run by the first
@@ -242,6 +263,8 @@ __device__ void finalize_layer(int E, const float* q, float* b, float* bounds, i
   __shared__ double s_mean;
   __shared__ int s_bad;
   __shared__ float s_min[kFinThreads / kWave], s_max[kFinThreads / kWave];
+  __shared__ double s_sum[kFinThreads / kWave];
+  __shared__ int s_lo[kFinThreads / kWave], s_hi[kFinThreads / kWave];
   const int lane = tid & (kWave - 1);
   const bool mine = tid < kFinThreads;
   if (tid == 0) s_bad = 0;
@@ -256,7 +279,43 @@ __device__ void finalize_layer(int E, const float* q, float* b, float* bounds, i
     if (tid == 0 && err) atomicOr(err, QB_ERR_RANK);
     return;
   }
-  if (tid == 0) {
+  bool tree = false;
+  if constexpr (QB_FIN_TREE != 0) {
+    const int lane_ = tid & (kWave - 1);
+    int lo = 1 << 20, hi = -(1 << 20);
+    double d = 0.0;
+    if (tid < E) {
+      const float v = sq[tid];
+      if (v != 0.0f) exp_span(v, lo, hi);
+      d = double(v) + 0.0;
+    }
+#pragma unroll
+    for (int k = 1; k < kWave; k <<= 1) {
+      lo = min(lo, __shfl_xor(lo, k));
+      hi = max(hi, __shfl_xor(hi, k));
+      d += __shfl_xor(d, k);
+    }
+    if (mine && lane_ == 0) {
+      s_lo[tid / kWave] = lo;
+      s_hi[tid / kWave] = hi;
+      s_sum[tid / kWave] = d;
+    }
+    __syncthreads();
+    lo = s_lo[0];
+    hi = s_hi[0];
+#pragma unroll
+    for (int w = 1; w < kFinThreads / kWave; ++w) {
+      lo = min(lo, s_lo[w]);
+      hi = max(hi, s_hi[w]);
+    }
+    tree = hi + 8 - lo <= 53;  // also true when every q is zero
+    if (tree && tid == 0) {
+      double sum = s_sum[0];
+      for (int w = 1; w < kFinThreads / kWave; ++w) sum += s_sum[w];
+      s_mean = sum / double(E);
+    }
+  }
+  if (!tree && tid == 0) {
     // E is a multiple of 4; vector LDS reads keep the in-order float64 chain
     // from waiting on one LDS round trip per term.
     double sum = 0.0;

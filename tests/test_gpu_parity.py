@@ -258,6 +258,29 @@ def test_select_error_flags_keep_bias():
     assert int(err.item()) & qb.QB_ERR_EMPTY
 
 
+def test_mean_over_a_wide_exponent_spread(O):
+    """Quantiles from 2^-120 to 1 (alpha = 2^-100: expert 0 sits 2^-120
+    below it, experts 4.. score -1): the float64 sum of q cannot be exact,
+    so the kernel's mean takes its expert-order loop; b_next equals the
+    oracle's bit for bit.  A second batch with every quantile near 1 takes
+    the order-free sum."""
+    N, E, K = 512, 16, 2
+    a = np.float32(2.0 ** -100)
+    s = np.full((N, E), -1.0, np.float32)
+    s[:, 1] = np.float32(2.0 ** -99)
+    s[:, 2] = np.float32(1.5 * 2.0 ** -99)
+    s[:, 3] = a
+    s[:, 0] = a - np.float32(2.0 ** -120) * (1 + (np.arange(N) % 3)).astype(np.float32)
+    s[:, 4:] -= (np.arange(12, dtype=np.float32) * np.float32(2.0 ** -10))[None, :]
+    b = np.zeros(E, np.float32)
+    G.say("wide exponent spread E=16")
+    ref = O.eqb_layer(s, b, K)
+    assert ref["q"][0] < 2.0 ** -110 and ref["q"][-1] > 0.5
+    G.compare_eqb(G.run_eqb(s, b, K), ref, tag="wide spread ")
+    s2 = np.clip(s + np.float32(0.5), 0.25, None).astype(np.float32)
+    G.compare_eqb(G.run_eqb(s2, b, K), O.eqb_layer(s2, b, K), tag="narrow spread ")
+
+
 def test_run_to_run_determinism():
     N, E, K = 65536, 256, 6
     s_np, b_np, _ = synth.single(N=N)
