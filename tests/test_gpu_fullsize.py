@@ -236,6 +236,12 @@ def test_streaming_passes_on_a_tiled_gib_layer(O, E):
     N = P * T
     assert N * E * 4 == 1 << 30
     blk, b_np, _ = synth.random_case(41 + E, P, E, K, quant=64.0)
+    if E == 256:
+        # Rows whose top K+1 all lie in one lane's columns of the 8-lane
+        # split (experts 32 b + c, c < 4, sit in its first lane): alpha then
+        # comes from one lane's list alone.
+        cols = np.array([0, 1, 2, 3, 32, 33, 34, 35, 64])[:K + 1]
+        blk[:64, cols] = (np.float32(3.0) - np.arange(K + 1, dtype=np.float32) / 64)[None, :]
     ref = O.eqb_layer(blk, b_np, K)
     n_mb = P * 8
     mb_ref = O.microbatch_loads(blk, b_np, K, P)  # one block per microbatch row of the oracle
