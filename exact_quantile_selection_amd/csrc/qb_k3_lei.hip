@@ -300,28 +300,36 @@ static int launch_uh(const float* s, const float* alpha, int L, int64_t N, int E
 // Wider slices read longer row segments (whole lines from 32 experts) but
 // give each workgroup a larger table to clear and merge; they are used when
 // every workgroup still gets enough rows: 64-expert slices from 1024 rows
-// per workgroup, 32-expert slices (more than 1024 bins) from 8192.  Measured
-// on one MI355X with 1000 bins and 256 experts, workspace merge: at 65,536
-// tokens (1024 rows per workgroup) the binning pass takes 20.8-21.1 us with
-// 64-expert slices, 22.4-23.3 with 32 and 27.5-28.3 with 16 (K3 step 48.9-
-// 49.3 against 53.2-54.3 us); at 131,072 tokens 52 us with 64-expert slices
+// per workgroup when the tables leave through the workspace, from 2048 when
+// they are flushed with global atomics (a larger tail per workgroup), and
+// 32-expert slices (more than 1024 bins) from 8192.  Measured on one MI355X
+// with 1000 bins and 256 experts: at 65,536 tokens (1024 rows per
+// workgroup) the workspace binning pass takes 20.8-21.1 us with 64-expert
+// slices, 22.4-23.3 with 32 and 27.5-28.3 with 16 (K3 step 48.9-49.3
+// against 53.2-54.3 us), while the atomic one took 47 us with 64-expert
+// slices against 35 with 16; at 131,072 tokens 52 us with 64-expert slices
 // against 59-63 us with 16 (atomic merge).
 #ifndef QB_UH_MIN_ROWS
 #define QB_UH_MIN_ROWS 8192
 #endif
+#ifndef QB_UH_MIN_ROWS64_WS
+#define QB_UH_MIN_ROWS64_WS 1024
+#endif
 #ifndef QB_UH_MIN_ROWS64
-#define QB_UH_MIN_ROWS64 1024
+#define QB_UH_MIN_ROWS64 2048
 #endif
 
-// Slice width of the binning pass for a shape.
-static int uh_slice(int L, int64_t N, int E, int n_bins) {
-  if (E >= 64 && n_bins <= 1024 && N / uh_groups<64>(L, N, E, 1) >= QB_UH_MIN_ROWS64) return 64;
+// Slice width of the binning pass for a shape; ws: the tables leave
+// through the workspace (else by global atomics).
+static int uh_slice(int L, int64_t N, int E, int n_bins, bool ws) {
+  const int64_t min64 = ws ? QB_UH_MIN_ROWS64_WS : QB_UH_MIN_ROWS64;
+  if (E >= 64 && n_bins <= 1024 && N / uh_groups<64>(L, N, E, 1) >= min64) return 64;
   if (E >= 32 && N / uh_groups<32>(L, N, E, 1) >= QB_UH_MIN_ROWS) return 32;
   return 16;
 }
 
 int64_t uniform_hist_groups(int L, int64_t N, int E, int n_bins) {
-  switch (uh_slice(L, N, E, n_bins)) {
+  switch (uh_slice(L, N, E, n_bins, true)) {
     case 64: return uh_groups<64>(L, N, E, uh_per_cu<64>(n_bins));
     case 32: return uh_groups<32>(L, N, E, uh_per_cu<32>(n_bins));
   }
@@ -330,7 +338,7 @@ int64_t uniform_hist_groups(int L, int64_t N, int E, int n_bins) {
 
 static int launch_uniform_hist_any(const float* s, const float* alpha, int L, int64_t N, int E,
                                    const float* bounds, int n_bins, int32_t* hist_u, uint8_t* ws, hipStream_t st) {
-  switch (uh_slice(L, N, E, n_bins)) {
+  switch (uh_slice(L, N, E, n_bins, ws != nullptr)) {
     case 64: return launch_uh<64>(s, alpha, L, N, E, bounds, n_bins, hist_u, ws, st);
     case 32: return launch_uh<32>(s, alpha, L, N, E, bounds, n_bins, hist_u, ws, st);
   }
