@@ -7,8 +7,10 @@ bias update and the in-place reset of the high-byte histogram.  Pass 1
 reads the layer's bias and the select writes b_next into a second buffer
 (the update reads q only, never the old bias), so every step is the same
 update with no copy between steps.  Inputs are
-resident in HBM before timing starts.  The timed steps run back to back from
-one HIP graph that holds all of them.
+resident in HBM before timing starts, and the untimed warm-up steps run for
+at least 50 ms (after idle the clocks settle over tens of milliseconds of
+load).  The timed steps run back to back from one HIP graph that holds all
+of them.
 
 Printed: one JSON line with the metric (tokens/s per layer), the roofline
 of the dominant kernel (algorithmic bytes / average duration from HIP events
@@ -101,24 +103,65 @@ class EqbStep:
             f()
 
 
-def time_graph(step, torch, steps, warmup):
-    """Run `warmup` steps eagerly, capture `steps` consecutive steps in one
+_CLOCK = {}
+
+
+def sustain_clock(torch, ms=50.0):
+    """Untimed streaming reads (libstreamprobe, non-temporal, unroll 16: a
+    form the ceiling sweep never times) for at least `ms` before a timed
+    region that has no step of its own to warm up with (the ceilings, the
+    single-kernel timings).  After a second or two of idle (data
+    generation, setup) the chip's clocks settle over tens of milliseconds;
+    a training job runs the update on a chip kept busy, so timings are
+    taken in that settled state."""
+    import time as _t
+    from exact_quantile_selection_amd import stream_probe as sp
+    if "buf" not in _CLOCK:
+        _CLOCK["buf"] = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        _CLOCK["sink"] = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = _t.perf_counter()
+    while (_t.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(32):
+            sp.read(_CLOCK["buf"], _CLOCK["sink"], 256, 16, nontemporal=True)
+        torch.cuda.synchronize()
+
+
+WARM_MS = 50.0
+
+
+def time_graph(step, torch, steps, warmup, before_timed=None):
+    """Run `warmup` steps eagerly (more if they take under 50 ms: after
+    idle the clocks settle over tens of milliseconds of the step's own load;
+    pass 1 over 1 GiB ran up to 226 us per launch in the first 50 launches
+    against 175-181 us once settled), capture `steps` consecutive steps in one
     HIP graph (as a training step's graph holds its layers' updates back to
     back), replay it once untimed, then time one replay: exactly `steps`
     steps between two device synchronizations.  Returns seconds per step.
     The side stream first waits for the current one, where the step's
-    inputs and buffers were written (generation, zero-filled histograms)."""
+    inputs and buffers were written (generation, zero-filled histograms).
+    before_timed (optional) runs after the untimed replay: it restores state
+    that the steps accumulate, so the timed replay's result does not depend
+    on how many warm-up steps ran."""
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
-        for _ in range(max(1, warmup)):
-            step.run()
+        # at least `warmup` steps, and at least 50 ms of them: the step's
+        # own load is what the clocks settle to (a plain read draws less)
+        t0, n = time.perf_counter(), 0
+        while n < max(1, warmup) or (time.perf_counter() - t0) * 1e3 < WARM_MS:
+            for _ in range(4):
+                step.run()
+            n += 4
+            stream.synchronize()
     stream.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for _ in range(steps):
             step.run()
     g.replay()
+    if before_timed is not None:
+        before_timed()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g.replay()
@@ -157,6 +200,7 @@ def ceilings(torch, s, reps=10):
     timed with HIP events around `reps` back-to-back launches; the fastest
     is the ceiling."""
     from exact_quantile_selection_amd import stream_probe as sp
+    sustain_clock(torch)
 
     cus = torch.cuda.get_device_properties(s.device).multi_processor_count
     nbytes = s.numel() * 4
@@ -193,6 +237,7 @@ def copy_ceiling(torch, src, reps=10):
     few (grid, unroll), HIP events around `reps` back-to-back launches;
     GB/s counts the bytes read plus the bytes written."""
     from exact_quantile_selection_amd import stream_probe as sp
+    sustain_clock(torch)
 
     cus = torch.cuda.get_device_properties(src.device).multi_processor_count
     dst = torch.empty_like(src)
@@ -376,7 +421,8 @@ def main():
                                        "when the pass sources changed since)",
                      "avg_launch_us": round(per_k[dominant] * 1e6, 2),
                      "timing": f"HIP events around each launch on its stream, {args.steps} eager steps in "
-                               "step order after the timed graph replay",
+                               "step order after the timed graph replay (both after at least 50 ms of "
+                               "untimed warm-up steps that settle the clocks)",
                      "frac_of_measured_read_ceiling": round(achieved / ceil["read"]["GBps"], 4),
                      "algorithmic_bytes_per_launch": dom_bytes},
         "kernels": kernels,
@@ -490,6 +536,7 @@ def lei_backward_suite(torch, qb, synth, dev, args):
     gout = torch.empty_like(grad)
     d = torch.empty_like(grad)
     out = dict(N=N, E=E, K=K, n_mb=n_mb, bytes_per_launch=16 * N * E)
+    sustain_clock(torch)
     for bounded in (False, True):
         f = lambda: qb.qb_lei_backward(grad, load, K, n_mb, 1e-5, bounded=bounded, s=s, g_out=gout, dlogits=d)
         f()
@@ -631,6 +678,7 @@ def sharding_suite(torch, qb, synth, dev, args, R=8):
     sh = ShardedUpdate(R, N, E, K, device=dev)
 
     def timed(f, n=5):
+        sustain_clock(torch)
         f()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -710,6 +758,13 @@ def controller_suite(torch, qb, synth, dev, args, T=8):
     graph.replay()
     torch.cuda.synchronize()
     same = bool(torch.equal(ctl.worst_global, traj[-1][0]))
+    # untimed replays of the same closed loop for at least 50 ms (the clocks
+    # settle over tens of milliseconds of load after idle)
+    tw = time.perf_counter()
+    while (time.perf_counter() - tw) * 1e3 < WARM_MS:
+        ctl.b.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
     ctl.b.zero_()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -764,6 +819,7 @@ def router_suite(torch, qb, synth, dev, args):
 
     n = max(3, args.steps // 2)
     hist = buf.hist_hi
+    sustain_clock(torch)
     # pass 1 fused into the GEMM's epilogue, against the GEMM alone followed
     # by the standalone pass 1 over the scores it wrote (same results)
     t_fused = reps(lambda: qb.qb_router_fused(hidden, w, b, K, s, alpha, load=load, hist_hi=hist), n)
@@ -821,8 +877,7 @@ def router_suite(torch, qb, synth, dev, args):
     b_ref = g_ref = None
     for name, fused, p2 in (("fused", True, False), ("unfused", False, False),
                             ("fused_loads_in_pass2", True, True), ("unfused_loads_in_pass2", False, True)):
-        grad.copy_(grad0)
-        chains[name], _ = time_graph(Chain(fused, p2), torch, n, 1)
+        chains[name], _ = time_graph(Chain(fused, p2), torch, n, 1, before_timed=lambda: grad.copy_(grad0))
         if b_ref is None:
             b_ref, g_ref = b.clone(), grad.clone()
         assert torch.equal(b, b_ref), name
