@@ -154,6 +154,7 @@ def time_graph(step, torch, steps, warmup, before_timed=None):
                 step.run()
             n += 4
             stream.synchronize()
+    _CLOCK["warm_steps"] = n
     stream.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
@@ -401,7 +402,7 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "warmup_steps_run": _CLOCK.get("warm_steps"),
         "ms_per_step": sec * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
