@@ -220,6 +220,39 @@ def test_k3_more_bins_on_a_later_call(O):
 
 
 @pytest.mark.timeout(600)
+def test_streaming_passes_with_a_ragged_last_trip(O):
+    """786,509 tokens x 256 experts: just above the size from which both
+    passes read with non-temporal loads (768 MiB), pass 1 with 8 lanes per
+    row, and 77 rows past a whole number of trips, so the last trip of the
+    8-lane form clamps and masks its rows.  The update with and without the
+    loads in pass 2 equals the oracle's, bit for bit."""
+    N, E, K = 786432 + 77, 256, 6
+    assert N * E * 4 >= 768 << 20
+    s_np, b_np, _ = synth.random_case(53, N, E, K, quant=64.0)
+    G.say(f"streaming ragged layer N={N} E={E}")
+    ref = O.eqb_layer(s_np, b_np, K)
+    s = G.dev(s_np)
+    ws = torch.empty(qb.qb_hist_lo_workspace_bytes(1, N, E), dtype=torch.uint8, device=G.DEV)
+    for with_load in (False, True):
+        b = G.dev(b_np)
+        alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+        buf = qb.EqbBuffers(1, E, device=G.DEV, lead=False)
+        load = torch.zeros(E, dtype=torch.int32, device=G.DEV)
+        qb.eqb_update_ws(s, b, K, alpha, buf, ws, load=load if with_load else None)
+        torch.cuda.synchronize()
+        assert int(buf.err.item()) == 0
+        got = dict(alpha=G.host(alpha), hist_hi=G.host(buf.hist_hi), sel_hi=G.host(buf.sel_hi),
+                   hist_lo=G.host(buf.hist_lo), key=G.host(buf.key), q=G.host(buf.q), b_next=G.host(b),
+                   bounds=G.host(buf.bounds))
+        for k in ("alpha", "hist_hi", "sel_hi", "hist_lo", "key", "q", "b_next", "bounds"):
+            G.assert_same(f"ragged {k}", got[k], ref[k])
+        if with_load:
+            G.assert_same("ragged load", G.host(load), ref["load"])
+    del s
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("E", [32, 64, 128, 256])
 def test_streaming_passes_on_a_tiled_gib_layer(O, E):
     """One GiB of scores per layer (a 4096-row block repeated 2^16 / E
