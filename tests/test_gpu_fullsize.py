@@ -225,7 +225,8 @@ def test_streaming_passes_with_a_ragged_last_trip(O):
     passes read with non-temporal loads (768 MiB), pass 1 with 8 lanes per
     row, and 77 rows past a whole number of trips, so the last trip of the
     8-lane form clamps and masks its rows.  The update with and without the
-    loads in pass 2 equals the oracle's, bit for bit."""
+    loads in pass 2, and the K3 update (whose binning pass streams too),
+    equal the oracle's, bit for bit."""
     N, E, K = 786432 + 77, 256, 6
     assert N * E * 4 >= 768 << 20
     s_np, b_np, _ = synth.random_case(53, N, E, K, quant=64.0)
@@ -248,6 +249,20 @@ def test_streaming_passes_with_a_ragged_last_trip(O):
             G.assert_same(f"ragged {k}", got[k], ref[k])
         if with_load:
             G.assert_same("ragged load", G.host(load), ref["load"])
+    # K3 on the same layer: its binning pass streams too (64-expert slices)
+    bounds = O.bounds_of(b_np)
+    k3 = O.k3_layer(s_np, b_np, K, bounds, 1000)
+    b = G.dev(b_np)
+    bnd = G.dev(bounds.astype(np.float32))
+    alpha = torch.empty(N, dtype=torch.float32, device=G.DEV)
+    hist_u = torch.zeros((E, 1000), dtype=torch.int32, device=G.DEV)
+    q = torch.zeros(E, dtype=torch.float32, device=G.DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=G.DEV)
+    qb.k3_update(s, b, K, alpha, bnd, hist_u, q_out=q, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for k, t in (("alpha", alpha), ("hist_u", hist_u), ("q", q), ("b_next", b), ("bounds", bnd)):
+        G.assert_same(f"ragged K3 {k}", G.host(t), k3[k])
     del s
     torch.cuda.empty_cache()
 
